@@ -1,0 +1,319 @@
+"""Benchmark of the HGA routed-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+
+A step is one decode step of the 32K-context workload (B=8, 32 query / 8 KV
+heads, d=128, C=64, G=16, sink 1, local 4, top-k 16, top-g 32, bf16): the
+library's hga_decode, which routes (summary scan + chunk top-k + group
+scoring + group top-g, and the summary update of the chunk the query
+completes) and attends over the gathered K/V.  Inputs are resident in HBM.
+Consecutive steps rotate over independent copies of the cache (as consecutive
+layers of a model would), so no step finds its working set in the 256 MB
+Infinity Cache; a warm-cache figure is reported separately.
+
+Printed: one JSON line with the throughput (query tokens/s), the roofline of
+the attention kernel (HIP events on the launch stream), the CPU oracle timed
+on a bounded sample, and the 32K prefill figures.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "routed-attention query tokens/s + % HBM/MFMA roofline, 32K decode & prefill"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(s):
+    """Algorithmic HBM bytes of one decode step, split by kernel.
+
+    attention: gathered K and V rows of the visible set, Q in, O out (fp32),
+               group ids;
+    routing:   candidate chunk summaries, the group summaries of the routed
+               chunks, Q; plus the summary update of the completed chunk.
+    """
+    C, G, d = s.chunk_size, s.group_size, s.head_dim
+    L = s.n_tokens
+    j = (L - 1) // C
+    n_forced = len(set(range(min(s.n_sink, j + 1))) | set(range(max(0, j - s.n_local), j + 1)))
+    m = C // G
+    n_cand = max(0, j - s.n_local - s.n_sink)
+    n_routed_chunks = min(s.top_k, n_cand)
+    n_groups = min(s.top_g, n_routed_chunks * m)
+    gq = s.n_q_heads // s.n_kv_heads
+    units = s.batch * s.n_kv_heads
+    e = 2 if s.dtype == "bf16" else 4
+    tokens = n_forced * C + n_groups * G
+    att = units * (tokens * d * e * 2 + gq * d * e + gq * d * 4 + s.top_g * 4)
+    route = units * ((n_cand + n_routed_chunks * m) * d * 4 + gq * d * e
+                     + (s.top_k + s.top_g) * 4)
+    if L % C == 0:  # summary update of the completed chunk: read C rows, write 1 + m summaries
+        route += units * (C * d * e + (1 + m) * d * 4)
+    return att, route, tokens
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the routed-attention path "
+                                   "shards by (batch, KV head) with no communication, so N GPUs "
+                                   "run N independent copies of this measurement"}))
+        sys.exit(2)
+
+    import torch
+    from hierarchical_sparse_attention_build_amd import hga
+    from hierarchical_sparse_attention_build_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    hga.lib()
+
+    s = W.spec("decode_32k")
+    log(f"[bench] generating {s.name} (seed {s.seed})")
+    w = W.make(s)
+    B, Hq, H, d, L, C, G = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens, s.chunk_size, s.group_size
+    m = C // G
+    p = hga.params(B, Hq, H, d, C, G, s.n_sink, s.n_local, s.top_k, s.top_g, s.rope_base,
+                   s.hf_threshold, qkv_dtype=hga.HGA_BF16, out_dtype=hga.HGA_F32)
+    Q0 = W.to_torch(w.Q, s.dtype).to(dev)
+    K0 = W.to_torch(w.K, s.dtype).to(dev)
+    V0 = W.to_torch(w.V, s.dtype).to(dev)
+    nC = L // C
+    jq = (L - 1) // C
+    R = max(1, args.replicas)
+    reps = []
+    for r in range(R):
+        K = K0 if r == 0 else K0.clone()
+        V = V0 if r == 0 else V0.clone()
+        cs = torch.zeros((B, H, nC, d), device=dev)
+        gs = torch.zeros((B, H, nC * m, d), device=dev)
+        hga.build_summaries(p, K, L, 0, jq, cs, gs)
+        reps.append(dict(K=K, V=V, Q=Q0.clone(), cs=cs, gs=gs,
+                         O=torch.empty((B, Hq, 1, d), device=dev),
+                         gi=torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device=dev),
+                         ci=torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device=dev),
+                         ws=hga.workspace(p, hga.OP_DECODE, 1, L, device=dev),
+                         wsr=hga.workspace(p, hga.OP_ROUTE, 1, L, device=dev),
+                         wsa=hga.workspace(p, hga.OP_ATTEND, 1, L, device=dev)))
+    seq = torch.from_numpy(w.seq_len.astype(np.int32)).to(dev)
+    qpos = seq - 1
+    torch.cuda.synchronize()
+    log(f"[bench] {R} cache replicas resident; warmup {args.warmup}, steps {args.steps}")
+
+    def step(i):
+        r = reps[i % R]
+        hga.decode(p, r["Q"], r["K"], r["V"], L, seq, r["cs"], r["gs"], r["O"], r["ws"],
+                   chunk_idx=r["ci"], group_idx=r["gi"])
+
+    def route_only(i):
+        r = reps[i % R]
+        hga.route(p, r["Q"], 1, qpos, r["cs"], r["gs"], L, r["ci"], r["gi"], r["wsr"])
+
+    def attend_only(i):
+        r = reps[i % R]
+        hga.attend(p, r["Q"], 1, qpos, r["K"], r["V"], L, r["gi"], r["O"], r["wsa"])
+
+    # The timed work is replayed from HIP graphs: one graph holds one step per
+    # cache replica, so the host issues one launch per R steps.
+    def capture(fn, n, rep0=None):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n):
+                fn(i if rep0 is None else rep0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i if rep0 is None else rep0)
+        torch.cuda.synchronize()
+        return g
+
+    g_cold = capture(step, R)
+    g_warm = capture(step, R, rep0=0)
+    reps_per_replay = R
+    n_replay = max(1, args.steps // reps_per_replay)
+    steps = n_replay * reps_per_replay
+    for _ in range(max(1, args.warmup // R)):
+        g_cold.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_replay):
+        g_cold.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / steps
+    value = B / sec_per_step
+    log(f"[bench] decode step {sec_per_step * 1e6:.2f} us -> {value:.0f} query tokens/s")
+
+    # warm-cache figure: the same step repeated on one replica
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(n_replay):
+        g_warm.replay()
+    torch.cuda.synchronize()
+    warm_sec = (time.perf_counter() - t2) / steps
+
+    # per-kernel durations: HIP events on the launch stream around graph replays
+    # of back-to-back launches of one kernel (same launch configuration as in
+    # hga_decode), cycling over the cache replicas
+    def kernel_us(fn):
+        n = 4 * R
+        g = capture(fn, n)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps_ = max(1, args.steps // n)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        for _ in range(reps_):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps_ * n)
+
+    route_us = kernel_us(route_only)
+    att_us = kernel_us(attend_only)
+    att_bytes, route_bytes, tokens = decode_bytes(s)
+    att_gbs = att_bytes / (att_us * 1e-6) / 1e9
+    route_gbs = route_bytes / (route_us * 1e-6) / 1e9
+    log(f"[bench] attend {att_us:.2f} us ({att_gbs:.0f} GB/s), route {route_us:.2f} us ({route_gbs:.0f} GB/s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_32k", "batch": B, "context": L, "q_heads": Hq, "kv_heads": H,
+                   "head_dim": d, "chunk": C, "group": G, "sink": s.n_sink, "local": s.n_local,
+                   "top_k": s.top_k, "top_g": s.top_g, "rope_base": s.rope_base,
+                   "tokens_attended": tokens, "cache_replicas": R},
+        "roofline": {"kernel": "attend_splitk_kernel<bf16,128,4>", "bound": "hbm",
+                     "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": att_bytes, "avg_us": round(att_us, 3)},
+        "route": {"kernel": "route_scan_kernel<bf16,128>", "avg_us": round(route_us, 3),
+                  "bytes_per_launch": route_bytes, "achieved_gbs": round(route_gbs, 1),
+                  "frac": round(route_gbs / HBM_PEAK_GBS, 4)},
+        "step_hbm_frac": round((att_bytes + route_bytes) / sec_per_step / 1e9 / HBM_PEAK_GBS, 4),
+        "warm_cache": {"ms_per_step": round(warm_sec * 1e3, 6), "value": round(B / warm_sec, 1)},
+    }
+
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill(args, dev)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(s, w)
+
+    print(json.dumps(out), flush=True)
+
+
+def bench_prefill(args, dev):
+    import torch
+    from hierarchical_sparse_attention_build_amd import hga
+    from hierarchical_sparse_attention_build_amd import workloads as W
+    s = W.spec("prefill_32k")
+    log(f"[bench] generating {s.name} (seed {s.seed})")
+    w = W.make(s)
+    B, Hq, H, d, n, C, G = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens, s.chunk_size, s.group_size
+    p = hga.params(B, Hq, H, d, C, G, s.n_sink, s.n_local, s.top_k, s.top_g, s.rope_base,
+                   s.hf_threshold, qkv_dtype=hga.HGA_BF16, out_dtype=hga.HGA_F32)
+    Q = W.to_torch(w.Q, s.dtype).to(dev)
+    K = W.to_torch(w.K, s.dtype).to(dev)
+    V = W.to_torch(w.V, s.dtype).to(dev)
+    nC = n // C
+    cs = torch.empty((B, H, nC, d), device=dev)
+    gs = torch.empty((B, H, nC * (C // G), d), device=dev)
+    O = torch.empty((B, Hq, n, d), device=dev)
+    ws = hga.workspace(p, hga.OP_PREFILL, n, n, device=dev)
+    hga.prefill(p, Q, K, V, n, cs, gs, O, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.prefill_steps):
+        hga.prefill(p, Q, K, V, n, cs, gs, O, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.prefill_steps
+    # algorithmic attention FLOPs: 4*d per (query row, visible key) pair
+    pairs = 0
+    m = C // G
+    for j in range(nC):
+        n_forced_full = len(set(range(min(s.n_sink, j + 1))) | set(range(max(0, j - s.n_local), j)))
+        n_cand = max(0, j - s.n_local - s.n_sink)
+        routed = min(s.top_g, min(s.top_k, n_cand) * m) * G
+        pairs += C * (n_forced_full * C + routed) + C * (C + 1) // 2
+    flops = pairs * Hq * B * 4 * d
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] prefill {ms:.2f} ms, attention {flops / 1e9:.1f} GFLOP -> {tf:.1f} TFLOP/s")
+    return {"workload": "prefill_32k", "ms": round(ms, 4), "query_tokens_per_s": round(B * n / (ms * 1e-3), 1),
+            "attention_gflop": round(flops / 1e9, 2),
+            "attention_tflops_whole_call": round(tf, 2),
+            "mfma_frac_whole_call": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def cpu_baseline(s, w):
+    """The oracle timed on this host's cores, one decode step of all sequences
+    (routing over prebuilt oracle summaries + exact attention), repeated."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from hierarchical_sparse_attention_build_amd import workloads as W
+    log("[bench] cpu baseline: preparing oracle tables")
+    cfg = O.HGAConfig(**W.hga_config_kwargs(s))
+    with threadpool_limits(limits=1):
+        Kf = W.to_f64(w.K, s.dtype)
+        Vf = W.to_f64(w.V, s.dtype)
+        Qf = W.to_f64(w.Q, s.dtype)
+        jq = (s.n_tokens - 1) // s.chunk_size
+        cs, gs = O.build_summaries(Kf[:, :, : jq * s.chunk_size], cfg)
+        cs = np.concatenate([cs, np.zeros((*cs.shape[:2], s.n_tokens // s.chunk_size - jq, s.head_dim))], 2)
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            O.decode(Qf, Kf, Vf, w.seq_len, cs, gs, cfg, s.n_kv_heads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 10.0 or reps >= 50:
+                break
+    rate = s.batch * reps / el
+    log(f"[bench] cpu oracle: {reps} steps in {el:.1f} s -> {rate:.1f} query tokens/s")
+    return {"value": round(rate, 2), "unit": "query tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full decode steps of decode_32k (all {s.batch} sequences, 64 units; "
+                      "routing over prebuilt oracle summary tables + exact attention), numpy float64, "
+                      "BLAS limited to 1 thread"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,81 @@
+"""Build ``libhga.so`` (HIP, gfx950) in-tree with hipcc.
+
+    python -m hierarchical_sparse_attention_build_amd.build [--jobs N] [--debug]
+
+Objects go to ``_build/`` at the repository root; the library lands next to
+this file, where the ctypes binding loads it.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libhga.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = [
+    "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+    # keep the compiler from forming packed-fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
+
+
+def _compile(src, opt):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"]
+    cmd = [HIPCC, *lang, *COMMON, opt, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj, r.stderr
+
+
+def build(jobs: int | None = None, debug: bool = False, verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    opt = "-O1" if debug else "-O3"
+    srcs = sources()
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 1)))
+    objs = []
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for obj, err in ex.map(lambda s: _compile(s, opt), srcs):
+            objs.append(obj)
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, LIB)
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--debug", action="store_true")
+    ap.add_argument("--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(a.jobs, a.debug, a.verbose))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,554 @@
+// C ABI of the HGA library: argument validation, workspace carving and launch
+// sequencing.  Nothing here allocates device memory or synchronises; every
+// launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hga.h"
+#include "hga_kernels.hpp"
+
+using namespace hga;
+
+namespace {
+
+thread_local std::string g_err;
+
+hga_status fail(hga_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+hga_status ok() {
+  g_err.clear();
+  return HGA_OK;
+}
+
+hga_status hip_fail(hipError_t e, const char* what) {
+  return fail(HGA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ------------------------------------------------------------------ params
+hga_status build_kparams(const hga_params* p, int64_t n_cap, KParams& kp) {
+  if (!p) return fail(HGA_ERR_ARG, "params is null");
+  if (p->batch < 1 || p->n_kv_heads < 1 || p->n_q_heads < 1)
+    return fail(HGA_ERR_SHAPE, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads != 0)
+    return fail(HGA_ERR_SHAPE, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", p->n_q_heads,
+                p->n_kv_heads);
+  const int gq = p->n_q_heads / p->n_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+    return fail(HGA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d: supported 1, 2, 4, 8, 16", gq);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(HGA_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", p->head_dim);
+  if (p->chunk_size < 1 || p->chunk_size > 256)
+    return fail(HGA_ERR_SHAPE, "chunk_size %d out of [1, 256]", p->chunk_size);
+  if (p->group_size < 1 || p->chunk_size % p->group_size != 0)
+    return fail(HGA_ERR_SHAPE, "group_size %d must divide chunk_size %d", p->group_size, p->chunk_size);
+  if (p->chunk_size / p->group_size > 64)
+    return fail(HGA_ERR_UNSUPPORTED, "chunk_size/group_size = %d > 64", p->chunk_size / p->group_size);
+  if (p->n_sink < 0 || p->n_local < 0) return fail(HGA_ERR_ARG, "n_sink and n_local must be >= 0");
+  if (p->top_k < 0 || p->top_k > 1024) return fail(HGA_ERR_ARG, "top_k %d out of [0, 1024]", p->top_k);
+  if (p->top_g < 0 || p->top_g > 1024) return fail(HGA_ERR_ARG, "top_g %d out of [0, 1024]", p->top_g);
+  if (!(p->rope_base > 1.0) || !std::isfinite(p->rope_base))
+    return fail(HGA_ERR_ARG, "rope_base must be a finite number > 1");
+  if (!(p->hf_threshold >= 0.0) || !std::isfinite(p->hf_threshold))
+    return fail(HGA_ERR_ARG, "hf_threshold must be finite and >= 0");
+  if ((p->qkv_dtype != HGA_BF16 && p->qkv_dtype != HGA_F32) ||
+      (p->out_dtype != HGA_BF16 && p->out_dtype != HGA_F32))
+    return fail(HGA_ERR_ARG, "unknown dtype");
+  if (n_cap < 1 || n_cap > (int64_t(1) << 30))
+    return fail(HGA_ERR_SHAPE, "n_cap %lld out of [1, 2^30]", static_cast<long long>(n_cap));
+  if (n_cap % p->chunk_size != 0)
+    return fail(HGA_ERR_SHAPE, "n_cap %lld must be a multiple of chunk_size %d",
+                static_cast<long long>(n_cap), p->chunk_size);
+  kp = KParams{};
+  kp.B = p->batch;
+  kp.Hq = p->n_q_heads;
+  kp.Hkv = p->n_kv_heads;
+  kp.d = p->head_dim;
+  kp.C = p->chunk_size;
+  kp.G = p->group_size;
+  kp.m = p->chunk_size / p->group_size;
+  kp.gq = gq;
+  kp.n_sink = p->n_sink;
+  kp.n_local = p->n_local;
+  kp.top_k = p->top_k;
+  kp.top_g = p->top_g;
+  kp.n_cap = n_cap;
+  kp.n_chunks_cap = static_cast<int32_t>(n_cap / p->chunk_size);
+  kp.inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(p->head_dim)));
+  kp.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(p->head_dim)));
+  kp.hf_mask = 0;
+  for (int i = 0; i < p->head_dim / 2; ++i) {
+    const double th = std::pow(p->rope_base, -2.0 * i / p->head_dim);
+    kp.theta_d[i] = th;
+    kp.theta_f[i] = static_cast<float>(th);
+    if (th * p->chunk_size > p->hf_threshold) kp.hf_mask |= (uint64_t(1) << i);
+  }
+  return HGA_OK;
+}
+
+size_t elem_bytes(const hga_params* p) { return p->qkv_dtype == HGA_BF16 ? 2 : 4; }
+
+// ------------------------------------------------------------------ workspace plans
+struct RoutePlan {
+  int n_units, slices, cps;
+  size_t scores_off, gscores_off, counters_off, bytes;
+};
+
+RoutePlan plan_route(const KParams& kp, int64_t nq, size_t base) {
+  RoutePlan r{};
+  r.n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
+  r.cps = route_chunks_per_slice(kp, nq);
+  const int64_t max_cand = std::max<int64_t>(0, kp.n_chunks_cap - 1 - kp.n_local - kp.n_sink);
+  r.slices = static_cast<int>(std::max<int64_t>(1, cdiv(max_cand, r.cps)));
+  const size_t units = static_cast<size_t>(kp.B) * kp.Hkv * r.n_units;
+  size_t off = base;
+  r.counters_off = off;
+  off = align256(off + units * sizeof(uint32_t));
+  r.scores_off = off;
+  off = align256(off + units * kp.n_chunks_cap * sizeof(float));
+  r.gscores_off = off;
+  off = align256(off + units * static_cast<size_t>(kp.top_k) * kp.m * sizeof(float));
+  r.bytes = off - base;
+  return r;
+}
+
+struct AttendPlan {
+  int splits1, splits2, tps, parts_total;  // splits2 > 0 only for the two-part (offload) schedule
+  size_t counters_off, partials_off, bytes;
+};
+
+AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base) {
+  AttendPlan a{};
+  const int64_t rows = static_cast<int64_t>(kp.B) * kp.Hkv * nq;
+  const int max_tiles = static_cast<int>(cdiv(attend_max_slots(kp), kTileSlots));
+  const int64_t target = 2048;  // workgroups wanted to fill 256 CUs several times over
+  int splits = static_cast<int>(std::min<int64_t>(max_tiles, std::max<int64_t>(1, cdiv(target, rows))));
+  a.tps = static_cast<int>(cdiv(max_tiles, splits));
+  if (two_part) {
+    const int ft = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kTileSlots));
+    const int rt = static_cast<int>(std::max<int64_t>(1, cdiv(static_cast<int64_t>(kp.top_g) * kp.G, kTileSlots)));
+    a.splits1 = static_cast<int>(cdiv(ft, a.tps));
+    a.splits2 = static_cast<int>(cdiv(rt, a.tps));
+    a.parts_total = a.splits1 + a.splits2;
+  } else {
+    a.splits1 = static_cast<int>(cdiv(max_tiles, a.tps));
+    a.splits2 = 0;
+    a.parts_total = a.splits1;
+  }
+  size_t off = base;
+  a.counters_off = off;
+  off = align256(off + static_cast<size_t>(rows) * sizeof(uint32_t));
+  a.partials_off = off;
+  if (a.parts_total > 1)
+    off = align256(off + static_cast<size_t>(rows) * a.parts_total * kp.gq * (kp.d + 2) * sizeof(float));
+  a.bytes = off - base;
+  return a;
+}
+
+struct IdxPlan {
+  size_t ci_off, gi_off, bytes;
+};
+
+IdxPlan plan_idx(const KParams& kp, int n_units, size_t base) {
+  IdxPlan r{};
+  const size_t units = static_cast<size_t>(kp.B) * kp.Hkv * n_units;
+  size_t off = base;
+  r.ci_off = off;
+  off = align256(off + units * std::max(1, kp.top_k) * sizeof(int32_t));
+  r.gi_off = off;
+  off = align256(off + units * std::max(1, kp.top_g) * sizeof(int32_t));
+  r.bytes = off - base;
+  return r;
+}
+
+struct FullPlan {
+  RoutePlan route;
+  AttendPlan attend;
+  IdxPlan idx;
+  size_t bytes;
+};
+
+FullPlan plan(const KParams& kp, int op, int64_t nq) {
+  FullPlan f{};
+  size_t off = 0;
+  const bool needs_route = op == HGA_OP_ROUTE || op == HGA_OP_PREFILL || op == HGA_OP_DECODE ||
+                           op == HGA_OP_DECODE_OFFLOAD;
+  const bool needs_attend = op == HGA_OP_ATTEND || op == HGA_OP_PREFILL || op == HGA_OP_DECODE ||
+                            op == HGA_OP_DECODE_OFFLOAD;
+  const bool needs_idx = op == HGA_OP_PREFILL || op == HGA_OP_DECODE || op == HGA_OP_DECODE_OFFLOAD;
+  // counters first, so that zeroing the head of the workspace is enough
+  if (needs_route) {
+    f.route = plan_route(kp, nq, off);
+    off += f.route.bytes;
+  }
+  if (needs_attend) {
+    f.attend = plan_attend(kp, nq, op == HGA_OP_DECODE_OFFLOAD, off);
+    off += f.attend.bytes;
+  }
+  if (needs_idx) {
+    f.idx = plan_idx(kp, f.route.n_units, off);
+    off += f.idx.bytes;
+  }
+  f.bytes = off;
+  return f;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+hga_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return HGA_OK;
+  if (!ws) return fail(HGA_ERR_WORKSPACE, "workspace is null (need %zu bytes)", need);
+  if (!aligned16(ws)) return fail(HGA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if (ws_bytes < need) return fail(HGA_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+  return HGA_OK;
+}
+
+#define HGA_CHECK_PTR(ptr)                                                         \
+  do {                                                                             \
+    if (!(ptr)) return fail(HGA_ERR_ARG, "%s is null", #ptr);                      \
+    if (!aligned16(ptr)) return fail(HGA_ERR_ALIGN, "%s not 16-byte aligned", #ptr); \
+  } while (0)
+
+#define HGA_TRY_HIP(expr, what)              \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+RouteArgs route_args(const KParams& kp, const FullPlan& f, void* ws, const void* Q, int64_t nq,
+                     const int32_t* q_pos, int32_t bias, const float* cs, const float* gs,
+                     int32_t* ci, int32_t* gi, float* scores_out) {
+  RouteArgs a{};
+  a.kp = kp;
+  a.Q = Q;
+  a.nq = nq;
+  a.q_pos = q_pos;
+  a.pos_bias = bias;
+  a.chunk_sum = cs;
+  a.group_sum = gs;
+  a.n_units = f.route.n_units;
+  a.slices = f.route.slices;
+  a.chunks_per_slice = f.route.cps;
+  a.scores = at<float>(ws, f.route.scores_off);
+  a.gscores = at<float>(ws, f.route.gscores_off);
+  a.counters = at<uint32_t>(ws, f.route.counters_off);
+  a.chunk_idx = ci;
+  a.group_idx = gi;
+  a.scores_out = scores_out;
+  a.build_summary = 0;
+  return a;
+}
+
+AttendArgs attend_args(const KParams& kp, const FullPlan& f, void* ws, const void* Q, int64_t nq,
+                       const int32_t* q_pos, int32_t bias, const void* K, const void* V,
+                       const int32_t* gi, int n_units, void* O, float* lse, bool out_bf16) {
+  AttendArgs a{};
+  a.kp = kp;
+  a.Q = Q;
+  a.nq = nq;
+  a.q_pos = q_pos;
+  a.pos_bias = bias;
+  a.K = K;
+  a.V = V;
+  a.kv.base = K;
+  a.kv.bh_rows = kp.n_cap;
+  a.kv.ring = 0;
+  a.group_idx = gi;
+  a.n_units = n_units;
+  a.O = O;
+  a.lse = lse;
+  a.out_bf16 = out_bf16 ? 1 : 0;
+  a.splits = f.attend.splits1;
+  a.tiles_per_split = f.attend.tps;
+  a.part = 0;
+  a.part_offset = 0;
+  a.parts_total = f.attend.parts_total;
+  a.partials = at<float>(ws, f.attend.partials_off);
+  a.counters = at<uint32_t>(ws, f.attend.counters_off);
+  return a;
+}
+
+hga_status check_nq(const KParams& kp, int64_t nq) {
+  if (nq < 1) return fail(HGA_ERR_SHAPE, "nq must be >= 1");
+  if (nq > 1 && nq % kp.C != 0) return fail(HGA_ERR_SHAPE, "prefill nq %lld must be a multiple of C", (long long)nq);
+  if (nq > kp.n_cap) return fail(HGA_ERR_SHAPE, "nq exceeds n_cap");
+  if (nq > 1 && nq / kp.C > 65535) return fail(HGA_ERR_UNSUPPORTED, "too many query chunks");
+  if (nq > 65535 && nq > 1) {
+    // grid.y carries the query row in the attention kernel
+    return fail(HGA_ERR_UNSUPPORTED, "nq %lld > 65535 rows per call", (long long)nq);
+  }
+  return HGA_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* hga_last_error(void) { return g_err.c_str(); }
+
+const char* hga_version(void) { return "hga-mi355x 0.1 (gfx950)"; }
+
+size_t hga_workspace_size(const hga_params* p, int32_t op, int64_t nq, int64_t n_cap) {
+  KParams kp;
+  if (build_kparams(p, n_cap, kp) != HGA_OK) return 0;
+  if (op < HGA_OP_ROUTE || op > HGA_OP_DECODE_OFFLOAD) {
+    fail(HGA_ERR_ARG, "unknown op %d", op);
+    return 0;
+  }
+  if (op == HGA_OP_DECODE || op == HGA_OP_DECODE_OFFLOAD) nq = 1;
+  if (check_nq(kp, nq) != HGA_OK) return 0;
+  ok();
+  return plan(kp, op, nq).bytes;
+}
+
+hga_status hga_build_summaries(const hga_params* p, const void* K, int64_t n_cap, int32_t chunk_begin,
+                               int32_t chunk_end, int32_t k_is_rotated, void* K_rot_out,
+                               float* chunk_sum, float* group_sum, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n_cap, kp);
+  if (s != HGA_OK) return s;
+  HGA_CHECK_PTR(K);
+  HGA_CHECK_PTR(chunk_sum);
+  HGA_CHECK_PTR(group_sum);
+  if (K_rot_out && !aligned16(K_rot_out)) return fail(HGA_ERR_ALIGN, "K_rot_out not 16-byte aligned");
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > kp.n_chunks_cap)
+    return fail(HGA_ERR_SHAPE, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, kp.n_chunks_cap);
+  if (k_is_rotated && K_rot_out) return fail(HGA_ERR_ARG, "K_rot_out needs k_is_rotated = 0");
+  if (static_cast<int64_t>(kp.B) * kp.Hkv > 65535) return fail(HGA_ERR_UNSUPPORTED, "B*Hkv > 65535");
+  SummariesArgs a{};
+  a.kp = kp;
+  a.K = K;
+  a.Krot = K_rot_out;
+  a.chunk_sum = chunk_sum;
+  a.group_sum = group_sum;
+  a.chunk_begin = chunk_begin;
+  a.chunk_end = chunk_end;
+  a.rotated = k_is_rotated ? 1 : 0;
+  HGA_TRY_HIP(launch_summaries(a, p->qkv_dtype == HGA_BF16, static_cast<hipStream_t>(stream)), "summaries");
+  return ok();
+}
+
+hga_status hga_route(const hga_params* p, const void* Q, int64_t nq, const int32_t* q_pos,
+                     const float* chunk_sum, const float* group_sum, int64_t n_cap, int32_t* chunk_idx,
+                     int32_t* group_idx, float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n_cap, kp);
+  if (s != HGA_OK) return s;
+  if ((s = check_nq(kp, nq)) != HGA_OK) return s;
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(chunk_sum);
+  HGA_CHECK_PTR(group_sum);
+  HGA_CHECK_PTR(chunk_idx);
+  HGA_CHECK_PTR(group_idx);
+  if (!q_pos) return fail(HGA_ERR_ARG, "q_pos is null");
+  if (scores_out && nq != 1) return fail(HGA_ERR_ARG, "scores_out is for decode (nq == 1) only");
+  FullPlan f = plan(kp, HGA_OP_ROUTE, nq);
+  if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  RouteArgs a = route_args(kp, f, ws, Q, nq, q_pos, 0, chunk_sum, group_sum, chunk_idx, group_idx, scores_out);
+  HGA_TRY_HIP(launch_route_scan(a, p->qkv_dtype == HGA_BF16, p->qkv_dtype == HGA_BF16,
+                                static_cast<hipStream_t>(stream)),
+              "route");
+  return ok();
+}
+
+hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int32_t* q_pos, const void* K,
+                      const void* V, int64_t n_cap, const int32_t* group_idx, void* O, float* lse_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n_cap, kp);
+  if (s != HGA_OK) return s;
+  if ((s = check_nq(kp, nq)) != HGA_OK) return s;
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(K);
+  HGA_CHECK_PTR(V);
+  HGA_CHECK_PTR(O);
+  if (kp.top_g > 0 && !group_idx) return fail(HGA_ERR_ARG, "group_idx is null");
+  if (!q_pos) return fail(HGA_ERR_ARG, "q_pos is null");
+  if (lse_out && !aligned16(lse_out)) return fail(HGA_ERR_ALIGN, "lse_out not 16-byte aligned");
+  FullPlan f = plan(kp, HGA_OP_ATTEND, nq);
+  if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  const int n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
+  AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, group_idx, n_units, O, lse_out,
+                             p->out_dtype == HGA_BF16);
+  HGA_TRY_HIP(launch_attend_splitk(a, p->qkv_dtype == HGA_BF16, static_cast<hipStream_t>(stream)), "attend");
+  return ok();
+}
+
+hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const void* V, int64_t n,
+                       float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx, int32_t* group_idx,
+                       void* ws, size_t ws_bytes, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n, kp);
+  if (s != HGA_OK) return s;
+  if ((s = check_nq(kp, n)) != HGA_OK) return s;
+  if (n < kp.C) return fail(HGA_ERR_SHAPE, "prefill needs n >= C");
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(K);
+  HGA_CHECK_PTR(V);
+  HGA_CHECK_PTR(O);
+  HGA_CHECK_PTR(chunk_sum);
+  HGA_CHECK_PTR(group_sum);
+  if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
+  if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
+  FullPlan f = plan(kp, HGA_OP_PREFILL, n);
+  if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = p->qkv_dtype == HGA_BF16;
+  int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
+  int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
+
+  SummariesArgs sa{};
+  sa.kp = kp;
+  sa.K = K;
+  sa.chunk_sum = chunk_sum;
+  sa.group_sum = group_sum;
+  sa.chunk_begin = 0;
+  sa.chunk_end = kp.n_chunks_cap;
+  sa.rotated = 1;
+  HGA_TRY_HIP(launch_summaries(sa, bf, st), "summaries");
+  RouteArgs ra = route_args(kp, f, ws, Q, n, nullptr, 0, chunk_sum, group_sum, ci, gi, nullptr);
+  HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
+  AttendArgs aa = attend_args(kp, f, ws, Q, n, nullptr, 0, K, V, gi, f.route.n_units, O, nullptr,
+                              p->out_dtype == HGA_BF16);
+  HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+  return ok();
+}
+
+hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const void* V, int64_t n_cap,
+                      const int32_t* seq_len, float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx,
+                      int32_t* group_idx, void* ws, size_t ws_bytes, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n_cap, kp);
+  if (s != HGA_OK) return s;
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(K);
+  HGA_CHECK_PTR(V);
+  HGA_CHECK_PTR(O);
+  HGA_CHECK_PTR(chunk_sum);
+  HGA_CHECK_PTR(group_sum);
+  if (!seq_len) return fail(HGA_ERR_ARG, "seq_len is null");
+  if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
+  if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
+  FullPlan f = plan(kp, HGA_OP_DECODE, 1);
+  if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = p->qkv_dtype == HGA_BF16;
+  int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
+  int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
+  RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);
+  ra.build_summary = 1;
+  ra.ksrc.base = K;
+  ra.ksrc.bh_rows = kp.n_cap;
+  ra.ksrc.ring = 0;
+  ra.chunk_sum_w = chunk_sum;
+  ra.group_sum_w = group_sum;
+  HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
+  AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K, V, gi, 1, O, nullptr, p->out_dtype == HGA_BF16);
+  HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+  return ok();
+}
+
+hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_host, const void* V_host,
+                              const void* K_hot, const void* V_hot, int64_t n_cap, const int32_t* seq_len,
+                              float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx,
+                              int32_t* group_idx, void* staging, size_t staging_bytes, void* ws,
+                              size_t ws_bytes, void* stream, void* copy_stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n_cap, kp);
+  if (s != HGA_OK) return s;
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(K_host);
+  HGA_CHECK_PTR(V_host);
+  HGA_CHECK_PTR(K_hot);
+  HGA_CHECK_PTR(V_hot);
+  HGA_CHECK_PTR(O);
+  HGA_CHECK_PTR(chunk_sum);
+  HGA_CHECK_PTR(group_sum);
+  HGA_CHECK_PTR(staging);
+  if (!seq_len) return fail(HGA_ERR_ARG, "seq_len is null");
+  if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
+  if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
+  const size_t half = static_cast<size_t>(kp.B) * kp.Hkv * std::max(1, kp.top_g) * kp.G * kp.d * elem_bytes(p);
+  if (staging_bytes < 2 * half)
+    return fail(HGA_ERR_WORKSPACE, "staging has %zu bytes, need %zu", staging_bytes, 2 * half);
+  FullPlan f = plan(kp, HGA_OP_DECODE_OFFLOAD, 1);
+  if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t cst = static_cast<hipStream_t>(copy_stream);
+  const bool bf = p->qkv_dtype == HGA_BF16;
+  int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
+  int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
+  void* Kst = staging;
+  void* Vst = static_cast<char*>(staging) + half;
+
+  // events ordering the copy stream between routing and the routed attention
+  thread_local hipEvent_t ev_routed = nullptr, ev_copied = nullptr;
+  if (!ev_routed) {
+    HGA_TRY_HIP(hipEventCreateWithFlags(&ev_routed, hipEventDisableTiming), "event create");
+    HGA_TRY_HIP(hipEventCreateWithFlags(&ev_copied, hipEventDisableTiming), "event create");
+  }
+
+  const int64_t hot_rows = static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C;
+  RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);
+  ra.build_summary = 1;
+  ra.ksrc.base = K_hot;
+  ra.ksrc.bh_rows = hot_rows;
+  ra.ksrc.ring = 1;
+  ra.chunk_sum_w = chunk_sum;
+  ra.group_sum_w = group_sum;
+  HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
+  HGA_TRY_HIP(hipEventRecord(ev_routed, st), "event record");
+  HGA_TRY_HIP(hipStreamWaitEvent(cst, ev_routed, 0), "stream wait");
+  GatherArgs ga{};
+  ga.kp = kp;
+  ga.K_host = K_host;
+  ga.V_host = V_host;
+  ga.group_idx = gi;
+  ga.K_stage = Kst;
+  ga.V_stage = Vst;
+  ga.elem_bytes = static_cast<int32_t>(elem_bytes(p));
+  HGA_TRY_HIP(launch_gather_groups(ga, cst), "gather");
+  HGA_TRY_HIP(hipEventRecord(ev_copied, cst), "event record");
+
+  // forced (hot) slots overlap the copy; routed slots read the staging buffer
+  AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K_hot, V_hot, gi, 1, O, nullptr,
+                              p->out_dtype == HGA_BF16);
+  aa.kv.base = K_hot;
+  aa.kv.bh_rows = hot_rows;
+  aa.kv.ring = 1;
+  aa.K_stage = Kst;
+  aa.V_stage = Vst;
+  aa.part = 1;
+  aa.splits = f.attend.splits1;
+  aa.part_offset = 0;
+  HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend (hot)");
+  HGA_TRY_HIP(hipStreamWaitEvent(st, ev_copied, 0), "stream wait");
+  aa.part = 2;
+  aa.splits = f.attend.splits2;
+  aa.part_offset = f.attend.splits1;
+  HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend (routed)");
+  return ok();
+}
+
+}  // extern "C"

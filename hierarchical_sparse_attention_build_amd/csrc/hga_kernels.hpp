@@ -1,0 +1,96 @@
+// Launch interfaces of the HGA kernels (host side of each .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hga_kparams.hpp"
+
+namespace hga {
+
+struct SummariesArgs {
+  KParams kp;
+  const void* K;      // [B, Hkv, n_cap, d]
+  void* Krot;         // nullable (raw mode): RoPE'd rows written here
+  float* chunk_sum;   // [B, Hkv, n_chunks_cap, d]
+  float* group_sum;   // [B, Hkv, n_chunks_cap * m, d]
+  int32_t chunk_begin, chunk_end, rotated;
+};
+
+// Where the rows of a chunk live for the fused summary update of a decode step.
+struct RowSource {
+  const void* base;       // rows of (b, kv head) bh start at base + bh * bh_rows * d
+  int64_t bh_rows;
+  int32_t ring;           // 0: chunk c at row c*C; 1: hot-window ring (sink slots, then n_local+1 ring slots)
+};
+
+struct RouteArgs {
+  KParams kp;
+  const void* Q;          // [B, Hq, nq, d]
+  int64_t nq;
+  const int32_t* q_pos;   // [B]: position of query row 0 is q_pos[b] + pos_bias
+  int32_t pos_bias;
+  const float* chunk_sum;
+  const float* group_sum;
+  int32_t n_units;        // units per (b, kv head)
+  int32_t slices;         // scan workgroups per unit
+  int32_t chunks_per_slice;
+  float* scores;          // ws [B*Hkv*n_units, n_chunks_cap]
+  float* gscores;         // ws [B*Hkv*n_units, top_k*m]
+  uint32_t* counters;     // ws [B*Hkv*n_units], zero between calls
+  int32_t* chunk_idx;     // [B*Hkv*n_units, top_k]
+  int32_t* group_idx;     // [B*Hkv*n_units, top_g]
+  float* scores_out;      // nullable [B*Hkv, n_chunks_cap] (decode)
+  // fused summary update (decode only): when the query completes its chunk
+  int32_t build_summary;
+  RowSource ksrc;
+  float* chunk_sum_w;
+  float* group_sum_w;
+};
+
+struct AttendArgs {
+  KParams kp;
+  const void* Q;          // [B, Hq, nq, d]
+  int64_t nq;
+  const int32_t* q_pos;
+  int32_t pos_bias;
+  const void* K;          // forced rows (and routed rows unless staged)
+  const void* V;
+  RowSource kv;           // layout of K/V rows for forced chunks (ring = hot window)
+  const void* K_stage;    // nullable: routed groups packed [B*Hkv, top_g*G, d]
+  const void* V_stage;
+  const int32_t* group_idx;  // [B*Hkv*n_units, top_g]
+  int32_t n_units;
+  void* O;                // [B, Hq, nq, d]
+  float* lse;             // nullable [B, Hq, nq]
+  int32_t out_bf16;
+  int32_t splits;         // workgroups per (bh, query row) in this launch
+  int32_t tiles_per_split;
+  int32_t part;           // 0 all slots, 1 forced slots only, 2 routed slots only
+  int32_t part_offset;    // partial slot of this launch's split 0
+  int32_t parts_total;    // partial slots per (bh, row) over all launches
+  float* partials;        // ws
+  uint32_t* counters;     // ws [B*Hkv*nq]
+};
+
+struct GatherArgs {
+  KParams kp;
+  const void* K_host;     // pinned host [B, Hkv, n_cap, d]
+  const void* V_host;
+  const int32_t* group_idx;  // [B*Hkv, top_g]
+  void* K_stage;          // [B*Hkv, top_g*G, d]
+  void* V_stage;
+  int32_t elem_bytes;
+};
+
+hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st);
+hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipStream_t st);
+hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);
+hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
+
+// Workgroup counts and tiling chosen by the host for a given shape.
+constexpr int kTileSlots = 64;     // K/V rows per attention tile
+int route_chunks_per_slice(const KParams& kp, int64_t nq);
+int attend_max_slots(const KParams& kp);
+
+}  // namespace hga

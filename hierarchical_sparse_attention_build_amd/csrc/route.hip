@@ -1,0 +1,218 @@
+// Steps 2-3 of HGA: two-level routing on the vector ALUs.
+// [HGA technical summary (it), Meccanismo Core, item 2, first two bullets]:
+// the current chunk (or decode query) scores the compact chunk-summary table and
+// keeps the top-k chunks; inside them it scores the group summaries and keeps
+// the top-g groups.
+//
+// Layout of the work: each (b, kv head, unit) has its candidate chunks
+// [n_sink, j - n_local) split over `slices` workgroups.  A workgroup streams
+// its slice of the fp32 summary table once (D/4 lanes per summary row, one
+// 16-byte load per lane), scores each row against every query vector of the
+// unit (max of the dot products, times 1/sqrt(d)) and writes the scores to the
+// workspace.  The last workgroup of the unit to finish (device-scope counter)
+// selects the top-k, scores the groups of the routed chunks and selects the
+// top-g.  The scan is bound by HBM bandwidth in decode.
+//
+// In a decode step one extra workgroup per (b, kv head) summarises the chunk
+// that the query completes, so a decode loop keeps the tables current.
+#include "hga_kernels.hpp"
+#include "hga_summarize.hpp"
+
+namespace hga {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kQB = 4;      // query vectors per register batch
+constexpr int kRounds = 8;  // summary rows in flight per lane
+
+constexpr int kLdsScores = 4096;  // scores staged in LDS for the selections
+
+struct RouteSmem {
+  TopkSmem<kRouteThreads> topk;
+  int sel_chunks[1024];
+  int sel_groups[1024];
+  float scores[kLdsScores];
+  int is_last;
+};
+
+// put(i, max over the unit's query vectors of q . row(i) / sqrt(d)) for i in
+// [0, n).  row(i) is a float32 row of D values.
+template <typename T, int D, typename RowFn, typename PutFn>
+__device__ void score_rows(const T* __restrict__ qbase, int64_t head_stride, int rows_per_head,
+                           int nqv, const KParams& kp, int n, RowFn row, PutFn put) {
+  constexpr int LPC = D / 4;             // lanes per row (one float4 each)
+  constexpr int CPW = kWave / LPC;       // rows per wave per round
+  constexpr int CPB = CPW * kRouteWaves; // rows per block per round
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int sub = lane % LPC;
+  const int cl = lane / LPC;
+  for (int base = 0; base < n; base += CPB * kRounds) {
+    float4 s[kRounds];
+    float mx[kRounds];
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const int i = base + k * CPB + wid * CPW + cl;
+      s[k] = i < n ? reinterpret_cast<const float4*>(row(i))[sub] : make_float4(0.f, 0.f, 0.f, 0.f);
+      mx[k] = -__builtin_huge_valf();
+    }
+    for (int v0 = 0; v0 < nqv; v0 += kQB) {
+      float4 q[kQB];
+#pragma unroll
+      for (int v = 0; v < kQB; ++v) {
+        const int vv = v0 + v < nqv ? v0 + v : nqv - 1;
+        const T* qr = qbase + (vv / rows_per_head) * head_stride +
+                      static_cast<int64_t>(vv % rows_per_head) * D + sub * 4;
+        q[v] = make_float4(elem<T>::get(qr, 0), elem<T>::get(qr, 1), elem<T>::get(qr, 2),
+                           elem<T>::get(qr, 3));
+      }
+#pragma unroll
+      for (int k = 0; k < kRounds; ++k) {
+#pragma unroll
+        for (int v = 0; v < kQB; ++v) {
+          float acc = q[v].x * s[k].x;
+          acc = fmaf(q[v].y, s[k].y, acc);
+          acc = fmaf(q[v].z, s[k].z, acc);
+          acc = fmaf(q[v].w, s[k].w, acc);
+          acc = group_sum<LPC>(acc);
+          mx[k] = fmaxf(mx[k], acc);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) {
+      const int i = base + k * CPB + wid * CPW + cl;
+      if (i < n && sub == 0) put(i, mx[k] * kp.inv_sqrt_d);
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) {
+  const KParams& kp = a.kp;
+  const int bh = blockIdx.z;
+  const int u = blockIdx.y;
+  const int x = blockIdx.x;
+  const int b = bh / kp.Hkv;
+  const int h = bh % kp.Hkv;
+  const int t0 = (a.q_pos ? a.q_pos[b] : 0) + a.pos_bias;
+  const bool prefill = a.nq > 1;
+  const int j = t0 / kp.C + (prefill ? u : 0);
+
+  __shared__ RouteSmem sm;
+
+  // positions outside the cache (or a prefill block not aligned to C): the unit
+  // gets empty index lists and nothing else happens
+  const int64_t t_last = static_cast<int64_t>(t0) + (prefill ? a.nq - 1 : 0);
+  if (t0 < 0 || t_last >= kp.n_cap || (prefill && t0 % kp.C != 0)) {
+    if (x == 0) {
+      const int64_t unit = static_cast<int64_t>(bh) * a.n_units + u;
+      for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads) a.chunk_idx[unit * kp.top_k + i] = -1;
+      for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) a.group_idx[unit * kp.top_g + i] = -1;
+    }
+    return;
+  }
+
+  if (x == a.slices) {
+    // fused summary update: this decode query completes chunk j
+    if (!a.build_summary || (t0 + 1) % kp.C != 0) return;
+    const int c = j;
+    int64_t slot = c;
+    if (a.ksrc.ring && c >= kp.n_sink) slot = kp.n_sink + (c - kp.n_sink) % (kp.n_local + 1);
+    const T* rows = static_cast<const T*>(a.ksrc.base) +
+                    (static_cast<int64_t>(bh) * a.ksrc.bh_rows + slot * kp.C) * D;
+    summarize_chunk<T, D>(rows, c, kp, true, nullptr,
+                          a.chunk_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap + c) * D,
+                          a.group_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m +
+                                           static_cast<int64_t>(c) * kp.m) * D);
+    return;
+  }
+
+  const int64_t unit = static_cast<int64_t>(bh) * a.n_units + u;
+  const int nM = max(0, j - kp.n_local - kp.n_sink);
+  const int c_lo = kp.n_sink + x * a.chunks_per_slice;
+  const int n_here = max(0, min(kp.n_sink + nM, c_lo + a.chunks_per_slice) - c_lo);
+
+  const int rows_per_head = prefill ? kp.C : 1;
+  const int nqv = kp.gq * rows_per_head;
+  const T* qbase = static_cast<const T*>(a.Q) +
+                   ((static_cast<int64_t>(b) * kp.Hq + static_cast<int64_t>(h) * kp.gq) * a.nq +
+                    (prefill ? static_cast<int64_t>(u) * kp.C : 0)) * D;
+  const int64_t head_stride = a.nq * D;
+
+  float* sc = a.scores + unit * kp.n_chunks_cap;
+  const float* ctab = a.chunk_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * D;
+  float* sc_out = a.scores_out ? a.scores_out + static_cast<int64_t>(bh) * kp.n_chunks_cap : nullptr;
+  if (n_here > 0) {
+    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, kp, n_here,
+                     [&](int i) { return ctab + static_cast<int64_t>(c_lo + i) * D; },
+                     [&](int i, float v) {
+                       st_agent(sc + c_lo + i, v);
+                       if (sc_out) sc_out[c_lo + i] = v;
+                     });
+  }
+
+  // ---- last workgroup of the unit does the selections
+  if (!arrive_last(&a.counters[unit], static_cast<uint32_t>(a.slices), &sm.is_last)) return;
+
+  int cnt;
+  const float* scand = sc + kp.n_sink;
+  if (nM <= kLdsScores) {
+    for (int i = threadIdx.x; i < nM; i += kRouteThreads) sm.scores[i] = ld_agent(scand + i);
+    __syncthreads();
+    cnt = block_topk<kRouteThreads>([&](int i) { return sm.scores[i]; }, nM, kp.top_k, sm.sel_chunks, sm.topk);
+  } else {
+    cnt = block_topk<kRouteThreads>([&](int i) { return ld_agent(scand + i); }, nM, kp.top_k, sm.sel_chunks,
+                                    sm.topk);
+  }
+  int32_t* ci = a.chunk_idx + unit * kp.top_k;
+  for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads)
+    ci[i] = i < cnt ? kp.n_sink + sm.sel_chunks[i] : -1;
+
+  const int nG = cnt * kp.m;
+  const int m = kp.m;
+  const float* gtab = a.group_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m * D;
+  float* gsc = nG <= kLdsScores ? sm.scores : a.gscores + unit * static_cast<int64_t>(kp.top_k) * kp.m;
+  __syncthreads();  // sm.scores is reused for the group scores
+  if (nG > 0) {
+    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, kp, nG,
+                     [&](int i) {
+                       const int64_t gid = static_cast<int64_t>(kp.n_sink + sm.sel_chunks[i / m]) * m + i % m;
+                       return gtab + gid * D;
+                     },
+                     [&](int i, float v) { gsc[i] = v; });
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int gcnt = block_topk<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
+  int32_t* gi = a.group_idx + unit * kp.top_g;
+  for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) {
+    int32_t v = -1;
+    if (i < gcnt) {
+      const int sg = sm.sel_groups[i];
+      v = (kp.n_sink + sm.sel_chunks[sg / m]) * m + sg % m;
+    }
+    gi[i] = v;
+  }
+}
+
+int route_chunks_per_slice(const KParams& kp, int64_t nq) {
+  // one round-set of rows per lane: kRounds rows of D/4 lanes each per wave
+  const int per_round = (kWave / (kp.d / 4)) * kRouteWaves;
+  (void)nq;
+  return per_round * kRounds;
+}
+
+template <typename T, int D>
+static hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
+  dim3 grid(a.slices + (a.build_summary ? 1 : 0), a.n_units, a.kp.B * a.kp.Hkv);
+  route_scan_kernel<T, D><<<grid, kRouteThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool /*bf16_k*/, hipStream_t st) {
+  if (bf16_q) return a.kp.d == 64 ? launch_t<bf16, 64>(a, st) : launch_t<bf16, 128>(a, st);
+  return a.kp.d == 64 ? launch_t<float, 64>(a, st) : launch_t<float, 128>(a, st);
+}
+
+}  // namespace hga

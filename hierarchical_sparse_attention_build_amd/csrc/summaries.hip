@@ -1,0 +1,41 @@
+// Step 1 of HGA: RoPE-aware chunk and group key summaries.
+// [HGA technical summary (it), Meccanismo Core, item 3].  One workgroup
+// summarises one chunk of one (b, kv head); see hga_summarize.hpp.
+#include "hga_kernels.hpp"
+#include "hga_summarize.hpp"
+
+namespace hga {
+
+constexpr int kSumThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSumThreads) void summaries_kernel(const T* __restrict__ K,
+                                                                T* __restrict__ Krot,
+                                                                float* __restrict__ chunk_sum,
+                                                                float* __restrict__ group_sum,
+                                                                int chunk_begin, int rotated,
+                                                                KParams kp) {
+  const int c = chunk_begin + blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t row0 = bh * kp.n_cap + static_cast<int64_t>(c) * kp.C;
+  summarize_chunk<T, D>(K + row0 * D, c, kp, rotated != 0, Krot ? Krot + row0 * D : nullptr,
+                        chunk_sum + (bh * kp.n_chunks_cap + c) * D,
+                        group_sum + (bh * kp.n_chunks_cap * kp.m + static_cast<int64_t>(c) * kp.m) * D);
+}
+
+template <typename T, int D>
+static hipError_t launch_summaries_t(const SummariesArgs& a, hipStream_t st) {
+  dim3 grid(a.chunk_end - a.chunk_begin, a.kp.B * a.kp.Hkv);
+  summaries_kernel<T, D><<<grid, kSumThreads, 0, st>>>(
+      static_cast<const T*>(a.K), static_cast<T*>(a.Krot), a.chunk_sum, a.group_sum, a.chunk_begin,
+      a.rotated, a.kp);
+  return hipGetLastError();
+}
+
+hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st) {
+  if (a.chunk_end <= a.chunk_begin) return hipSuccess;
+  if (bf16_in) return a.kp.d == 64 ? launch_summaries_t<bf16, 64>(a, st) : launch_summaries_t<bf16, 128>(a, st);
+  return a.kp.d == 64 ? launch_summaries_t<float, 64>(a, st) : launch_summaries_t<float, 128>(a, st);
+}
+
+}  // namespace hga

@@ -179,7 +179,8 @@ def make(s: Spec | str, **overrides) -> Workload:
                 needles[(b, h)] = np.sort(cs)
         if s.needles and s.mode == "prefill":
             for h in range(Hkv):
-                cs = rng.choice(np.arange(1, min(14, n_chunks - 2)), size=s.needles, replace=False)
+                pool = np.arange(1, max(2, min(14, n_chunks - 2)))
+                cs = rng.choice(pool, size=min(s.needles, len(pool)), replace=False)
                 for c in cs:
                     u = _unit(rng, d)
                     Kb[h, c * C:(c + 1) * C] += (2.0 * u).astype(Kb.dtype)

@@ -1,0 +1,391 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every case prints its name, shape and seed before touching the GPU.  Inputs are
+the seeded workloads; the oracle runs in float64 on the same rounded values.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from hierarchical_sparse_attention_build_amd import workloads as W
+from tests.hga_testutil import (GAP, TOL, cfg_of, check_routing, dev, f64, max_abs, params_of,
+                                say)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hga():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hierarchical_sparse_attention_build_amd import hga as H
+    H.lib()
+    return H
+
+
+def _summ_tables(s):
+    nC = s.n_tokens // s.chunk_size
+    m = s.chunk_size // s.group_size
+    cs = torch.full((s.batch, s.n_kv_heads, nC, s.head_dim), float("nan"), device="cuda")
+    gs = torch.full((s.batch, s.n_kv_heads, nC * m, s.head_dim), float("nan"), device="cuda")
+    return cs, gs
+
+
+# --------------------------------------------------------------------------- summaries
+@pytest.mark.parametrize("name,over", [
+    ("tiny_prefill_fp32", {}),
+    ("decode_32k", {"batch": 2, "n_tokens": 4096}),
+    ("tiny_prefill_fp32", {"group_size": 1, "n_tokens": 256}),
+    ("decode_32k", {"batch": 1, "n_tokens": 2048, "chunk_size": 32, "group_size": 8, "head_dim": 64}),
+])
+def test_summaries(hga, name, over):
+    s = W.spec(name, **over)
+    say(f"[summaries] {name} {over} seed={s.seed}")
+    w = W.make(s)
+    p = params_of(s)
+    K = dev(w.K, s.dtype)
+    cs, gs = _summ_tables(s)
+    nC = s.n_tokens // s.chunk_size
+    hga.build_summaries(p, K, s.n_tokens, 0, nC, cs, gs)
+    torch.cuda.synchronize()
+    ocs, ogs = O.build_summaries(f64(w.K, s.dtype), cfg_of(s))
+    e1, e2 = max_abs(cs.cpu().numpy(), ocs), max_abs(gs.cpu().numpy(), ogs)
+    say(f"  chunk max-abs {e1:.3e}  group max-abs {e2:.3e}")
+    assert e1 < 1e-5 and e2 < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_summaries_raw_keys(hga, dtype):
+    """Raw projected keys: literal form with absolute angles, plus the RoPE'd copy."""
+    s = W.spec("tiny_prefill_fp32", dtype=dtype, n_tokens=2048, chunk_size=64, group_size=16)
+    say(f"[summaries raw] dtype={dtype} seed={s.seed}")
+    w = W.make(s)
+    p = params_of(s)
+    K = dev(w.K, s.dtype)
+    Krot = torch.empty_like(K)
+    cs, gs = _summ_tables(s)
+    nC = s.n_tokens // s.chunk_size
+    # a sub-range first: only chunks [3, nC) are written
+    hga.build_summaries(p, K, s.n_tokens, 3, nC, cs, gs, k_is_rotated=False, K_rot_out=Krot)
+    torch.cuda.synchronize()
+    cfg = cfg_of(s)
+    Kf = f64(w.K, s.dtype)
+    ocs, ogs = O.build_summaries(Kf, cfg, k_is_rotated=False, form="literal")
+    m = s.chunk_size // s.group_size
+    e1 = max_abs(cs[:, :, 3:].cpu().numpy(), ocs[:, :, 3:])
+    e2 = max_abs(gs[:, :, 3 * m:].cpu().numpy(), ogs[:, :, 3 * m:])
+    assert torch.isnan(cs[:, :, :3]).all()
+    rot = O.apply_rope(Kf, np.arange(s.n_tokens), cfg)
+    kr = Krot.float().cpu().numpy()
+    t0 = 3 * s.chunk_size
+    if dtype == "fp32":
+        e3 = max_abs(kr[:, :, t0:], rot[:, :, t0:])
+        assert e3 < 1e-5, e3
+    else:  # one bf16 rounding of a value within fp32 error of the exact one
+        err = np.abs(kr[:, :, t0:] - rot[:, :, t0:])
+        scale = np.abs(Kf[:, :, t0:]).max()
+        assert np.all(err <= np.abs(rot[:, :, t0:]) * 2.0 ** -7 + 1e-6 * scale)
+    say(f"  chunk {e1:.3e} group {e2:.3e}")
+    assert e1 < 2e-5 and e2 < 2e-5
+
+
+# --------------------------------------------------------------------------- routing
+def _decode_inputs(s, w):
+    q_pos = (w.seq_len - 1).astype(np.int32)
+    return q_pos
+
+
+@pytest.mark.parametrize("name,over", [
+    ("decode_32k", {"batch": 2, "n_tokens": 8192}),
+    ("decode_64k", {"batch": 1, "n_tokens": 16384}),
+    ("offload_decode_128k", {"batch": 1, "n_tokens": 16384}),
+])
+def test_route_decode(hga, name, over):
+    s = W.spec(name, **over)
+    say(f"[route decode] {name} {over} seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    ocs, ogs = O.build_summaries(f64(w.K, s.dtype), cfg)
+    cs32, gs32 = ocs.astype(np.float32), ogs.astype(np.float32)
+    q_pos = _decode_inputs(s, w)
+    or_ci, or_gi, diags = O.route(f64(w.Q, s.dtype), q_pos, cs32.astype(np.float64),
+                                  gs32.astype(np.float64), cfg, s.n_kv_heads)
+    p = params_of(s)
+    B, H = s.batch, s.n_kv_heads
+    ci = torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device="cuda")
+    sc = torch.full((B, H, s.n_tokens // s.chunk_size), float("nan"), device="cuda")
+    ws = hga.workspace(p, hga.OP_ROUTE, 1, s.n_tokens)
+    hga.route(p, dev(w.Q, s.dtype), 1, torch.from_numpy(q_pos).cuda(), torch.from_numpy(cs32).cuda(),
+              torch.from_numpy(gs32).cuda(), s.n_tokens, ci, gi, ws, scores_out=sc)
+    torch.cuda.synchronize()
+    n, unique = check_routing(ci.cpu().numpy(), gi.cpu().numpy(), or_ci, or_gi, diags, s.top_k, s.top_g)
+    say(f"  units {n}, unique {len(unique)}")
+    scn = sc.cpu().numpy()
+    for (b, h, u), dg in diags.items():
+        got = scn[b, h, dg["chunk_cand"]]
+        np.testing.assert_allclose(got, dg["chunk_scores"], rtol=1e-5, atol=1e-6)
+    # second call on the same workspace (counters reset themselves)
+    hga.route(p, dev(w.Q, s.dtype), 1, torch.from_numpy(q_pos).cuda(), torch.from_numpy(cs32).cuda(),
+              torch.from_numpy(gs32).cuda(), s.n_tokens, ci, gi, ws)
+    torch.cuda.synchronize()
+    check_routing(ci.cpu().numpy(), gi.cpu().numpy(), or_ci, or_gi, diags, s.top_k, s.top_g)
+    assert int(ws[:64].sum()) == 0
+
+
+# --------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("name,over", [
+    ("decode_32k", {"batch": 2, "n_tokens": 8192}),
+    ("decode_32k", {"batch": 2, "n_tokens": 4096, "dtype": "fp32"}),
+    ("offload_decode_128k", {"batch": 1, "n_tokens": 8192}),
+])
+def test_attend_decode_given_indices(hga, name, over):
+    """Attention alone, on index sets chosen by the oracle (given to both sides)."""
+    s = W.spec(name, **over)
+    say(f"[attend decode] {name} {over} seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    q_pos = _decode_inputs(s, w)
+    _, or_gi, _ = O.route(Qf, q_pos, ocs, ogs, cfg, s.n_kv_heads)
+    Oo, lse_o = O.attend(Qf, q_pos, Kf, Vf, or_gi, cfg, s.n_kv_heads)
+    p = params_of(s)
+    out = torch.empty((s.batch, s.n_q_heads, 1, s.head_dim), device="cuda")
+    lse = torch.empty((s.batch, s.n_q_heads, 1), device="cuda")
+    ws = hga.workspace(p, hga.OP_ATTEND, 1, s.n_tokens)
+    hga.attend(p, dev(w.Q, s.dtype), 1, torch.from_numpy(q_pos).cuda(), dev(w.K, s.dtype),
+               dev(w.V, s.dtype), s.n_tokens, torch.from_numpy(or_gi).cuda(), out, ws, lse_out=lse)
+    torch.cuda.synchronize()
+    e = max_abs(out.cpu().numpy(), Oo)
+    el = max_abs(lse.cpu().numpy(), lse_o)
+    say(f"  O max-abs {e:.3e}  lse max-abs {el:.3e}")
+    assert e <= TOL[s.dtype] and el <= 10 * TOL[s.dtype]
+
+
+# --------------------------------------------------------------------------- end to end
+def _run_decode_e2e(hga, s, w, check_all_rows=False):
+    cfg = cfg_of(s)
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    p = params_of(s)
+    B, H, n = s.batch, s.n_kv_heads, s.n_tokens
+    K, V, Q = dev(w.K, s.dtype), dev(w.V, s.dtype), dev(w.Q, s.dtype)
+    cs, gs = _summ_tables(s)
+    seq = torch.from_numpy(w.seq_len.astype(np.int32)).cuda()
+    # tables for every complete chunk before the query's chunk (a decode loop's state)
+    jq = int((w.seq_len.min() - 1) // s.chunk_size)
+    hga.build_summaries(p, K, n, 0, jq, cs, gs)
+    ci = torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, 1, s.head_dim), device="cuda")
+    ws = hga.workspace(p, hga.OP_DECODE, 1, n)
+    hga.decode(p, Q, K, V, n, seq, cs, gs, out, ws, chunk_idx=ci, group_idx=gi)
+    torch.cuda.synchronize()
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    q_pos = (w.seq_len - 1).astype(np.int64)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, H)
+    n_units, unique = check_routing(ci.cpu().numpy(), gi.cpu().numpy(), or_ci, or_gi, diags,
+                                    s.top_k, s.top_g)
+    gq = s.n_q_heads // H
+    rows = [(b, h * gq + r, 0) for (b, h, u) in sorted(unique) for r in range(gq)]
+    Oo, _ = O.attend(Qf, q_pos, Kf, Vf, or_gi, cfg, H, rows=rows)
+    got = out.cpu().numpy()
+    e = max(max_abs(got[b, hq, i], Oo[b, hq, i]) for (b, hq, i) in rows) if rows else 0.0
+    say(f"  units {n_units} unique {len(unique)}  O max-abs on unique rows {e:.3e}")
+    assert e <= TOL[s.dtype]
+    assert len(unique) >= 0.5 * n_units
+    # the step completed chunk (L-1)/C: its summaries were written
+    csn = cs.cpu().numpy()
+    for b in range(B):
+        L = int(w.seq_len[b])
+        if L % s.chunk_size == 0:
+            c = L // s.chunk_size - 1
+            assert max_abs(csn[b, :, c], ocs[b, :, c]) < 1e-5
+    return ws
+
+
+@pytest.mark.parametrize("name,over", [
+    ("decode_32k", {"batch": 2, "n_tokens": 8192}),
+    ("decode_64k", {"batch": 2, "n_tokens": 16384}),
+    ("decode_32k", {"batch": 2, "n_tokens": 4096, "dtype": "fp32"}),
+    ("decode_32k", {"batch": 2, "n_tokens": 4096, "n_q_heads": 8, "n_kv_heads": 8}),
+    ("decode_32k", {"batch": 1, "n_tokens": 4096, "n_q_heads": 16, "n_kv_heads": 1, "head_dim": 64}),
+])
+def test_decode_end_to_end(hga, name, over):
+    s = W.spec(name, **over)
+    say(f"[decode e2e] {name} {over} seed={s.seed}")
+    w = W.make(s)
+    _run_decode_e2e(hga, s, w)
+
+
+def test_decode_full_size_32k(hga):
+    """The benchmarked decode workload at full size (B=8, 32K context)."""
+    s = W.spec("decode_32k")
+    say(f"[decode e2e full] decode_32k seed={s.seed}")
+    w = W.make(s)
+    _run_decode_e2e(hga, s, w)
+
+
+def test_decode_ragged_and_short(hga):
+    """Per-sequence lengths from 1 token up to the capacity, partial current chunks,
+    sequences with no routing candidates yet."""
+    s = W.spec("decode_32k", batch=6, n_tokens=4096, needles=0)
+    say(f"[decode ragged] seed={s.seed}")
+    w = W.make(s)
+    w.seq_len = np.array([1, 64, 65, 300, 1000, 4096], dtype=np.int32)
+    cfg = cfg_of(s)
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    p = params_of(s)
+    n = s.n_tokens
+    K, V, Q = dev(w.K, s.dtype), dev(w.V, s.dtype), dev(w.Q, s.dtype)
+    cs, gs = _summ_tables(s)
+    hga.build_summaries(p, K, n, 0, n // s.chunk_size, cs, gs)
+    seq = torch.from_numpy(w.seq_len).cuda()
+    ci = torch.empty((s.batch, s.n_kv_heads, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((s.batch, s.n_kv_heads, 1, s.top_g), dtype=torch.int32, device="cuda")
+    out = torch.empty((s.batch, s.n_q_heads, 1, s.head_dim), device="cuda")
+    ws = hga.workspace(p, hga.OP_DECODE, 1, n)
+    hga.decode(p, Q, K, V, n, seq, cs, gs, out, ws, chunk_idx=ci, group_idx=gi)
+    torch.cuda.synchronize()
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    q_pos = (w.seq_len - 1).astype(np.int64)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, s.n_kv_heads)
+    _, unique = check_routing(ci.cpu().numpy(), gi.cpu().numpy(), or_ci, or_gi, diags, s.top_k, s.top_g)
+    gq = s.n_q_heads // s.n_kv_heads
+    rows = [(b, h * gq + r, 0) for (b, h, u) in sorted(unique) for r in range(gq)]
+    Oo, _ = O.attend(Qf, q_pos, Kf, Vf, or_gi, cfg, s.n_kv_heads, rows=rows)
+    got = out.cpu().numpy()
+    for (b, hq, i) in rows:
+        assert max_abs(got[b, hq, i], Oo[b, hq, i]) <= TOL[s.dtype], (b, hq)
+    # first sequences have no candidates: empty routing
+    assert (ci.cpu().numpy()[0] == -1).all() and (gi.cpu().numpy()[0] == -1).all()
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("over", [{}, {"n_tokens": 512}, {"top_k": 0, "top_g": 0, "n_tokens": 512},
+                                  {"n_sink": 0, "n_local": 0, "n_tokens": 512},
+                                  {"group_size": 64, "top_g": 3, "n_tokens": 512}])
+def test_prefill_tiny_fp32(hga, over):
+    s = W.spec("tiny_prefill_fp32", **over)
+    say(f"[prefill fp32] {over} seed={s.seed}")
+    w = W.make(s)
+    _run_prefill(hga, s, w)
+
+
+@pytest.mark.parametrize("over", [{"n_tokens": 2048}, {"n_tokens": 4096, "batch": 1}])
+def test_prefill_bf16(hga, over):
+    s = W.spec("prefill_32k", **over)
+    say(f"[prefill bf16] {over} seed={s.seed}")
+    w = W.make(s)
+    _run_prefill(hga, s, w)
+
+
+def _run_prefill(hga, s, w, units=None):
+    cfg = cfg_of(s)
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    p = params_of(s)
+    B, H, n = s.batch, s.n_kv_heads, s.n_tokens
+    nU = n // s.chunk_size
+    cs, gs = _summ_tables(s)
+    ci = torch.empty((B, H, nU, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, nU, max(1, s.top_g)), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, n, s.head_dim), device="cuda")
+    ws = hga.workspace(p, hga.OP_PREFILL, n, n)
+    hga.prefill(p, dev(w.Q, s.dtype), dev(w.K, s.dtype), dev(w.V, s.dtype), n, cs, gs, out, ws,
+                chunk_idx=ci, group_idx=gi)
+    torch.cuda.synchronize()
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    assert max_abs(cs.cpu().numpy(), ocs) < 1e-5
+    assert max_abs(gs.cpu().numpy(), ogs) < 1e-5
+    q_pos = np.zeros(B, dtype=np.int64)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, H, units=units)
+    n_units, unique = check_routing(ci.cpu().numpy(), gi.cpu().numpy()[..., :s.top_g] if s.top_g else
+                                    np.zeros((B, H, nU, 0), np.int32), or_ci, or_gi, diags, s.top_k, s.top_g)
+    got = out.cpu().numpy()
+    gq = s.n_q_heads // H
+    emax = 0.0
+    for (b, h, u) in sorted(unique):
+        o, _ = O.attend_unit_block(Qf, q_pos, Kf, Vf, or_gi, cfg, H, b, h, u)
+        g = got[b, h * gq:(h + 1) * gq, u * s.chunk_size:(u + 1) * s.chunk_size]
+        emax = max(emax, max_abs(g, o))
+    say(f"  units {n_units} unique {len(unique)}  O max-abs {emax:.3e}")
+    assert emax <= TOL[s.dtype]
+    assert len(unique) >= 0.5 * n_units
+    return out
+
+
+def test_offload_decode(hga):
+    """Cold tier: K/V in pinned host memory, hot windows in HBM, routed groups copied."""
+    s = W.spec("offload_decode_128k", batch=2, n_tokens=16384)
+    say(f"[offload decode] seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    p = params_of(s)
+    B, H, n, C, d = s.batch, s.n_kv_heads, s.n_tokens, s.chunk_size, s.head_dim
+    Kf, Vf, Qf = f64(w.K, s.dtype), f64(w.V, s.dtype), f64(w.Q, s.dtype)
+    K_host = W.to_torch(w.K, s.dtype, pin=True)
+    V_host = W.to_torch(w.V, s.dtype, pin=True)
+    hot_chunks = s.n_sink + s.n_local + 1
+    Kt, Vt = W.to_torch(w.K, s.dtype), W.to_torch(w.V, s.dtype)
+    K_hot = torch.zeros((B, H, hot_chunks * C, d), dtype=Kt.dtype)
+    V_hot = torch.zeros_like(K_hot)
+    j = (n - 1) // C
+    for c in list(range(s.n_sink)) + list(range(j - s.n_local, j + 1)):
+        sl = hga.hot_slot(c, s.n_sink, s.n_local)
+        K_hot[:, :, sl * C:(sl + 1) * C] = Kt[:, :, c * C:(c + 1) * C]
+        V_hot[:, :, sl * C:(sl + 1) * C] = Vt[:, :, c * C:(c + 1) * C]
+    K_hot, V_hot = K_hot.cuda(), V_hot.cuda()
+    cs, gs = _summ_tables(s)
+    hga.build_summaries(p, dev(w.K, s.dtype), n, 0, j, cs, gs)
+    seq = torch.from_numpy(w.seq_len.astype(np.int32)).cuda()
+    out = torch.empty((B, s.n_q_heads, 1, d), device="cuda")
+    ci = torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device="cuda")
+    staging = torch.empty(2 * B * H * s.top_g * s.group_size * d * 2, dtype=torch.uint8, device="cuda")
+    ws = hga.workspace(p, hga.OP_DECODE_OFFLOAD, 1, n)
+    copy_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    hga.decode_offload(p, dev(w.Q, s.dtype), K_host, V_host, K_hot, V_hot, n, seq, cs, gs, out,
+                       staging, ws, chunk_idx=ci, group_idx=gi, copy_stream=copy_stream.cuda_stream)
+    torch.cuda.synchronize()
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    q_pos = (w.seq_len - 1).astype(np.int64)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, H)
+    _, unique = check_routing(ci.cpu().numpy(), gi.cpu().numpy(), or_ci, or_gi, diags, s.top_k, s.top_g)
+    gq = s.n_q_heads // H
+    rows = [(b, h * gq + r, 0) for (b, h, u) in sorted(unique) for r in range(gq)]
+    Oo, _ = O.attend(Qf, q_pos, Kf, Vf, or_gi, cfg, H, rows=rows)
+    got = out.cpu().numpy()
+    e = max(max_abs(got[b, hq, i], Oo[b, hq, i]) for (b, hq, i) in rows)
+    say(f"  unique units {len(unique)}  O max-abs {e:.3e}")
+    assert e <= TOL[s.dtype]
+    # the step completed the last chunk: summary built from the hot window
+    assert max_abs(cs.cpu().numpy()[:, :, j], ocs[:, :, j]) < 1e-5
+
+
+def test_nan_summaries_after_routing_leave_output_unchanged(hga):
+    """No summary value enters the output: poisoning the tables after routing
+    changes nothing in a second attention pass."""
+    s = W.spec("decode_32k", batch=2, n_tokens=4096)
+    say(f"[nan summaries] seed={s.seed}")
+    w = W.make(s)
+    p = params_of(s)
+    n = s.n_tokens
+    K, V, Q = dev(w.K, s.dtype), dev(w.V, s.dtype), dev(w.Q, s.dtype)
+    cs, gs = _summ_tables(s)
+    hga.build_summaries(p, K, n, 0, n // s.chunk_size, cs, gs)
+    gi = torch.empty((s.batch, s.n_kv_heads, 1, s.top_g), dtype=torch.int32, device="cuda")
+    ci = torch.empty((s.batch, s.n_kv_heads, 1, s.top_k), dtype=torch.int32, device="cuda")
+    out1 = torch.empty((s.batch, s.n_q_heads, 1, s.head_dim), device="cuda")
+    out2 = torch.empty_like(out1)
+    ws = hga.workspace(p, hga.OP_DECODE, 1, n)
+    seq = torch.from_numpy(w.seq_len.astype(np.int32)).cuda()
+    hga.decode(p, Q, K, V, n, seq - 1, cs, gs, out1, ws, chunk_idx=ci, group_idx=gi)
+    cs.fill_(float("nan"))
+    gs.fill_(float("nan"))
+    ws2 = hga.workspace(p, hga.OP_ATTEND, 1, n)
+    hga.attend(p, Q, 1, seq - 2, K, V, n, gi, out2, ws2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out2).all()
+    assert torch.equal(out1, out2)
