@@ -5,50 +5,92 @@
 // over the bounded exact token set; no summary enters the output)].
 //
 // Token slots of a query at position t in chunk j: first the forced chunks
-// (sink + local + current, C slots each, tokens after t masked), then the
-// routed groups (G slots each).  Slots are cut into tiles of 64; a workgroup
-// takes a contiguous range of tiles and each of its four waves owns 16 rows of
-// every tile, keeping its own running max / sum / output (online softmax, base
-// 2).  Per tile a lane loads one quarter of a K row and of a V row (16-byte
-// loads, 4 lanes per row): QK^T reduces over the 4 lanes, the V rows and the
-// probabilities go through LDS and PV runs with lanes over output dims.  All
-// query heads sharing the KV head are served by the same K/V loads.  The
-// waves are merged in LDS; with several workgroups per query the partial
-// (max, sum, output) goes to the workspace and the last workgroup (device
-// counter) merges them.  In decode this kernel is bound by HBM bandwidth.
-#include "hga_kernels.hpp"
+// (sink + local + current, C slots each; tokens after t masked), then the
+// routed groups (G slots each; -1 entries masked).  Slots are cut into blocks
+// of 16 rows.  A workgroup takes a contiguous range of blocks; its four waves
+// take every fourth block and run independently (online softmax in base 2, no
+// LDS and no barrier inside the loop).  Within a block, lane (g, c) holds rows
+// g, g+4, g+8, g+12 and the c-th sixteenth of each row, so one load
+// instruction fetches four whole rows; QK^T reduces over the 16 lanes of a
+// row with DPP, the block max and sum over the 4 row groups with permlane
+// swaps, and PV accumulates per lane into its sixteenth of the output.  The
+// next block's loads are issued before the current block is computed.  All
+// query heads that share the KV head are served by the same loads.  With
+// several workgroups per query the partial (max, sum, output) goes to the
+// workspace and the last workgroup merges.  In decode the kernel is bound by
+// HBM bandwidth.
 #include "hga_device.hpp"
+#include "hga_kernels.hpp"
 
 namespace hga {
 
 constexpr int kAttThreads = 256;
 constexpr int kAttWaves = kAttThreads / kWave;
-constexpr int kRowsPerWave = kTileSlots / kAttWaves;  // 16
+constexpr int kBlockRows = kAttBlockRows;
+constexpr int kMaxParts = kAttMaxParts;
 
-template <typename T, int D, int GQ>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int BYTES> struct RawVec;
+template <> struct RawVec<8> { uint2 v; };
+template <> struct RawVec<16> { uint4 v; };
+template <> struct RawVec<32> { uint4 v0, v1; };
+
+template <int BYTES>
+__device__ __forceinline__ RawVec<BYTES> load_raw(const void* p) {
+  RawVec<BYTES> r;
+  if constexpr (BYTES == 8) r.v = *reinterpret_cast<const uint2*>(p);
+  else if constexpr (BYTES == 16) r.v = *reinterpret_cast<const uint4*>(p);
+  else {
+    r.v0 = reinterpret_cast<const uint4*>(p)[0];
+    r.v1 = reinterpret_cast<const uint4*>(p)[1];
+  }
+  return r;
+}
+
+template <int BYTES>
+__device__ __forceinline__ RawVec<BYTES> zero_raw() {
+  RawVec<BYTES> r;
+  if constexpr (BYTES == 8) r.v = make_uint2(0u, 0u);
+  else if constexpr (BYTES == 16) r.v = make_uint4(0u, 0u, 0u, 0u);
+  else {
+    r.v0 = make_uint4(0u, 0u, 0u, 0u);
+    r.v1 = r.v0;
+  }
+  return r;
+}
+
+// the 32-bit words of a raw vector
+template <int BYTES>
+__device__ __forceinline__ uint32_t word(const RawVec<BYTES>& r, int i) {
+  if constexpr (BYTES == 8) return i == 0 ? r.v.x : r.v.y;
+  else if constexpr (BYTES == 16) return i == 0 ? r.v.x : i == 1 ? r.v.y : i == 2 ? r.v.z : r.v.w;
+  else {
+    const uint4& hv = i < 4 ? r.v0 : r.v1;
+    const int k = i & 3;
+    return k == 0 ? hv.x : k == 1 ? hv.y : k == 2 ? hv.z : hv.w;
+  }
+}
+
+template <int GQ, int D>
 struct AttSmem {
-  static constexpr int kVRowBytes = D * static_cast<int>(sizeof(T)) + 16;  // padded against bank conflicts
-  float q[GQ][D];
-  float p[kAttWaves][kRowsPerWave][GQ];
-  alignas(16) unsigned char v[kAttWaves][kRowsPerWave][kVRowBytes];
+  int gl[1024];
   float wm[kAttWaves][GQ];
   float wl[kAttWaves][GQ];
-  int gl[1024];
-  BlockScanSmem<kAttThreads> scan;
-  int n_routed;
+  float wgt[kAttWaves][GQ];
+  float L[GQ];
+  float M[GQ];
+  float ow[kAttWaves][GQ * D];
+  float pm[kMaxParts * GQ];  // merge: per-part max, then weight
+  float pl[kMaxParts * GQ];
   int is_last;
-};
-
-struct SlotMap {
-  Forced f;
-  int C, G, nF_slots, n_slots;
 };
 
 template <typename T, int D, int GQ>
 __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a) {
-  constexpr int QD = D / 4;          // dims per lane in the QK layout
-  constexpr int DPL = D / kWave;     // dims per lane in the PV layout
-  static_assert(DPL >= 1, "head_dim >= 64");
+  constexpr int EPL = D / 16;                            // elements of a row per lane
+  constexpr int RB = EPL * static_cast<int>(sizeof(T));  // bytes of a row per lane
+  constexpr bool kBF = sizeof(T) == 2;
   const KParams& kp = a.kp;
   const int bh = blockIdx.z;
   const int qi = blockIdx.y;
@@ -58,12 +100,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
+  const int rg = lane >> 4;  // row group within a block
+  const int cc = lane & 15;  // sixteenth of the row
   const int t_row0 = (a.q_pos ? a.q_pos[b] : 0) + a.pos_bias;
   const int t = t_row0 + qi;
   const int j = t / kp.C;
   const int u = a.nq == 1 ? 0 : j - t_row0 / kp.C;
 
-  __shared__ AttSmem<T, D, GQ> sm;
+  __shared__ AttSmem<GQ, D> sm;
 
   // a position outside the cache (or a prefill block not aligned to C) yields NaN
   if (t_row0 < 0 || static_cast<int64_t>(t_row0) + a.nq - 1 >= kp.n_cap ||
@@ -80,228 +124,205 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
     return;
   }
 
-  // ---- query rows of the GQ heads (pre-scaled to base-2 logits), group list
+  // ---- routed group list of the unit (entries outside [0, n_cap/G) are masked)
+  const int32_t* glg = a.group_idx + (static_cast<int64_t>(bh) * a.n_units + u) * kp.top_g;
+  for (int e = tid; e < kp.top_g; e += kAttThreads) sm.gl[e] = glg[e];
+
+  // ---- this lane's sixteenth of the query rows of the GQ heads
   const T* Qb = static_cast<const T*>(a.Q);
-  for (int e = tid; e < GQ * D; e += kAttThreads) {
-    const int hh = e / D, dd = e % D;
-    const int64_t off = ((static_cast<int64_t>(b) * kp.Hq + h * GQ + hh) * a.nq + qi) * D + dd;
-    sm.q[hh][dd] = elem<T>::get(Qb, off) * kp.scale_log2;
-  }
-  // routed groups of the unit, compacted (-1 and out-of-range ids dropped)
-  {
-    const int32_t* gl = a.group_idx + (static_cast<int64_t>(bh) * a.n_units + u) * kp.top_g;
-    const int n_groups_cap = static_cast<int>(kp.n_cap / kp.G);
-    const int per = (kp.top_g + kAttThreads - 1) / kAttThreads;
-    const int e0 = min(kp.top_g, tid * per), e1 = min(kp.top_g, e0 + per);
-    int cnt = 0;
-    for (int e = e0; e < e1; ++e) {
-      const int g = gl[e];
-      cnt += (g >= 0 && g < n_groups_cap);
+  uint32_t qbf[GQ][EPL / 2];  // bf16 pairs (bf16 inputs)
+  float qf[kBF ? 1 : GQ][kBF ? 1 : EPL];
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh) {
+    const T* qr = Qb + ((static_cast<int64_t>(b) * kp.Hq + h * GQ + hh) * a.nq + qi) * D + cc * EPL;
+    const RawVec<RB> r = load_raw<RB>(qr);
+    if constexpr (kBF) {
+#pragma unroll
+      for (int w = 0; w < EPL / 2; ++w) qbf[hh][w] = word(r, w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[hh][e] = __uint_as_float(word(r, e));
     }
-    int tot;
-    int pos = block_excl_scan<kAttThreads>(cnt, tot, sm.scan);
-    for (int e = e0; e < e1; ++e) {
-      const int g = gl[e];
-      if (g >= 0 && g < n_groups_cap) sm.gl[pos++] = g;
-    }
-    if (tid == 0) sm.n_routed = tot;
   }
   __syncthreads();
 
-  SlotMap sl;
-  sl.f = forced_chunks(j, kp.n_sink, kp.n_local);
-  sl.C = kp.C;
-  sl.G = kp.G;
-  sl.nF_slots = sl.f.n * kp.C;
-  sl.n_slots = sl.nF_slots + sm.n_routed * kp.G;
-  int R0 = 0, R1 = sl.n_slots;
-  if (a.part == 1) R1 = sl.nF_slots;
-  if (a.part == 2) R0 = sl.nF_slots;
-  const int ntiles = (R1 - R0 + kTileSlots - 1) / kTileSlots;
-  const int tb = min(ntiles, x * a.tiles_per_split);
-  const int te = min(ntiles, tb + a.tiles_per_split);
+  const Forced fc = forced_chunks(j, kp.n_sink, kp.n_local);
+  const int nF = fc.n * kp.C;
+  const int n_slots = nF + kp.top_g * kp.G;
+  int R0 = 0, R1 = n_slots;
+  if (a.part == 1) R1 = nF;
+  if (a.part == 2) R0 = nF;
+  const int nblocks = (R1 - R0 + kBlockRows - 1) / kBlockRows;
+  const int bb = min(nblocks, x * a.tiles_per_split);
+  const int be = min(nblocks, bb + a.tiles_per_split);
+  const int n_groups_cap = static_cast<int>(kp.n_cap / kp.G);
 
   const T* Kb = static_cast<const T*>(a.K);
   const T* Vb = static_cast<const T*>(a.V);
   const T* Ks = static_cast<const T*>(a.K_stage);
   const T* Vs = static_cast<const T*>(a.V_stage);
-  const int r_in_wave = lane >> 2;
-  const int qd = lane & 3;
+  const bool staged_routed = Ks != nullptr;
 
-  float m_w[GQ], l_w[GQ], o_acc[GQ][DPL];
+  // element offset of slot s's row, or -1 when the slot is masked
+  auto row_of = [&](int s) -> int64_t {
+    if (s >= R1) return -1;
+    if (s < nF) {
+      const int fi = s / kp.C, off = s - fi * kp.C;
+      const int c = forced_chunk_at(fc, fi);
+      const int64_t tok = static_cast<int64_t>(c) * kp.C + off;
+      if (tok > t) return -1;
+      int64_t hs = c;
+      if (a.kv.ring && c >= kp.n_sink) hs = kp.n_sink + (c - kp.n_sink) % (kp.n_local + 1);
+      return (static_cast<int64_t>(bh) * a.kv.bh_rows + hs * kp.C + off) * D;
+    }
+    const int rs = s - nF;
+    const int e = rs / kp.G;
+    const int g = sm.gl[e];
+    if (g < 0 || g >= n_groups_cap) return -1;
+    const int64_t tok = static_cast<int64_t>(g) * kp.G + (rs - e * kp.G);
+    if (tok > t) return -1;
+    if (staged_routed) return (static_cast<int64_t>(bh) * kp.top_g * kp.G + rs) * D;
+    return (static_cast<int64_t>(bh) * a.kv.bh_rows + tok) * D;
+  };
+
+  float m_run[GQ], l_run[GQ], o[GQ][EPL];
 #pragma unroll
   for (int hh = 0; hh < GQ; ++hh) {
-    m_w[hh] = -__builtin_huge_valf();
-    l_w[hh] = 0.f;
+    m_run[hh] = -__builtin_huge_valf();
+    l_run[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o_acc[hh][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
   }
 
-  for (int tile = tb; tile < te; ++tile) {
-    // ---- which token this lane's row holds
-    const int slot = R0 + tile * kTileSlots + wid * kRowsPerWave + r_in_wave;
-    bool valid = slot < R1;
-    const T* krow = nullptr;
-    const T* vrow = nullptr;
-    if (valid) {
-      int64_t tok, row;
-      if (slot < sl.nF_slots) {
-        const int fi = slot / sl.C, off = slot % sl.C;
-        const int c = forced_chunk_at(sl.f, fi);
-        tok = static_cast<int64_t>(c) * sl.C + off;
-        int64_t hs = c;
-        if (a.kv.ring && c >= kp.n_sink) hs = kp.n_sink + (c - kp.n_sink) % (kp.n_local + 1);
-        row = static_cast<int64_t>(bh) * a.kv.bh_rows + hs * sl.C + off;
-        krow = Kb + row * D;
-        vrow = Vb + row * D;
+  RawVec<RB> kc[4], vc[4];
+  bool okc[4];
+  auto fetch = [&](int blkid, RawVec<RB>* kr, RawVec<RB>* vr, bool* ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = R0 + blkid * kBlockRows + rg + 4 * i;
+      const int64_t ro = row_of(s);
+      ok[i] = ro >= 0;
+      if (ok[i]) {
+        const bool st = staged_routed && s >= nF;
+        kr[i] = load_raw<RB>((st ? Ks : Kb) + ro + cc * EPL);
+        vr[i] = load_raw<RB>((st ? Vs : Vb) + ro + cc * EPL);
       } else {
-        const int rs = slot - sl.nF_slots;
-        const int g = sm.gl[rs / sl.G];
-        tok = static_cast<int64_t>(g) * sl.G + rs % sl.G;
-        if (Ks) {
-          row = static_cast<int64_t>(bh) * kp.top_g * sl.G + rs;
-          krow = Ks + row * D;
-          vrow = Vs + row * D;
-        } else {
-          row = static_cast<int64_t>(bh) * a.kv.bh_rows + tok;
-          krow = Kb + row * D;
-          vrow = Vb + row * D;
-        }
-      }
-      valid = tok <= t;
-    }
-    float kf[QD], vf[QD];
-    if (valid) {
-      load_row<T, QD>(krow + qd * QD, kf);
-      load_row<T, QD>(vrow + qd * QD, vf);
-    } else {
-#pragma unroll
-      for (int e = 0; e < QD; ++e) kf[e] = vf[e] = 0.f;
-    }
-    // ---- scores (base 2) of this row for every head
-    float s[GQ];
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-      const float4* q4 = reinterpret_cast<const float4*>(&sm.q[hh][qd * QD]);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < QD / 4; ++e) {
-        const float4 qq = q4[e];
-        acc = fmaf(qq.x, kf[4 * e + 0], acc);
-        acc = fmaf(qq.y, kf[4 * e + 1], acc);
-        acc = fmaf(qq.z, kf[4 * e + 2], acc);
-        acc = fmaf(qq.w, kf[4 * e + 3], acc);
-      }
-      acc += __shfl_xor(acc, 1, kWave);
-      acc += __shfl_xor(acc, 2, kWave);
-      s[hh] = valid ? acc : -__builtin_huge_valf();
-    }
-    // ---- online softmax update of this wave's 16 rows
-    float alpha[GQ];
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-      float tm = s[hh];
-      tm = wave_xor_max(tm, 4);
-      tm = wave_xor_max(tm, 8);
-      tm = wave_xor_max(tm, 16);
-      tm = wave_xor_max(tm, 32);
-      const float m_new = fmaxf(m_w[hh], tm);
-      alpha[hh] = m_new == -__builtin_huge_valf() ? 1.f : exp2f(m_w[hh] - m_new);
-      const float p = valid ? exp2f(s[hh] - m_new) : 0.f;
-      float ps = qd == 0 ? p : 0.f;
-      ps += __shfl_xor(ps, 4, kWave);
-      ps += __shfl_xor(ps, 8, kWave);
-      ps += __shfl_xor(ps, 16, kWave);
-      ps += __shfl_xor(ps, 32, kWave);
-      l_w[hh] = l_w[hh] * alpha[hh] + ps;
-      m_w[hh] = m_new;
-      if (qd == 0) sm.p[wid][r_in_wave][hh] = p;
-    }
-    // ---- V rows to LDS (as stored), then PV with lanes over output dims
-    {
-      unsigned char* dst = &sm.v[wid][r_in_wave][0] + qd * QD * static_cast<int>(sizeof(T));
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < QD / 8; ++e) {
-          uint4 w;
-          w.x = (__float_as_uint(vf[8 * e + 0]) >> 16) | (__float_as_uint(vf[8 * e + 1]) & 0xffff0000u);
-          w.y = (__float_as_uint(vf[8 * e + 2]) >> 16) | (__float_as_uint(vf[8 * e + 3]) & 0xffff0000u);
-          w.z = (__float_as_uint(vf[8 * e + 4]) >> 16) | (__float_as_uint(vf[8 * e + 5]) & 0xffff0000u);
-          w.w = (__float_as_uint(vf[8 * e + 6]) >> 16) | (__float_as_uint(vf[8 * e + 7]) & 0xffff0000u);
-          reinterpret_cast<uint4*>(dst)[e] = w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < QD / 4; ++e)
-          reinterpret_cast<float4*>(dst)[e] = make_float4(vf[4 * e], vf[4 * e + 1], vf[4 * e + 2], vf[4 * e + 3]);
+        kr[i] = zero_raw<RB>();
+        vr[i] = zero_raw<RB>();
       }
     }
-    __syncthreads();
+  };
+
+  int blk = bb + wid;
+  if (blk < be) fetch(blk, kc, vc, okc);
+  for (; blk < be; blk += kAttWaves) {
+    RawVec<RB> kn[4], vn[4];
+    bool okn[4];
+    const int nxt = blk + kAttWaves;
+    if (nxt < be) fetch(nxt, kn, vn, okn);
+
+    // ---- scores (base 2) of the lane's 4 rows for every head
+    float s[4][GQ];
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o_acc[hh][e] *= alpha[hh];
-#pragma unroll 4
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      float vv[DPL];
-      const unsigned char* src = &sm.v[wid][r][0];
-      if constexpr (sizeof(T) == 2) {
-        if constexpr (DPL == 2) {
-          const uint32_t w = reinterpret_cast<const uint32_t*>(src)[lane];
-          vv[0] = bf16lo(w);
-          vv[1] = bf16hi(w);
-        } else {
-          vv[0] = bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[lane]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) vv[e] = reinterpret_cast<const float*>(src)[lane * DPL + e];
-      }
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh) {
-        const float p = sm.p[wid][r][hh];
+        float acc = 0.f;
+        if constexpr (kBF) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o_acc[hh][e] = fmaf(p, vv[e], o_acc[hh][e]);
+          for (int w = 0; w < EPL / 2; ++w)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qbf[hh][w]),
+                                                   __builtin_bit_cast(bf16x2_t, word(kc[i], w)), acc, false);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc = fmaf(qf[hh][e], __uint_as_float(word(kc[i], e)), acc);
+        }
+        acc = sum16(acc);
+        s[i][hh] = okc[i] ? acc * kp.scale_log2 : -__builtin_huge_valf();
       }
     }
-    __syncthreads();
-  }
-
-  // ---- merge the four waves
-  if (lane == 0) {
+    // ---- online softmax over this block's 16 rows
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
-      sm.wm[wid][hh] = m_w[hh];
-      sm.wl[wid][hh] = l_w[hh];
-    }
-  }
-  __syncthreads();
-  float M[GQ], L[GQ], wgt[GQ];
+      float bm = fmaxf(fmaxf(s[0][hh], s[1][hh]), fmaxf(s[2][hh], s[3][hh]));
+      bm = max_rows(bm);
+      const float m_new = fmaxf(m_run[hh], bm);
+      const float alpha = m_new == -__builtin_huge_valf() ? 1.f : exp2f(m_run[hh] - m_new);
+      float ps = 0.f;
 #pragma unroll
-  for (int hh = 0; hh < GQ; ++hh) {
-    M[hh] = -__builtin_huge_valf();
-    for (int w = 0; w < kAttWaves; ++w) M[hh] = fmaxf(M[hh], sm.wm[w][hh]);
-    L[hh] = 0.f;
-    for (int w = 0; w < kAttWaves; ++w) {
-      const float mw = sm.wm[w][hh];
-      if (mw != -__builtin_huge_valf()) L[hh] += sm.wl[w][hh] * exp2f(mw - M[hh]);
+      for (int i = 0; i < 4; ++i) {
+        const float p = okc[i] ? exp2f(s[i][hh] - m_new) : 0.f;
+        s[i][hh] = p;
+        ps += p;
+      }
+      l_run[hh] = l_run[hh] * alpha + sum_rows(ps);
+      m_run[hh] = m_new;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[hh][e] *= alpha;
     }
-    wgt[hh] = m_w[hh] == -__builtin_huge_valf() ? 0.f : exp2f(m_w[hh] - M[hh]);
-  }
-  __syncthreads();
-  // o of the block, summed over waves through LDS (reuse the V area as floats)
-  float* osum = reinterpret_cast<float*>(&sm.v[0][0][0]);  // GQ*D floats fit: 4*16*(D*sizeof(T)+16) >= GQ*D*4 for GQ<=16
-  for (int e = tid; e < GQ * D; e += kAttThreads) osum[e] = 0.f;
-  __syncthreads();
-  for (int w = 0; w < kAttWaves; ++w) {
-    if (wid == w) {
+    // ---- PV
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float vf[EPL];
+      if constexpr (kBF) {
+#pragma unroll
+        for (int w = 0; w < EPL / 2; ++w) {
+          const uint32_t x2 = word(vc[i], w);
+          vf[2 * w] = bf16lo(x2);
+          vf[2 * w + 1] = bf16hi(x2);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = __uint_as_float(word(vc[i], e));
+      }
 #pragma unroll
       for (int hh = 0; hh < GQ; ++hh)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) osum[hh * D + lane * DPL + e] += o_acc[hh][e] * wgt[hh];
+        for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(s[i][hh], vf[e], o[hh][e]);
     }
-    __syncthreads();
+    if (nxt < be) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kc[i] = kn[i];
+        vc[i] = vn[i];
+        okc[i] = okn[i];
+      }
+    }
   }
+
+  // ---- wave result: sum the 4 row groups, then merge the waves in LDS
+#pragma unroll
+  for (int hh = 0; hh < GQ; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[hh][e] = sum_rows(o[hh][e]);
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+      sm.wm[wid][hh] = m_run[hh];
+      sm.wl[wid][hh] = l_run[hh];
+    }
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm.ow[wid][hh * D + cc * EPL + e] = o[hh][e];
+  }
+  __syncthreads();
+  if (tid < GQ) {
+    float M = -__builtin_huge_valf();
+    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, sm.wm[w][tid]);
+    float L = 0.f;
+    for (int w = 0; w < kAttWaves; ++w) {
+      const float mw = sm.wm[w][tid];
+      const float wt = mw == -__builtin_huge_valf() ? 0.f : exp2f(mw - M);
+      sm.wgt[w][tid] = wt;
+      L += sm.wl[w][tid] * wt;
+    }
+    sm.M[tid] = M;
+    sm.L[tid] = L;
+  }
+  __syncthreads();
 
   const int64_t row_id = static_cast<int64_t>(bh) * a.nq + qi;  // (b, kv head, query row)
   auto write_out = [&](int hh, int dd, float val) {
@@ -315,40 +336,74 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
       a.lse[off] = (mlog2 + log2f(lsum)) * 0.69314718055994531f;
     }
   };
+  auto wave_sum = [&](int e) {
+    const int hh = e / D;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttWaves; ++w) v += sm.ow[w][e] * sm.wgt[w][hh];
+    return v;
+  };
 
   if (a.parts_total == 1) {
-    for (int e = tid; e < GQ * D; e += kAttThreads) {
-      const int hh = e / D;
-      write_out(hh, e % D, osum[e] / L[hh]);
-    }
-    if (tid < GQ) write_lse(tid, M[tid], L[tid]);
+    for (int e = tid; e < GQ * D; e += kAttThreads) write_out(e / D, e % D, wave_sum(e) / sm.L[e / D]);
+    if (tid < GQ) write_lse(tid, sm.M[tid], sm.L[tid]);
     return;
   }
 
-  // ---- partial to the workspace: [o (GQ*D) | m (GQ) | l (GQ)]
+  // ---- partial to the workspace: [o (GQ*D) | m (GQ) | l (GQ)], device-coherent stores
   const int stride = GQ * (D + 2);
   float* part = a.partials + (row_id * a.parts_total + a.part_offset + x) * stride;
-  for (int e = tid; e < GQ * D; e += kAttThreads) st_agent(part + e, osum[e]);
+  for (int e = tid; e < GQ * D; e += kAttThreads) st_agent(part + e, wave_sum(e));
   if (tid < GQ) {
-    st_agent(part + GQ * D + tid, M[tid]);
-    st_agent(part + GQ * D + GQ + tid, L[tid]);
+    st_agent(part + GQ * D + tid, sm.M[tid]);
+    st_agent(part + GQ * D + GQ + tid, sm.L[tid]);
   }
   if (!arrive_last(&a.counters[row_id], static_cast<uint32_t>(a.parts_total), &sm.is_last)) return;
+
+  // ---- last workgroup: merge the parts (plain loads after the acquire)
   const float* parts = a.partials + row_id * a.parts_total * stride;
+  const int P = a.parts_total;
+  for (int e = tid; e < P * GQ; e += kAttThreads) {
+    const int p = e / GQ, hh = e % GQ;
+    sm.pm[e] = parts[p * stride + GQ * D + hh];
+    sm.pl[e] = parts[p * stride + GQ * D + GQ + hh];
+  }
+  __syncthreads();
+  if (tid < GQ) {
+    float M = -__builtin_huge_valf();
+    for (int p = 0; p < P; ++p) M = fmaxf(M, sm.pm[p * GQ + tid]);
+    float L = 0.f;
+    for (int p = 0; p < P; ++p) {
+      const float mp = sm.pm[p * GQ + tid];
+      const float wt = mp == -__builtin_huge_valf() ? 0.f : exp2f(mp - M);
+      sm.pm[p * GQ + tid] = wt;
+      L += wt * sm.pl[p * GQ + tid];
+    }
+    sm.M[tid] = M;
+    sm.L[tid] = L;
+  }
+  __syncthreads();
   for (int e = tid; e < GQ * D; e += kAttThreads) {
     const int hh = e / D;
-    float mx = -__builtin_huge_valf();
-    for (int p = 0; p < a.parts_total; ++p) mx = fmaxf(mx, ld_agent(parts + p * stride + GQ * D + hh));
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < a.parts_total; ++p) {
-      const float mp = ld_agent(parts + p * stride + GQ * D + hh);
-      if (mp == -__builtin_huge_valf()) continue;
-      const float w = exp2f(mp - mx);
-      num += w * ld_agent(parts + p * stride + e);
-      den += w * ld_agent(parts + p * stride + GQ * D + GQ + hh);
+    float num = 0.f;
+    int p = 0;
+    for (; p + 8 <= P; p += 8) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = parts[(p + r) * stride + e];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float wt = sm.pm[(p + r) * GQ + hh];
+        num += wt == 0.f ? 0.f : wt * v[r];
+      }
     }
-    write_out(hh, e % D, num / den);
-    if (e % D == 0) write_lse(hh, mx, den);
+    for (; p < P; ++p) {
+      const float wt = sm.pm[p * GQ + hh];
+      const float v = parts[p * stride + e];
+      num += wt == 0.f ? 0.f : wt * v;
+    }
+    write_out(hh, e % D, num / sm.L[hh]);
+    if (e % D == 0) write_lse(hh, sm.M[hh], sm.L[hh]);
   }
 }
 

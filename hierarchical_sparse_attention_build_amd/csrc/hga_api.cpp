@@ -137,18 +137,20 @@ struct AttendPlan {
 AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base) {
   AttendPlan a{};
   const int64_t rows = static_cast<int64_t>(kp.B) * kp.Hkv * nq;
-  const int max_tiles = static_cast<int>(cdiv(attend_max_slots(kp), kTileSlots));
-  const int64_t target = 2048;  // workgroups wanted to fill 256 CUs several times over
-  int splits = static_cast<int>(std::min<int64_t>(max_tiles, std::max<int64_t>(1, cdiv(target, rows))));
-  a.tps = static_cast<int>(cdiv(max_tiles, splits));
+  const int max_blocks = static_cast<int>(cdiv(attend_max_slots(kp), kAttBlockRows));
+  // enough workgroups to give every CU work, each with several 16-row blocks
+  const int64_t target = 512;
+  const int splits = static_cast<int>(
+      std::min<int64_t>(std::min(max_blocks, kAttMaxParts / 2), std::max<int64_t>(1, cdiv(target, rows))));
+  a.tps = static_cast<int>(cdiv(max_blocks, splits));
   if (two_part) {
-    const int ft = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kTileSlots));
-    const int rt = static_cast<int>(std::max<int64_t>(1, cdiv(static_cast<int64_t>(kp.top_g) * kp.G, kTileSlots)));
-    a.splits1 = static_cast<int>(cdiv(ft, a.tps));
-    a.splits2 = static_cast<int>(cdiv(rt, a.tps));
+    const int fb = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kAttBlockRows));
+    const int rb = static_cast<int>(std::max<int64_t>(1, cdiv(static_cast<int64_t>(kp.top_g) * kp.G, kAttBlockRows)));
+    a.splits1 = static_cast<int>(cdiv(fb, a.tps));
+    a.splits2 = static_cast<int>(cdiv(rb, a.tps));
     a.parts_total = a.splits1 + a.splits2;
   } else {
-    a.splits1 = static_cast<int>(cdiv(max_tiles, a.tps));
+    a.splits1 = static_cast<int>(cdiv(max_blocks, a.tps));
     a.splits2 = 0;
     a.parts_total = a.splits1;
   }

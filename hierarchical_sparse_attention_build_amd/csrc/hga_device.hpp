@@ -72,26 +72,84 @@ struct Raw16 {
   uint4 v[NV];
 };
 
-// ---------------------------------------------------------------- wave ops
-__device__ __forceinline__ float wave_xor_max(float v, int lane_mask) {
-  return fmaxf(v, __shfl_xor(v, lane_mask, kWave));
-}
+// ---------------------------------------------------------------- DPP lane ops
+// Lane exchanges through DPP (within rows of 16 lanes) and the gfx950 permlane
+// swaps (across rows), instead of LDS-routed shuffles.
+namespace dpp {
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kQuad2301 = 0x4E, kQuad1032 = 0xB1;       // quad_perm [2,3,0,1], [1,0,3,2]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float movf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int movi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+// value of the same lane in the paired row: xor 16 and xor 32 (results identical
+// in both rows of a pair, so "a + other" is the pair's reduction)
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+}  // namespace dpp
+
+// all-reduce over each aligned group of 8 lanes
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp::movf<dpp::kRowHalfMirror>(v);
+  v += dpp::movf<dpp::kQuad2301>(v);
+  v += dpp::movf<dpp::kQuad1032>(v);
   return v;
 }
+// all-reduce over each row of 16 lanes
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp::movf<dpp::kRowRor8>(v);
+  v += dpp::movf<dpp::kRowRor4>(v);
+  v += dpp::movf<dpp::kQuad2301>(v);
+  v += dpp::movf<dpp::kQuad1032>(v);
+  return v;
+}
+// all-reduce over the 4 rows of the wave (lanes with equal lane%16)
+__device__ __forceinline__ float sum_rows(float v) {
+  float a, b;
+  dpp::swap16(v, a, b);
+  v = a + b;
+  dpp::swap32(v, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max_rows(float v) {
+  float a, b;
+  dpp::swap16(v, a, b);
+  v = fmaxf(a, b);
+  dpp::swap32(v, a, b);
+  return fmaxf(a, b);
+}
+// all-reduce over the 32-lane halves (lane pairs of rows 0/1 and 2/3)
+__device__ __forceinline__ float sum_rowpair(float v) {
+  float a, b;
+  dpp::swap16(v, a, b);
+  return a + b;
+}
 
-// Inclusive scan of ints across a wave.
+// ---------------------------------------------------------------- wave ops
+// Inclusive scan of ints across a wave (DPP row shifts, then row broadcasts).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+  v += dpp::movi<dpp::kRowShr1>(v);
+  v += dpp::movi<dpp::kRowShr2>(v);
+  v += dpp::movi<dpp::kRowShr4>(v);
+  v += dpp::movi<dpp::kRowShr8>(v);
+  v += dpp::movi<dpp::kRowBcast15, 0xA>(v);
+  v += dpp::movi<dpp::kRowBcast31, 0xC>(v);
   return v;
 }
 
@@ -238,15 +296,21 @@ __device__ __forceinline__ void st_agent(int* p, int v) {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Every thread of a workgroup calls this after its st_agent() writes.  One
-// thread counts the arrival; the last arriver resets the counter.  Returns
-// true in every thread of the last workgroup, which then reads with ld_agent().
+// thread counts the arrival; the last arriver resets the counter and
+// invalidates its caches.  Returns true in every thread of the last
+// workgroup, which may then read the others' data with plain loads.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* flag_lds) {
   wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == expected - 1u;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) {
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // drop this CU's and this XCD's cached copies, so that plain loads of the
+      // other workgroups' data see memory
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     *flag_lds = last;
   }
   __syncthreads();

@@ -65,7 +65,7 @@ struct AttendArgs {
   float* lse;             // nullable [B, Hq, nq]
   int32_t out_bf16;
   int32_t splits;         // workgroups per (bh, query row) in this launch
-  int32_t tiles_per_split;
+  int32_t tiles_per_split; // 16-row blocks per workgroup
   int32_t part;           // 0 all slots, 1 forced slots only, 2 routed slots only
   int32_t part_offset;    // partial slot of this launch's split 0
   int32_t parts_total;    // partial slots per (bh, row) over all launches
@@ -89,7 +89,8 @@ hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t s
 hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
 
 // Workgroup counts and tiling chosen by the host for a given shape.
-constexpr int kTileSlots = 64;     // K/V rows per attention tile
+constexpr int kAttBlockRows = 16;  // K/V rows per attention block
+constexpr int kAttMaxParts = 128;  // partial results per query row (workspace merge)
 int route_chunks_per_slice(const KParams& kp, int64_t nq);
 int attend_max_slots(const KParams& kp);
 

@@ -6,12 +6,15 @@
 //
 // Layout of the work: each (b, kv head, unit) has its candidate chunks
 // [n_sink, j - n_local) split over `slices` workgroups.  A workgroup streams
-// its slice of the fp32 summary table once (D/4 lanes per summary row, one
-// 16-byte load per lane), scores each row against every query vector of the
-// unit (max of the dot products, times 1/sqrt(d)) and writes the scores to the
-// workspace.  The last workgroup of the unit to finish (device-scope counter)
-// selects the top-k, scores the groups of the routed chunks and selects the
-// top-g.  The scan is bound by HBM bandwidth in decode.
+// its slice of the fp32 summary table once.  Eight lanes share one summary row
+// and every load instruction of a wave covers eight whole 128-byte pieces of
+// eight rows; a lane keeps D/8 values of its row and of every query vector,
+// the dot products are reduced over the eight lanes with DPP.  The score of a
+// row is the max over the unit's query vectors of q.s / sqrt(d).  Scores go to
+// the workspace with device-coherent stores; the last workgroup of the unit to
+// finish (device-scope counter) selects the top-k, scores the groups of the
+// routed chunks and selects the top-g.  The scan is bound by HBM bandwidth in
+// decode.
 //
 // In a decode step one extra workgroup per (b, kv head) summarises the chunk
 // that the query completes, so a decode loop keeps the tables current.
@@ -22,10 +25,11 @@ namespace hga {
 
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kQB = 4;      // query vectors per register batch
-constexpr int kRounds = 8;  // summary rows in flight per lane
-
-constexpr int kLdsScores = 4096;  // scores staged in LDS for the selections
+constexpr int kRowLanes = 8;                                    // lanes per summary row
+constexpr int kRowsPerRound = kRouteWaves * kWave / kRowLanes;  // 32 rows per block round
+constexpr int kRounds = 4;                                      // rounds in flight per lane
+constexpr int kQB = 4;                                          // query vectors per register batch
+constexpr int kLdsScores = 4096;                                // scores staged in LDS for the selections
 
 struct RouteSmem {
   TopkSmem<kRouteThreads> topk;
@@ -36,53 +40,62 @@ struct RouteSmem {
 };
 
 // put(i, max over the unit's query vectors of q . row(i) / sqrt(d)) for i in
-// [0, n).  row(i) is a float32 row of D values.
+// [0, n); only lanes with lane % 8 == 0 call put.  row(i) is a float32 row.
 template <typename T, int D, typename RowFn, typename PutFn>
-__device__ void score_rows(const T* __restrict__ qbase, int64_t head_stride, int rows_per_head,
-                           int nqv, const KParams& kp, int n, RowFn row, PutFn put) {
-  constexpr int LPC = D / 4;             // lanes per row (one float4 each)
-  constexpr int CPW = kWave / LPC;       // rows per wave per round
-  constexpr int CPB = CPW * kRouteWaves; // rows per block per round
+__device__ __forceinline__ void score_rows(const T* __restrict__ qbase, int64_t head_stride,
+                                           int rows_per_head, int nqv, const KParams& kp, int n,
+                                           RowFn row, PutFn put) {
+  constexpr int NV = D / 32;  // float4 pieces per lane per row
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  const int sub = lane % LPC;
-  const int cl = lane / LPC;
-  for (int base = 0; base < n; base += CPB * kRounds) {
-    float4 s[kRounds];
-    float mx[kRounds];
+  const int piece = lane % kRowLanes;
+  const int rw = wid * (kWave / kRowLanes) + lane / kRowLanes;  // row within a round
+  for (int base = 0; base < n; base += kRowsPerRound * kRounds) {
+    float4 s[kRounds][NV];
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-      const int i = base + k * CPB + wid * CPW + cl;
-      s[k] = i < n ? reinterpret_cast<const float4*>(row(i))[sub] : make_float4(0.f, 0.f, 0.f, 0.f);
-      mx[k] = -__builtin_huge_valf();
-    }
-    for (int v0 = 0; v0 < nqv; v0 += kQB) {
-      float4 q[kQB];
+      const int i = base + k * kRowsPerRound + rw;
+      const float4* r = i < n ? reinterpret_cast<const float4*>(row(i)) : nullptr;
 #pragma unroll
-      for (int v = 0; v < kQB; ++v) {
-        const int vv = v0 + v < nqv ? v0 + v : nqv - 1;
-        const T* qr = qbase + (vv / rows_per_head) * head_stride +
-                      static_cast<int64_t>(vv % rows_per_head) * D + sub * 4;
-        q[v] = make_float4(elem<T>::get(qr, 0), elem<T>::get(qr, 1), elem<T>::get(qr, 2),
-                           elem<T>::get(qr, 3));
+      for (int v = 0; v < NV; ++v)
+        s[k][v] = r ? r[v * kRowLanes + piece] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mx[kRounds];
+#pragma unroll
+    for (int k = 0; k < kRounds; ++k) mx[k] = -__builtin_huge_valf();
+    for (int v0 = 0; v0 < nqv; v0 += kQB) {
+      float4 q[kQB][NV];
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int vv = v0 + qb < nqv ? v0 + qb : nqv - 1;
+        const T* qr = qbase + (vv / rows_per_head) * head_stride + static_cast<int64_t>(vv % rows_per_head) * D;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int d0 = v * 32 + piece * 4;
+          q[qb][v] = make_float4(elem<T>::get(qr, d0), elem<T>::get(qr, d0 + 1), elem<T>::get(qr, d0 + 2),
+                                 elem<T>::get(qr, d0 + 3));
+        }
       }
 #pragma unroll
       for (int k = 0; k < kRounds; ++k) {
 #pragma unroll
-        for (int v = 0; v < kQB; ++v) {
-          float acc = q[v].x * s[k].x;
-          acc = fmaf(q[v].y, s[k].y, acc);
-          acc = fmaf(q[v].z, s[k].z, acc);
-          acc = fmaf(q[v].w, s[k].w, acc);
-          acc = group_sum<LPC>(acc);
-          mx[k] = fmaxf(mx[k], acc);
+        for (int qb = 0; qb < kQB; ++qb) {
+          float acc = 0.f;
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            acc = fmaf(q[qb][v].x, s[k][v].x, acc);
+            acc = fmaf(q[qb][v].y, s[k][v].y, acc);
+            acc = fmaf(q[qb][v].z, s[k][v].z, acc);
+            acc = fmaf(q[qb][v].w, s[k][v].w, acc);
+          }
+          mx[k] = fmaxf(mx[k], sum8(acc));
         }
       }
     }
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
-      const int i = base + k * CPB + wid * CPW + cl;
-      if (i < n && sub == 0) put(i, mx[k] * kp.inv_sqrt_d);
+      const int i = base + k * kRowsPerRound + rw;
+      if (i < n && piece == 0) put(i, mx[k] * kp.inv_sqrt_d);
     }
   }
 }
@@ -158,12 +171,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   int cnt;
   const float* scand = sc + kp.n_sink;
   if (nM <= kLdsScores) {
-    for (int i = threadIdx.x; i < nM; i += kRouteThreads) sm.scores[i] = ld_agent(scand + i);
+    for (int i = threadIdx.x; i < nM; i += kRouteThreads) sm.scores[i] = scand[i];
     __syncthreads();
     cnt = block_topk<kRouteThreads>([&](int i) { return sm.scores[i]; }, nM, kp.top_k, sm.sel_chunks, sm.topk);
   } else {
-    cnt = block_topk<kRouteThreads>([&](int i) { return ld_agent(scand + i); }, nM, kp.top_k, sm.sel_chunks,
-                                    sm.topk);
+    cnt = block_topk<kRouteThreads>([&](int i) { return scand[i]; }, nM, kp.top_k, sm.sel_chunks, sm.topk);
   }
   int32_t* ci = a.chunk_idx + unit * kp.top_k;
   for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads)
@@ -197,10 +209,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
 }
 
 int route_chunks_per_slice(const KParams& kp, int64_t nq) {
-  // one round-set of rows per lane: kRounds rows of D/4 lanes each per wave
-  const int per_round = (kWave / (kp.d / 4)) * kRouteWaves;
+  (void)kp;
   (void)nq;
-  return per_round * kRounds;
+  return kRowsPerRound * kRounds;
 }
 
 template <typename T, int D>
