@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   auto row_of = [&](int s) -> int64_t {
     if (s >= R1) return -1;
     if (s < nF) {
-      const int fi = s / kp.C, off = s - fi * kp.C;
+      const int fi = kp.log2C >= 0 ? s >> kp.log2C : s / kp.C;
+      const int off = s - fi * kp.C;
       const int c = forced_chunk_at(fc, fi);
       const int64_t tok = static_cast<int64_t>(c) * kp.C + off;
       if (tok > t) return -1;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
       return (static_cast<int64_t>(bh) * a.kv.bh_rows + hs * kp.C + off) * D;
     }
     const int rs = s - nF;
-    const int e = rs / kp.G;
+    const int e = kp.log2G >= 0 ? rs >> kp.log2G : rs / kp.G;
     const int g = sm.gl[e];
     if (g < 0 || g >= n_groups_cap) return -1;
     const int64_t tok = static_cast<int64_t>(g) * kp.G + (rs - e * kp.G);
@@ -360,49 +361,87 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   }
   if (!arrive_last(&a.counters[row_id], static_cast<uint32_t>(a.parts_total), &sm.is_last)) return;
 
-  // ---- last workgroup: merge the parts (plain loads after the acquire)
+  // ---- last workgroup: merge the parts (plain loads after the acquire).  The
+  // output values of all parts are loaded together with their maxima and sums.
   const float* parts = a.partials + row_id * a.parts_total * stride;
   const int P = a.parts_total;
-  for (int e = tid; e < P * GQ; e += kAttThreads) {
-    const int p = e / GQ, hh = e % GQ;
-    sm.pm[e] = parts[p * stride + GQ * D + hh];
-    sm.pl[e] = parts[p * stride + GQ * D + GQ + hh];
+  constexpr int kOut = GQ * D / kAttThreads > 0 ? GQ * D / kAttThreads : 1;  // outputs per thread
+  constexpr int kPR = 16;  // parts held in registers per pass
+  float num[kOut];
+#pragma unroll
+  for (int r = 0; r < kOut; ++r) num[r] = 0.f;
+  for (int p0 = 0; p0 < P; p0 += kPR) {
+    const int np = min(kPR, P - p0);
+    float ov[kPR][kOut];
+#pragma unroll
+    for (int q = 0; q < kPR; ++q)
+#pragma unroll
+      for (int r = 0; r < kOut; ++r) {
+        const int e = tid + r * kAttThreads;
+        ov[q][r] = (q < np && e < GQ * D) ? parts[(p0 + q) * stride + e] : 0.f;
+      }
+    for (int e = tid; e < np * GQ; e += kAttThreads) {
+      const int p = p0 + e / GQ, hh = e % GQ;
+      sm.pm[p * GQ + hh] = parts[p * stride + GQ * D + hh];
+      sm.pl[p * GQ + hh] = parts[p * stride + GQ * D + GQ + hh];
+    }
+    __syncthreads();
+    if (p0 == 0 && tid < GQ) {
+      float M = -__builtin_huge_valf();
+      for (int p = 0; p < P && p < kPR; ++p) M = fmaxf(M, sm.pm[p * GQ + tid]);
+      sm.M[tid] = M;
+    }
+    if (p0 > 0 && tid < GQ) {
+      float M = sm.M[tid];
+      for (int p = p0; p < p0 + np; ++p) M = fmaxf(M, sm.pm[p * GQ + tid]);
+      sm.M[tid] = M;
+    }
+    __syncthreads();
+    if (P <= kPR) {
+#pragma unroll
+      for (int r = 0; r < kOut; ++r) {
+        const int e = tid + r * kAttThreads;
+        if (e >= GQ * D) continue;
+        const int hh = e / D;
+        const float M = sm.M[hh];
+        for (int q = 0; q < np; ++q) {
+          const float mp = sm.pm[q * GQ + hh];
+          if (mp != -__builtin_huge_valf()) num[r] += exp2f(mp - M) * ov[q][r];
+        }
+      }
+    }
   }
-  __syncthreads();
+  if (P > kPR) {
+    // second pass with the final maxima (rare: more than 16 parts per row)
+    for (int r = 0; r < kOut; ++r) {
+      const int e = tid + r * kAttThreads;
+      if (e >= GQ * D) continue;
+      const int hh = e / D;
+      const float M = sm.M[hh];
+      float acc = 0.f;
+      for (int p = 0; p < P; ++p) {
+        const float mp = sm.pm[p * GQ + hh];
+        if (mp != -__builtin_huge_valf()) acc += exp2f(mp - M) * parts[p * stride + e];
+      }
+      num[r] = acc;
+    }
+  }
   if (tid < GQ) {
-    float M = -__builtin_huge_valf();
-    for (int p = 0; p < P; ++p) M = fmaxf(M, sm.pm[p * GQ + tid]);
+    const float M = sm.M[tid];
     float L = 0.f;
     for (int p = 0; p < P; ++p) {
       const float mp = sm.pm[p * GQ + tid];
-      const float wt = mp == -__builtin_huge_valf() ? 0.f : exp2f(mp - M);
-      sm.pm[p * GQ + tid] = wt;
-      L += wt * sm.pl[p * GQ + tid];
+      if (mp != -__builtin_huge_valf()) L += exp2f(mp - M) * sm.pl[p * GQ + tid];
     }
-    sm.M[tid] = M;
     sm.L[tid] = L;
   }
   __syncthreads();
-  for (int e = tid; e < GQ * D; e += kAttThreads) {
+#pragma unroll
+  for (int r = 0; r < kOut; ++r) {
+    const int e = tid + r * kAttThreads;
+    if (e >= GQ * D) continue;
     const int hh = e / D;
-    float num = 0.f;
-    int p = 0;
-    for (; p + 8 <= P; p += 8) {
-      float v[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = parts[(p + r) * stride + e];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float wt = sm.pm[(p + r) * GQ + hh];
-        num += wt == 0.f ? 0.f : wt * v[r];
-      }
-    }
-    for (; p < P; ++p) {
-      const float wt = sm.pm[p * GQ + hh];
-      const float v = parts[p * stride + e];
-      num += wt == 0.f ? 0.f : wt * v;
-    }
-    write_out(hh, e % D, num / sm.L[hh]);
+    write_out(hh, e % D, num[r] / sm.L[hh]);
     if (e % D == 0) write_lse(hh, sm.M[hh], sm.L[hh]);
   }
 }

@@ -91,6 +91,13 @@ hga_status build_kparams(const hga_params* p, int64_t n_cap, KParams& kp) {
   kp.top_g = p->top_g;
   kp.n_cap = n_cap;
   kp.n_chunks_cap = static_cast<int32_t>(n_cap / p->chunk_size);
+  auto ilog2_exact = [](int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return (1 << l) == v ? l : -1;
+  };
+  kp.log2C = ilog2_exact(p->chunk_size);
+  kp.log2G = ilog2_exact(p->group_size);
   kp.inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(p->head_dim)));
   kp.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(p->head_dim)));
   kp.hf_mask = 0;
@@ -108,7 +115,7 @@ size_t elem_bytes(const hga_params* p) { return p->qkv_dtype == HGA_BF16 ? 2 : 4
 // ------------------------------------------------------------------ workspace plans
 struct RoutePlan {
   int n_units, slices, cps;
-  size_t scores_off, gscores_off, counters_off, bytes;
+  size_t scores_off, cand_off, gscores_off, counters_off, bytes;
 };
 
 RoutePlan plan_route(const KParams& kp, int64_t nq, size_t base) {
@@ -123,6 +130,8 @@ RoutePlan plan_route(const KParams& kp, int64_t nq, size_t base) {
   off = align256(off + units * sizeof(uint32_t));
   r.scores_off = off;
   off = align256(off + units * kp.n_chunks_cap * sizeof(float));
+  r.cand_off = off;
+  off = align256(off + units * kp.n_chunks_cap * sizeof(int32_t));
   r.gscores_off = off;
   off = align256(off + units * static_cast<size_t>(kp.top_k) * kp.m * sizeof(float));
   r.bytes = off - base;
@@ -252,6 +261,7 @@ RouteArgs route_args(const KParams& kp, const FullPlan& f, void* ws, const void*
   a.slices = f.route.slices;
   a.chunks_per_slice = f.route.cps;
   a.scores = at<float>(ws, f.route.scores_off);
+  a.cand_ids = at<int32_t>(ws, f.route.cand_off);
   a.gscores = at<float>(ws, f.route.gscores_off);
   a.counters = at<uint32_t>(ws, f.route.counters_off);
   a.chunk_idx = ci;
@@ -393,7 +403,11 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
   const int n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
   AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, group_idx, n_units, O, lse_out,
                              p->out_dtype == HGA_BF16);
-  HGA_TRY_HIP(launch_attend_splitk(a, p->qkv_dtype == HGA_BF16, static_cast<hipStream_t>(stream)), "attend");
+  const bool bf = p->qkv_dtype == HGA_BF16;
+  if (prefill_mfma_supported(kp, bf, nq))
+    HGA_TRY_HIP(launch_attend_prefill_mfma(a, static_cast<hipStream_t>(stream)), "attend (mfma)");
+  else
+    HGA_TRY_HIP(launch_attend_splitk(a, bf, static_cast<hipStream_t>(stream)), "attend");
   return ok();
 }
 
@@ -433,7 +447,10 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
   HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
   AttendArgs aa = attend_args(kp, f, ws, Q, n, nullptr, 0, K, V, gi, f.route.n_units, O, nullptr,
                               p->out_dtype == HGA_BF16);
-  HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+  if (prefill_mfma_supported(kp, bf, n))
+    HGA_TRY_HIP(launch_attend_prefill_mfma(aa, st), "attend (mfma)");
+  else
+    HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
   return ok();
 }
 

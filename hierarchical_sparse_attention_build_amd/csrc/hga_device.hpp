@@ -134,6 +134,26 @@ __device__ __forceinline__ float max_rows(float v) {
   dpp::swap32(v, a, b);
   return fmaxf(a, b);
 }
+// all-reduce max / min over the whole wave
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp::movf<dpp::kRowRor8>(v));
+  v = fmaxf(v, dpp::movf<dpp::kRowRor4>(v));
+  v = fmaxf(v, dpp::movf<dpp::kQuad2301>(v));
+  v = fmaxf(v, dpp::movf<dpp::kQuad1032>(v));
+  return max_rows(v);
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp::movf<dpp::kRowRor8>(v));
+  v = fminf(v, dpp::movf<dpp::kRowRor4>(v));
+  v = fminf(v, dpp::movf<dpp::kQuad2301>(v));
+  v = fminf(v, dpp::movf<dpp::kQuad1032>(v));
+  float a, b;
+  dpp::swap16(v, a, b);
+  v = fminf(a, b);
+  dpp::swap32(v, a, b);
+  return fminf(a, b);
+}
+
 // all-reduce over the 32-lane halves (lane pairs of rows 0/1 and 2/3)
 __device__ __forceinline__ float sum_rowpair(float v) {
   float a, b;
@@ -188,42 +208,52 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Key unique per candidate and ordered like (score desc, index asc).
+__device__ __forceinline__ uint64_t composite_key(float v, int i) {
+  return (static_cast<uint64_t>(order_key(v)) << 32) | static_cast<uint32_t>(~i);
+}
+
 // ---------------------------------------------------------------- top-k
-// Exact selection of the min(k, n) best of sc[0..n) under (score desc, index
-// asc), by radix select on the ordered 32-bit key followed by an index-ordered
-// tie fill.  Writes the selected candidate indices ascending to sel[0..cnt)
-// (sel may be LDS or global) and returns cnt to every thread.  sc may live in
-// LDS or global memory.  Every thread of the block must call it.
+// Exact selection of the min(k, n) best of sc(0..n) under (score desc, index
+// asc).  Writes the selected candidate indices ascending to sel[0..cnt) (LDS or
+// global) and returns cnt in every thread.  Every thread of the block must
+// call it.
+//
+// Scores are first bucketed by value over [min, max] of the finite scores
+// (the bucket map is monotone, so equal scores share a bucket); one histogram
+// finds the bucket that holds the k-th best.  Buckets above it are taken
+// whole; inside it the candidates are ranked exactly by (score, index).  When
+// that bucket is large (many equal or near-equal scores) a radix select on the
+// ordered 32-bit keys finishes the job instead.
 template <int NT>
 struct TopkSmem {
   unsigned hist[256];
   BlockScanSmem<NT> scan;
+  float red[2][NT / kWave];
+  float lo, scale;
   unsigned prefix;
-  int krem;
+  int krem, bucket, above, n_cand;
+  uint64_t cand_key[1024];
 };
 
+__device__ __forceinline__ float sanitize_score(float s) { return s != s ? -__builtin_huge_valf() : s; }
+
+// radix select on the ordered keys (slow path); returns the threshold key and,
+// through krem, how many keys equal to it to take (lowest indices first)
 template <int NT, typename ScoreFn>
-__device__ int block_topk(ScoreFn sc, int n, int k, int* sel, TopkSmem<NT>& sm) {
+__device__ unsigned radix_threshold(ScoreFn sc, int n, int k, int& krem_out, TopkSmem<NT>& sm) {
   const int tid = threadIdx.x;
-  if (k <= 0 || n <= 0) return 0;
-  if (n <= k) {
-    for (int i = tid; i < n; i += NT) sel[i] = i;
-    __syncthreads();
-    return n;
-  }
-  // ---- radix select: threshold key T and how many keys equal to T to take
   unsigned prefix = 0u, mask = 0u;
   int krem = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += NT) sm.hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
-      unsigned key = order_key(sc(i));
+      const unsigned key = order_key(sc(i));
       if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
       unsigned c[4];
       unsigned lsum = 0;
 #pragma unroll
@@ -231,8 +261,8 @@ __device__ int block_topk(ScoreFn sc, int n, int k, int* sel, TopkSmem<NT>& sm) 
         c[r] = sm.hist[255 - 4 * tid - r];
         lsum += c[r];
       }
-      int incl = wave_incl_scan(static_cast<int>(lsum));
-      unsigned above = static_cast<unsigned>(incl) - lsum;  // keys with a larger digit
+      const int incl = wave_incl_scan(static_cast<int>(lsum));
+      unsigned above = static_cast<unsigned>(incl) - lsum;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (above < static_cast<unsigned>(krem) && static_cast<unsigned>(krem) <= above + c[r]) {
@@ -248,32 +278,185 @@ __device__ int block_topk(ScoreFn sc, int n, int k, int* sel, TopkSmem<NT>& sm) 
     mask |= 255u << shift;
     __syncthreads();
   }
-  const unsigned T = prefix;
-  // ---- index-ordered fill: contiguous ranges per thread
+  krem_out = krem;
+  return prefix;
+}
+
+template <int NT, typename ScoreFn>
+__device__ int block_topk(ScoreFn sc_raw, int n, int k, int* sel, TopkSmem<NT>& sm) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  if (k <= 0 || n <= 0) return 0;
+  if (n <= k) {
+    for (int i = tid; i < n; i += NT) sel[i] = i;
+    __syncthreads();
+    return n;
+  }
+  auto sc = [&](int i) { return sanitize_score(sc_raw(i)); };
+  // ---- range of the finite scores
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  for (int i = tid; i < n; i += NT) {
+    const float v = sc(i);
+    if (v > -__builtin_huge_valf() && v < __builtin_huge_valf()) {
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    sm.red[0][wid] = lo;
+    sm.red[1][wid] = hi;
+  }
+  for (int i = tid; i < 256; i += NT) sm.hist[i] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    float l = sm.red[0][0], h = sm.red[1][0];
+    for (int w = 1; w < NT / kWave; ++w) {
+      l = fminf(l, sm.red[0][w]);
+      h = fmaxf(h, sm.red[1][w]);
+    }
+    sm.lo = l;
+    sm.scale = (h > l && h - l < __builtin_huge_valf()) ? 255.99f / (h - l) : 0.f;
+    sm.n_cand = 0;
+  }
+  __syncthreads();
+  const float blo = sm.lo, bscale = sm.scale;
+  // bucket of a score: monotone non-decreasing in the score
+  auto bucket = [&](float v) -> int {
+    if (!(v > -__builtin_huge_valf())) return 0;
+    const float f = (v - blo) * bscale;
+    return f >= 255.f ? 255 : (f > 0.f ? static_cast<int>(f) : 0);
+  };
+  for (int i = tid; i < n; i += NT) atomicAdd(&sm.hist[bucket(sc(i))], 1u);
+  __syncthreads();
+  if (tid < kWave) {
+    unsigned c[4];
+    unsigned lsum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c[r] = sm.hist[255 - 4 * tid - r];
+      lsum += c[r];
+    }
+    const int incl = wave_incl_scan(static_cast<int>(lsum));
+    unsigned above = static_cast<unsigned>(incl) - lsum;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (above < static_cast<unsigned>(k) && static_cast<unsigned>(k) <= above + c[r]) {
+        sm.bucket = 255 - 4 * tid - r;
+        sm.above = static_cast<int>(above);
+      }
+      above += c[r];
+    }
+  }
+  __syncthreads();
+  const int bt = sm.bucket;
+  const int need = k - sm.above;
+  const int n_bt = static_cast<int>(sm.hist[bt]);
+  bool fast = n_bt <= 1024;
+  unsigned T = 0u;
+  int krem = 0;
+  if (fast) {
+    // candidates of the boundary bucket, ranked exactly
+    for (int i = tid; i < n; i += NT) {
+      const float v = sc(i);
+      if (bucket(v) == bt) sm.cand_key[atomicAdd(&sm.n_cand, 1)] = composite_key(v, i);
+    }
+    __syncthreads();
+  } else {
+    T = radix_threshold<NT>(sc, n, k, krem, sm);
+  }
+  // ---- flags in index order (contiguous ranges per thread), then positions
   const int per = (n + NT - 1) / NT;
   const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
-  int n_gt = 0, n_eq = 0;
-  for (int i = b0; i < b1; ++i) {
-    unsigned key = order_key(sc(i));
-    n_gt += key > T;
-    n_eq += key == T;
+  auto selected = [&](int i, int& eq_seen) -> bool {
+    const float v = sc(i);
+    if (fast) {
+      const int bi = bucket(v);
+      if (bi != bt) return bi > bt;
+      const uint64_t mine = composite_key(v, i);
+      int rank = 0;
+      int c = 0;
+      for (; c + 16 <= n_bt; c += 16) {
+        uint64_t w[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w[r] = sm.cand_key[c + r];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rank += w[r] > mine;
+      }
+      for (; c < n_bt; ++c) rank += sm.cand_key[c] > mine;
+      return rank < need;
+    }
+    const unsigned key = order_key(v);
+    if (key != T) return key > T;
+    return eq_seen++ < krem;
+  };
+  int eq_before = 0;
+  if (!fast) {
+    int n_eq = 0;
+    for (int i = b0; i < b1; ++i) n_eq += order_key(sc(i)) == T;
+    int tot;
+    eq_before = block_excl_scan<NT>(n_eq, tot, sm.scan);
+  }
+  int cnt_local = 0;
+  {
+    int eq_seen = eq_before;
+    for (int i = b0; i < b1; ++i) cnt_local += selected(i, eq_seen);
   }
   int tot;
-  int eq_before = block_excl_scan<NT>(n_eq, tot, sm.scan);
-  int take_eq = max(0, min(n_eq, krem - eq_before));
-  int out_before = block_excl_scan<NT>(n_gt + take_eq, tot, sm.scan);
-  int pos = out_before, eq_seen = eq_before;
-  for (int i = b0; i < b1; ++i) {
-    unsigned key = order_key(sc(i));
-    bool s = key > T;
-    if (key == T) {
-      s = eq_seen < krem;
-      ++eq_seen;
-    }
-    if (s) sel[pos++] = i;
+  int pos = block_excl_scan<NT>(cnt_local, tot, sm.scan);
+  {
+    int eq_seen = eq_before;
+    for (int i = b0; i < b1; ++i)
+      if (selected(i, eq_seen)) sel[pos++] = i;
   }
   __syncthreads();
   return k;
+}
+
+// Exact top-k for n <= NT candidates, one per thread: thread i (< n) passes its
+// score v and candidate index i.  Each candidate gets the composite key
+// (ordered score << 32 | ~i), unique and ordered like (score desc, index asc);
+// rank = number of larger keys, counted with one 64-bit compare per pair.  The
+// selected ones (rank < k) are written to sel[] in ascending index order.
+// Returns min(n, k).
+template <int NT>
+struct RankSmem {
+  uint64_t keys[NT];
+  int wave_cnt[NT / kWave];
+};
+
+template <int NT>
+__device__ int rank_select(float v, int n, int k, int* sel, RankSmem<NT>& sm) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const uint64_t mine = composite_key(v, tid);
+  if (tid < n) sm.keys[tid] = mine;
+  __syncthreads();
+  bool take = false;
+  if (tid < n) {
+    int rank = 0;
+    int j = 0;
+    for (; j + 16 <= n; j += 16) {
+      uint64_t w[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w[r] = sm.keys[j + r];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rank += w[r] > mine;
+    }
+    for (; j < n; ++j) rank += sm.keys[j] > mine;
+    take = rank < k;
+  }
+  const uint64_t ballot = __ballot(take);
+  if (lane == 0) sm.wave_cnt[wid] = __popcll(ballot);
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += sm.wave_cnt[w];
+  if (take) sel[before + __popcll(ballot & ((uint64_t(1) << lane) - 1))] = tid;
+  __syncthreads();
+  return n < k ? n : k;
 }
 
 // ---------------------------------------------------------------- cross-workgroup hand-off

@@ -35,7 +35,8 @@ struct RouteArgs {
   int32_t n_units;        // units per (b, kv head)
   int32_t slices;         // scan workgroups per unit
   int32_t chunks_per_slice;
-  float* scores;          // ws [B*Hkv*n_units, n_chunks_cap]
+  float* scores;          // ws [B*Hkv*n_units, n_chunks_cap]: published slice winners
+  int32_t* cand_ids;      // ws [B*Hkv*n_units, n_chunks_cap]
   float* gscores;         // ws [B*Hkv*n_units, top_k*m]
   uint32_t* counters;     // ws [B*Hkv*n_units], zero between calls
   int32_t* chunk_idx;     // [B*Hkv*n_units, top_k]
@@ -87,6 +88,9 @@ hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st
 hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipStream_t st);
 hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
+// Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
+bool prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
+hipError_t launch_attend_prefill_mfma(const AttendArgs& a, hipStream_t st);
 
 // Workgroup counts and tiling chosen by the host for a given shape.
 constexpr int kAttBlockRows = 16;  // K/V rows per attention block

@@ -12,6 +12,7 @@ struct KParams {
   int32_t n_sink, n_local, top_k, top_g;
   int64_t n_cap;        // token capacity of K/V rows per (b, kv head)
   int32_t n_chunks_cap; // n_cap / C
+  int32_t log2C, log2G; // log2 of C and G when they are powers of two, else -1
   float inv_sqrt_d;     // 1 / sqrt(d)
   float scale_log2;     // log2(e) / sqrt(d): attention scores are kept in base-2 units
   uint64_t hf_mask;     // bit i set: RoPE pair i is high-frequency

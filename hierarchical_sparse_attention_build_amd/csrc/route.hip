@@ -10,11 +10,13 @@
 // and every load instruction of a wave covers eight whole 128-byte pieces of
 // eight rows; a lane keeps D/8 values of its row and of every query vector,
 // the dot products are reduced over the eight lanes with DPP.  The score of a
-// row is the max over the unit's query vectors of q.s / sqrt(d).  Scores go to
-// the workspace with device-coherent stores; the last workgroup of the unit to
-// finish (device-scope counter) selects the top-k, scores the groups of the
-// routed chunks and selects the top-g.  The scan is bound by HBM bandwidth in
-// decode.
+// row is the max over the unit's query vectors of q.s / sqrt(d).  Every
+// workgroup keeps the top-k of its own slice (a chunk of the global top-k is
+// in the top-k of its slice) and publishes those (score, chunk) pairs with
+// device-coherent stores; the last workgroup of the unit to finish
+// (device-scope counter) selects the top-k among them, scores the groups of
+// the routed chunks and selects the top-g.  The scan is bound by HBM
+// bandwidth in decode.
 //
 // In a decode step one extra workgroup per (b, kv head) summarises the chunk
 // that the query completes, so a decode loop keeps the tables current.
@@ -29,15 +31,27 @@ constexpr int kRowLanes = 8;                                    // lanes per sum
 constexpr int kRowsPerRound = kRouteWaves * kWave / kRowLanes;  // 32 rows per block round
 constexpr int kRounds = 4;                                      // rounds in flight per lane
 constexpr int kQB = 4;                                          // query vectors per register batch
-constexpr int kLdsScores = 4096;                                // scores staged in LDS for the selections
+constexpr int kSliceRows = kRowsPerRound * kRounds;             // candidate chunks per workgroup
+constexpr int kLdsCand = 2048;                                  // candidates staged in LDS for the selections
 
 struct RouteSmem {
   TopkSmem<kRouteThreads> topk;
+  RankSmem<kRouteThreads> rank;
+  float loc[kSliceRows];
+  int loc_sel[kSliceRows];
   int sel_chunks[1024];
   int sel_groups[1024];
-  float scores[kLdsScores];
+  float cand_s[kLdsCand];
+  int cand_i[kLdsCand];
   int is_last;
 };
+
+// number of slice-local winners published by slice x (and, summed, the offset
+// of slice x's entries): min(k, rows of the slice)
+__device__ __forceinline__ int slice_count(int x, int nM, int cps, int k) {
+  const int rows = max(0, min(cps, nM - x * cps));
+  return min(k, rows);
+}
 
 // put(i, max over the unit's query vectors of q . row(i) / sqrt(d)) for i in
 // [0, n); only lanes with lane % 8 == 0 call put.  row(i) is a float32 row.
@@ -153,56 +167,100 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
                     (prefill ? static_cast<int64_t>(u) * kp.C : 0)) * D;
   const int64_t head_stride = a.nq * D;
 
-  float* sc = a.scores + unit * kp.n_chunks_cap;
+  float* cand_s = a.scores + unit * kp.n_chunks_cap;   // published (score, chunk) pairs
+  int* cand_i = a.cand_ids + unit * kp.n_chunks_cap;
   const float* ctab = a.chunk_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * D;
   float* sc_out = a.scores_out ? a.scores_out + static_cast<int64_t>(bh) * kp.n_chunks_cap : nullptr;
   if (n_here > 0) {
     score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, kp, n_here,
                      [&](int i) { return ctab + static_cast<int64_t>(c_lo + i) * D; },
                      [&](int i, float v) {
-                       st_agent(sc + c_lo + i, v);
+                       sm.loc[i] = v;
                        if (sc_out) sc_out[c_lo + i] = v;
                      });
+  }
+  __syncthreads();
+  // ---- top-k of this slice, published in ascending chunk order
+  {
+    int off = 0;
+    for (int xx = 0; xx < x; ++xx) off += slice_count(xx, nM, a.chunks_per_slice, kp.top_k);
+    const int kk = slice_count(x, nM, a.chunks_per_slice, kp.top_k);
+    if (kk > 0) {
+      if (kk < n_here) {
+        rank_select<kRouteThreads>(threadIdx.x < n_here ? sm.loc[threadIdx.x] : 0.f, n_here, kk, sm.loc_sel,
+                                   sm.rank);
+        for (int r = threadIdx.x; r < kk; r += kRouteThreads) {
+          const int i = sm.loc_sel[r];
+          st_agent(cand_s + off + r, sm.loc[i]);
+          st_agent(cand_i + off + r, c_lo + i);
+        }
+      } else {
+        for (int r = threadIdx.x; r < kk; r += kRouteThreads) {
+          st_agent(cand_s + off + r, sm.loc[r]);
+          st_agent(cand_i + off + r, c_lo + r);
+        }
+      }
+    }
   }
 
   // ---- last workgroup of the unit does the selections
   if (!arrive_last(&a.counters[unit], static_cast<uint32_t>(a.slices), &sm.is_last)) return;
 
-  int cnt;
-  const float* scand = sc + kp.n_sink;
-  if (nM <= kLdsScores) {
-    for (int i = threadIdx.x; i < nM; i += kRouteThreads) sm.scores[i] = scand[i];
-    __syncthreads();
-    cnt = block_topk<kRouteThreads>([&](int i) { return sm.scores[i]; }, nM, kp.top_k, sm.sel_chunks, sm.topk);
-  } else {
-    cnt = block_topk<kRouteThreads>([&](int i) { return scand[i]; }, nM, kp.top_k, sm.sel_chunks, sm.topk);
+  int n_c = 0;
+  for (int xx = 0; xx < a.slices; ++xx) n_c += slice_count(xx, nM, a.chunks_per_slice, kp.top_k);
+  const bool in_lds = n_c <= kLdsCand;
+  if (in_lds) {
+    for (int i = threadIdx.x; i < n_c; i += kRouteThreads) {
+      sm.cand_s[i] = cand_s[i];
+      sm.cand_i[i] = cand_i[i];
+    }
   }
+  __syncthreads();
+  // candidates are in ascending chunk order, so position order breaks ties
+  int cnt;
+  if (n_c <= kRouteThreads) {
+    cnt = rank_select<kRouteThreads>(threadIdx.x < n_c ? sm.cand_s[threadIdx.x] : 0.f, n_c, kp.top_k,
+                                     sm.sel_chunks, sm.rank);
+  } else if (in_lds) {
+    cnt = block_topk<kRouteThreads>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
+  } else {
+    cnt = block_topk<kRouteThreads>([&](int i) { return cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
+  }
+  // selected positions -> chunk ids (ascending)
+  for (int i = threadIdx.x; i < cnt; i += kRouteThreads) {
+    const int pos = sm.sel_chunks[i];
+    sm.sel_chunks[i] = in_lds ? sm.cand_i[pos] : cand_i[pos];
+  }
+  __syncthreads();
   int32_t* ci = a.chunk_idx + unit * kp.top_k;
-  for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads)
-    ci[i] = i < cnt ? kp.n_sink + sm.sel_chunks[i] : -1;
+  for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads) ci[i] = i < cnt ? sm.sel_chunks[i] : -1;
 
   const int nG = cnt * kp.m;
   const int m = kp.m;
   const float* gtab = a.group_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m * D;
-  float* gsc = nG <= kLdsScores ? sm.scores : a.gscores + unit * static_cast<int64_t>(kp.top_k) * kp.m;
-  __syncthreads();  // sm.scores is reused for the group scores
+  float* gsc = nG <= kLdsCand ? sm.cand_s : a.gscores + unit * static_cast<int64_t>(kp.top_k) * kp.m;
   if (nG > 0) {
     score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, kp, nG,
                      [&](int i) {
-                       const int64_t gid = static_cast<int64_t>(kp.n_sink + sm.sel_chunks[i / m]) * m + i % m;
+                       const int64_t gid = static_cast<int64_t>(sm.sel_chunks[i / m]) * m + i % m;
                        return gtab + gid * D;
                      },
                      [&](int i, float v) { gsc[i] = v; });
   }
   __threadfence_block();
   __syncthreads();
-  const int gcnt = block_topk<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
+  int gcnt;
+  if (nG <= kRouteThreads)
+    gcnt = rank_select<kRouteThreads>(threadIdx.x < nG ? gsc[threadIdx.x] : 0.f, nG, kp.top_g, sm.sel_groups,
+                                      sm.rank);
+  else
+    gcnt = block_topk<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
   int32_t* gi = a.group_idx + unit * kp.top_g;
   for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) {
     int32_t v = -1;
     if (i < gcnt) {
       const int sg = sm.sel_groups[i];
-      v = (kp.n_sink + sm.sel_chunks[sg / m]) * m + sg % m;
+      v = sm.sel_chunks[sg / m] * m + sg % m;
     }
     gi[i] = v;
   }
@@ -211,7 +269,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
 int route_chunks_per_slice(const KParams& kp, int64_t nq) {
   (void)kp;
   (void)nq;
-  return kRowsPerRound * kRounds;
+  return kSliceRows;
 }
 
 template <typename T, int D>

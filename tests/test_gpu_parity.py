@@ -389,3 +389,81 @@ def test_nan_summaries_after_routing_leave_output_unchanged(hga):
     torch.cuda.synchronize()
     assert torch.isfinite(out2).all()
     assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("case", ["all_tied_small", "all_tied_large", "two_levels", "nan_rows"])
+def test_route_ties_and_nan(hga, case):
+    """Selections on hand-made summary tables: exact ties go to the lower index
+    (both the bucket path and the radix path of the top-k), NaN scores rank
+    with -inf."""
+    n = 131072 if case == "all_tied_large" else 8192
+    s = W.spec("decode_32k", batch=1, n_q_heads=2, n_kv_heads=1, n_tokens=n, top_k=40, top_g=100)
+    say(f"[route ties] {case} n={n}")
+    rng = np.random.default_rng(7)
+    d, C, G = s.head_dim, s.chunk_size, s.group_size
+    nC, m = n // C, C // G
+    Q = rng.standard_normal((1, 2, 1, d)).astype(np.float32)
+    Qb = W.bf16_bits(Q)
+    Qf = W.to_f64(Qb, "bf16")
+    if case.startswith("all_tied"):
+        cs = np.tile(rng.standard_normal(d), (1, 1, nC, 1))
+        gs = np.tile(rng.standard_normal(d), (1, 1, nC * m, 1))
+    elif case == "two_levels":
+        base = rng.standard_normal(d)
+        cs = np.tile(base, (1, 1, nC, 1)) * np.where(rng.random(nC) < 0.5, 1.0, 2.0)[None, None, :, None]
+        gs = rng.standard_normal((1, 1, nC * m, d))
+    else:
+        cs = rng.standard_normal((1, 1, nC, d))
+        gs = rng.standard_normal((1, 1, nC * m, d))
+        cs[0, 0, rng.choice(nC, 50, replace=False)] = np.nan
+        gs[0, 0, rng.choice(nC * m, 200, replace=False)] = np.nan
+    cs32, gs32 = cs.astype(np.float32), gs.astype(np.float32)
+    cfg = cfg_of(s)
+    q_pos = np.array([n - 1], dtype=np.int32)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, cs32.astype(np.float64), gs32.astype(np.float64), cfg, 1)
+    p = params_of(s)
+    ci = torch.empty((1, 1, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((1, 1, 1, s.top_g), dtype=torch.int32, device="cuda")
+    ws = hga.workspace(p, hga.OP_ROUTE, 1, n)
+    hga.route(p, dev(Qb, "bf16"), 1, torch.from_numpy(q_pos).cuda(), torch.from_numpy(cs32).cuda(),
+              torch.from_numpy(gs32).cuda(), n, ci, gi, ws)
+    torch.cuda.synchronize()
+    g_ci, g_gi = ci.cpu().numpy(), gi.cpu().numpy()
+    if case in ("all_tied_small", "all_tied_large", "nan_rows"):
+        # ties are exact on both sides: the sets must be identical
+        np.testing.assert_array_equal(g_ci, or_ci)
+        np.testing.assert_array_equal(g_gi, or_gi)
+    else:
+        check_routing(g_ci, g_gi, or_ci, or_gi, diags, s.top_k, s.top_g)
+    if case.startswith("all_tied"):
+        assert g_ci[0, 0, 0].tolist() == list(range(s.n_sink, s.n_sink + s.top_k))
+
+
+def test_attend_masks_holes_in_group_list(hga):
+    """-1 entries anywhere in a group list contribute nothing."""
+    s = W.spec("decode_32k", batch=2, n_tokens=4096)
+    say(f"[attend holes] seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    rng = np.random.default_rng(3)
+    q_pos = (w.seq_len - 1).astype(np.int32)
+    j = int(q_pos[0]) // s.chunk_size
+    m = s.chunk_size // s.group_size
+    gi = np.full((s.batch, s.n_kv_heads, 1, s.top_g), -1, dtype=np.int32)
+    for b in range(s.batch):
+        for h in range(s.n_kv_heads):
+            pool = np.arange(s.n_sink * m, (j - s.n_local) * m)
+            pick = np.sort(rng.choice(pool, s.top_g, replace=False))
+            keep = rng.random(s.top_g) < 0.6
+            gi[b, h, 0] = np.where(keep, pick, -1)
+    Oo, _ = O.attend(Qf, q_pos, Kf, Vf, gi, cfg, s.n_kv_heads)
+    p = params_of(s)
+    out = torch.empty((s.batch, s.n_q_heads, 1, s.head_dim), device="cuda")
+    ws = hga.workspace(p, hga.OP_ATTEND, 1, s.n_tokens)
+    hga.attend(p, dev(w.Q, s.dtype), 1, torch.from_numpy(q_pos).cuda(), dev(w.K, s.dtype), dev(w.V, s.dtype),
+               s.n_tokens, torch.from_numpy(gi).cuda(), out, ws)
+    torch.cuda.synchronize()
+    e = max_abs(out.cpu().numpy(), Oo)
+    say(f"  O max-abs {e:.3e}")
+    assert e <= TOL[s.dtype]
