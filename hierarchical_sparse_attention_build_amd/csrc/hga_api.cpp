@@ -378,9 +378,11 @@ hga_status hga_route(const hga_params* p, const void* Q, int64_t nq, const int32
   FullPlan f = plan(kp, HGA_OP_ROUTE, nq);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   RouteArgs a = route_args(kp, f, ws, Q, nq, q_pos, 0, chunk_sum, group_sum, chunk_idx, group_idx, scores_out);
-  HGA_TRY_HIP(launch_route_scan(a, p->qkv_dtype == HGA_BF16, p->qkv_dtype == HGA_BF16,
-                                static_cast<hipStream_t>(stream)),
-              "route");
+  const bool bf = p->qkv_dtype == HGA_BF16;
+  if (route_prefill_mfma_supported(kp, bf, nq))
+    HGA_TRY_HIP(launch_route_prefill_mfma(a, static_cast<hipStream_t>(stream)), "route (mfma)");
+  else
+    HGA_TRY_HIP(launch_route_scan(a, bf, bf, static_cast<hipStream_t>(stream)), "route");
   return ok();
 }
 
@@ -444,7 +446,10 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
   sa.rotated = 1;
   HGA_TRY_HIP(launch_summaries(sa, bf, st), "summaries");
   RouteArgs ra = route_args(kp, f, ws, Q, n, nullptr, 0, chunk_sum, group_sum, ci, gi, nullptr);
-  HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
+  if (route_prefill_mfma_supported(kp, bf, n))
+    HGA_TRY_HIP(launch_route_prefill_mfma(ra, st), "route (mfma)");
+  else
+    HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
   AttendArgs aa = attend_args(kp, f, ws, Q, n, nullptr, 0, K, V, gi, f.route.n_units, O, nullptr,
                               p->out_dtype == HGA_BF16);
   if (prefill_mfma_supported(kp, bf, n))

@@ -91,6 +91,9 @@ hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
 // Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
 bool prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_attend_prefill_mfma(const AttendArgs& a, hipStream_t st);
+// Prefill routing on the matrix cores (bf16, C = 64, Hq/Hkv <= 4).
+bool route_prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
+hipError_t launch_route_prefill_mfma(const RouteArgs& a, hipStream_t st);
 
 // Workgroup counts and tiling chosen by the host for a given shape.
 constexpr int kAttBlockRows = 16;  // K/V rows per attention block

@@ -467,3 +467,43 @@ def test_attend_masks_holes_in_group_list(hga):
     e = max_abs(out.cpu().numpy(), Oo)
     say(f"  O max-abs {e:.3e}")
     assert e <= TOL[s.dtype]
+
+
+def test_prefill_full_size_32k(hga):
+    """The benchmarked prefill workload at full size (32K tokens, 32/8 heads),
+    checked on a sample of units spread over the sequence and the heads."""
+    s = W.spec("prefill_32k")
+    say(f"[prefill full] prefill_32k seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    p = params_of(s)
+    B, H, n, C = s.batch, s.n_kv_heads, s.n_tokens, s.chunk_size
+    nU = n // C
+    cs, gs = _summ_tables(s)
+    ci = torch.empty((B, H, nU, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, nU, s.top_g), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, n, s.head_dim), device="cuda")
+    ws = hga.workspace(p, hga.OP_PREFILL, n, n)
+    hga.prefill(p, dev(w.Q, s.dtype), dev(w.K, s.dtype), dev(w.V, s.dtype), n, cs, gs, out, ws,
+                chunk_idx=ci, group_idx=gi)
+    torch.cuda.synchronize()
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    assert max_abs(cs.cpu().numpy(), ocs) < 1e-5
+    assert max_abs(gs.cpu().numpy(), ogs) < 1e-5
+    rng = np.random.default_rng(0)
+    units = [(0, h, u) for h in range(H) for u in sorted(rng.choice(nU, 5, replace=False).tolist())]
+    units += [(0, 0, 0), (0, 3, 1), (0, 5, 2), (0, 7, nU - 1)]
+    q_pos = np.zeros(B, dtype=np.int64)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, H, units=units)
+    n_units, unique = check_routing(ci.cpu().numpy(), gi.cpu().numpy(), or_ci, or_gi, diags, s.top_k, s.top_g)
+    got = out.cpu().numpy()
+    gq = s.n_q_heads // H
+    emax = 0.0
+    for (b, h, u) in sorted(unique):
+        o, _ = O.attend_unit_block(Qf, q_pos, Kf, Vf, or_gi, cfg, H, b, h, u)
+        emax = max(emax, max_abs(got[b, h * gq:(h + 1) * gq, u * C:(u + 1) * C], o))
+    say(f"  sampled units {n_units} unique {len(unique)}  O max-abs {emax:.3e}")
+    assert emax <= TOL[s.dtype]
+    assert len(unique) >= 0.5 * n_units
+    assert np.isfinite(got).all()
