@@ -20,6 +20,9 @@
 //                      permuted consistently on the V^T side), so no P
 //                      round trip through LDS is needed.
 // P is rounded to fp16 (2^-11 relative), V to fp16 exactly for |v| < 65504.
+// The running max is raised only when a tile's max exceeds it by more than
+// 2^8 (base 2): O / l does not depend on the reference max, p stays <= 256,
+// and most tiles skip the rescale of the accumulators.
 #include "hga_device.hpp"
 #include "hga_kernels.hpp"
 
@@ -28,6 +31,7 @@ namespace hga {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kPTile = 64;  // keys per tile
@@ -48,8 +52,6 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_mfma_kernel(AttendArgs
   constexpr int KSTEPS = D / 16;             // QK^T k-steps
   constexpr int DBLK = D / 32;               // output blocks of 32 dims
   constexpr int CH = D / 8;                  // 16-byte chunks per row
-  constexpr int CPT = kPTile * CH / NT;       // chunks per thread per tile (K and V each)
-  static_assert(CPT >= 1 && kPTile * CH % NT == 0, "tile split");
   using Smem = PrefillSmem<D>;
   const KParams& kp = a.kp;
 
@@ -114,43 +116,55 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_mfma_kernel(AttendArgs
     if (tt == 0) return static_cast<int64_t>(j) * kPTile + r;
     if (tt <= n_forced_other) return static_cast<int64_t>(forced_chunk_at(fc, tt - 1)) * kPTile + r;
     const int rt = tt - 1 - n_forced_other;
-    const int e = rt * gpt + r / kp.G;
+    const int rg = kp.log2G >= 0 ? r >> kp.log2G : r / kp.G;
+    const int e = rt * gpt + rg;
     if (e >= kp.top_g) return -1;
     const int g = sm.gl[e];
     if (g < 0 || g >= n_groups_cap) return -1;
-    return static_cast<int64_t>(g) * kp.G + r % kp.G;
+    return static_cast<int64_t>(g) * kp.G + (r - rg * kp.G);
   };
 
-  uint4 kreg[CPT], vreg[CPT];
-  bool rok[CPT];
+  // Each thread moves CPT 16-byte pieces of K and of V per tile: pieces of two
+  // adjacent rows (same columns), so that V^T gets packed pairs of fp16 keys.
+  constexpr int PAIRS = kPTile / 2 * CH;
+  constexpr int NPAIR = (PAIRS + NT - 1) / NT;
+  uint4 kreg[2 * NPAIR], vreg[2 * NPAIR];
   auto fetch = [&](int tt) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cid = tid + i * NT;
-      const int r = cid / CH, c = cid % CH;
-      const int64_t tok = tile_token(tt, r);
-      rok[i] = tok >= 0;
-      if (rok[i]) {
-        const int64_t off = (static_cast<int64_t>(bh) * kp.n_cap + tok) * D + c * 8;
-        kreg[i] = *reinterpret_cast<const uint4*>(Kb + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(Vb + off);
-      } else {
-        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
-        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < NPAIR; ++i) {
+      const int q = tid + i * NT;
+      if (PAIRS % NT != 0 && q >= PAIRS) break;
+      const int r = 2 * (q / CH), c = q % CH;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int64_t tok = tile_token(tt, r + w);
+        if (tok >= 0) {
+          const int64_t off = (static_cast<int64_t>(bh) * kp.n_cap + tok) * D + c * 8;
+          kreg[2 * i + w] = *reinterpret_cast<const uint4*>(Kb + off);
+          vreg[2 * i + w] = *reinterpret_cast<const uint4*>(Vb + off);
+        } else {
+          kreg[2 * i + w] = make_uint4(0u, 0u, 0u, 0u);
+          vreg[2 * i + w] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
   };
   auto stage = [&](int buf, int tt) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cid = tid + i * NT;
-      const int r = cid / CH, c = cid % CH;
-      *reinterpret_cast<uint4*>(&sm.k[buf][r * Smem::KROW + c * 16]) = kreg[i];
-      const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+    for (int i = 0; i < NPAIR; ++i) {
+      const int q = tid + i * NT;
+      if (PAIRS % NT != 0 && q >= PAIRS) break;
+      const int r = 2 * (q / CH), c = q % CH;
+      *reinterpret_cast<uint4*>(&sm.k[buf][r * Smem::KROW + c * 16]) = kreg[2 * i];
+      *reinterpret_cast<uint4*>(&sm.k[buf][(r + 1) * Smem::KROW + c * 16]) = kreg[2 * i + 1];
+      const uint32_t w0[4] = {vreg[2 * i].x, vreg[2 * i].y, vreg[2 * i].z, vreg[2 * i].w};
+      const uint32_t w1[4] = {vreg[2 * i + 1].x, vreg[2 * i + 1].y, vreg[2 * i + 1].z, vreg[2 * i + 1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float f = (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
-        *reinterpret_cast<_Float16*>(&sm.vt[buf][(c * 8 + e) * Smem::VROW + r * 2]) = static_cast<_Float16>(f);
+        const float f0 = (e & 1) ? bf16hi(w0[e >> 1]) : bf16lo(w0[e >> 1]);
+        const float f1 = (e & 1) ? bf16hi(w1[e >> 1]) : bf16lo(w1[e >> 1]);
+        const f16x2_t h2 = {static_cast<_Float16>(f0), static_cast<_Float16>(f1)};
+        *reinterpret_cast<f16x2_t*>(&sm.vt[buf][(c * 8 + e) * Smem::VROW + r * 2]) = h2;
       }
     }
     if (tid < kPTile) {
@@ -186,35 +200,51 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_mfma_kernel(AttendArgs
     }
     // ---- online softmax (this lane: one query, 32 keys; partner lane: the rest)
     const uint64_t vmask = sm.valid[buf];
+    const bool full = tt > 0 && vmask == ~0ull;  // uniform: no masked key in the tile
     float tmax = -__builtin_huge_valf();
+    if (full) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kt = 32 * blk + 8 * (v >> 2) + 4 * hb + (v & 3);
-        bool ok = (vmask >> kt) & 1ull;
-        if (tt == 0) ok = ok && kt <= pos0 + ql;  // causal inside the current chunk
-        const float sv = ok ? s[blk][v] * scale : -__builtin_huge_valf();
-        s[blk][v] = sv;
-        tmax = fmaxf(tmax, sv);
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[blk][v]);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kt = 32 * blk + 8 * (v >> 2) + 4 * hb + (v & 3);
+          bool ok = (vmask >> kt) & 1ull;
+          if (tt == 0) ok = ok && kt <= pos0 + ql;  // causal inside the current chunk
+          const float sv = ok ? s[blk][v] : -__builtin_huge_valf();
+          s[blk][v] = sv;
+          tmax = fmaxf(tmax, sv);
+        }
       }
     }
     {
       float pa, pb;
       dpp::swap32(tmax, pa, pb);
-      tmax = fmaxf(pa, pb);
+      tmax = fmaxf(pa, pb) * scale;
     }
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_run == -__builtin_huge_valf() ? 0.f : exp2f(m_run - m_new);
+    // raise the reference max only when this tile's max exceeds it by > 8
+    const bool raise = !(tmax <= m_run + 8.f);
+    if (__ballot(raise)) {
+      const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
+      const float alpha = m_run == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
     float rs = 0.f;
     f16x8_t pk[4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(s[blk][v] - m_new);
-        rs += p;
-        pk[2 * blk + (v >> 3)][v & 7] = static_cast<_Float16>(p);
+        const _Float16 ph = static_cast<_Float16>(__builtin_amdgcn_exp2f(fmaf(s[blk][v], scale, -m_run)));
+        rs += static_cast<float>(ph);  // normalise by the weights actually used
+        pk[2 * blk + (v >> 3)][v & 7] = ph;
       }
     }
     {
@@ -222,10 +252,7 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_mfma_kernel(AttendArgs
       dpp::swap32(rs, pa, pb);
       rs = pa + pb;
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+    l_run += rs;
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
