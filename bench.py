@@ -73,7 +73,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy, a known-size reference for HBM counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -89,6 +91,14 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     dev = torch.device("cuda:0")
     hga.lib()
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x 1 GiB device-to-device copies done")
 
     s = W.spec("decode_32k")
     log(f"[bench] generating {s.name} (seed {s.seed})")
@@ -239,7 +249,34 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def prefill_flops(s):
+    """Algorithmic attention FLOPs of a full prefill: 4*d per (query row, visible key)."""
+    C, G = s.chunk_size, s.group_size
+    m = C // G
+    pairs = 0
+    for j in range(s.n_tokens // C):
+        n_forced_full = len(set(range(min(s.n_sink, j + 1))) | set(range(max(0, j - s.n_local), j)))
+        n_cand = max(0, j - s.n_local - s.n_sink)
+        routed = min(s.top_g, min(s.top_k, n_cand) * m) * G
+        pairs += C * (n_forced_full * C + routed) + C * (C + 1) // 2
+    return pairs * s.n_q_heads * s.batch * 4 * s.head_dim
+
+
+def routing_flops(s):
+    """Algorithmic routing FLOPs: 2*d per (query row, scored summary), chunks and groups."""
+    C, G = s.chunk_size, s.group_size
+    m = C // G
+    gq = s.n_q_heads // s.n_kv_heads
+    tot = 0
+    for j in range(s.n_tokens // C):
+        n_cand = max(0, j - s.n_local - s.n_sink)
+        tot += n_cand + min(s.top_k, n_cand) * m
+    return tot * gq * C * s.n_kv_heads * s.batch * 2 * s.head_dim
+
+
 def bench_prefill(args, dev):
+    """hga_prefill on the 32K workload: the whole call, and each of its three
+    kernels launched alone (same launch configurations) timed with HIP events."""
     import torch
     from hierarchical_sparse_attention_build_amd import hga
     from hierarchical_sparse_attention_build_amd import workloads as W
@@ -256,31 +293,48 @@ def bench_prefill(args, dev):
     cs = torch.empty((B, H, nC, d), device=dev)
     gs = torch.empty((B, H, nC * (C // G), d), device=dev)
     O = torch.empty((B, Hq, n, d), device=dev)
+    ci = torch.empty((B, H, nC, s.top_k), dtype=torch.int32, device=dev)
+    gi = torch.empty((B, H, nC, s.top_g), dtype=torch.int32, device=dev)
     ws = hga.workspace(p, hga.OP_PREFILL, n, n, device=dev)
-    hga.prefill(p, Q, K, V, n, cs, gs, O, ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.prefill_steps):
-        hga.prefill(p, Q, K, V, n, cs, gs, O, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.prefill_steps
-    # algorithmic attention FLOPs: 4*d per (query row, visible key) pair
-    pairs = 0
-    m = C // G
-    for j in range(nC):
-        n_forced_full = len(set(range(min(s.n_sink, j + 1))) | set(range(max(0, j - s.n_local), j)))
-        n_cand = max(0, j - s.n_local - s.n_sink)
-        routed = min(s.top_g, min(s.top_k, n_cand) * m) * G
-        pairs += C * (n_forced_full * C + routed) + C * (C + 1) // 2
-    flops = pairs * Hq * B * 4 * d
-    tf = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] prefill {ms:.2f} ms, attention {flops / 1e9:.1f} GFLOP -> {tf:.1f} TFLOP/s")
-    return {"workload": "prefill_32k", "ms": round(ms, 4), "query_tokens_per_s": round(B * n / (ms * 1e-3), 1),
-            "attention_gflop": round(flops / 1e9, 2),
-            "attention_tflops_whole_call": round(tf, 2),
-            "mfma_frac_whole_call": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    wsr = hga.workspace(p, hga.OP_ROUTE, n, n, device=dev)
+    wsa = hga.workspace(p, hga.OP_ATTEND, n, n, device=dev)
+    qpos = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    reps = max(1, args.prefill_steps)
+    t_all = timed(lambda: hga.prefill(p, Q, K, V, n, cs, gs, O, ws, chunk_idx=ci, group_idx=gi), reps)
+    t_sum = timed(lambda: hga.build_summaries(p, K, n, 0, nC, cs, gs), reps)
+    t_route = timed(lambda: hga.route(p, Q, n, qpos, cs, gs, n, ci, gi, wsr), reps)
+    t_att = timed(lambda: hga.attend(p, Q, n, qpos, K, V, n, gi, O, wsa), reps)
+    fl_att = prefill_flops(s)
+    fl_route = routing_flops(s)
+    tf_att = fl_att / (t_att * 1e-6) / 1e12
+    tf_route = fl_route / (t_route * 1e-6) / 1e12
+    summ_bytes = B * H * n * d * 2 + B * H * (nC + n // G) * d * 4
+    log(f"[bench] prefill {t_all:.1f} us: summaries {t_sum:.1f}, route {t_route:.1f}, attend {t_att:.1f} us "
+        f"({tf_att:.1f} TFLOP/s = {tf_att / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 peak)")
+    return {"workload": "prefill_32k", "ms_per_call": round(t_all / 1e3, 4),
+            "query_tokens_per_s": round(B * n / (t_all * 1e-6), 1),
+            "roofline": {"kernel": "attend_prefill_mfma_kernel<128,8>", "bound": "mfma",
+                         "achieved": round(tf_att, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_att / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "flops_per_launch": fl_att, "avg_us": round(t_att, 2)},
+            "route": {"kernel": "route_prefill_mfma_kernel<128,8>", "avg_us": round(t_route, 2),
+                      "flops_per_launch": fl_route, "achieved_tflops": round(tf_route, 1),
+                      "frac": round(tf_route / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "summaries": {"kernel": "summaries_kernel<bf16,128>", "avg_us": round(t_sum, 2),
+                          "bytes_per_launch": summ_bytes,
+                          "achieved_gbs": round(summ_bytes / (t_sum * 1e-6) / 1e9, 1)}}
 
 
 def cpu_baseline(s, w):
