@@ -173,6 +173,46 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base
   return a;
 }
 
+// Decode step in three launches: F forced-window workgroups and one routing
+// workgroup per (b, kv head); R split-K workgroups per (b, kv head) over the
+// routed rows; the merge of the F + R partials.
+#ifndef HGA_DECODE_FORCED_WGS
+#define HGA_DECODE_FORCED_WGS 2
+#endif
+#ifndef HGA_DECODE_ROUTED_WGS
+#define HGA_DECODE_ROUTED_WGS 8
+#endif
+
+struct FusedPlan {
+  bool use;
+  int forced_wgs, forced_bpw, routed_wgs, routed_bpw, units_per_xcd;
+  size_t partials_off, bytes;
+};
+
+FusedPlan plan_fused(const KParams& kp, size_t base) {
+  FusedPlan r{};
+  r.use = decode_fused_supported(kp);
+  if (!r.use) return r;
+  const int fblocks = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kAttBlockRows));
+  const int rblocks = static_cast<int>(std::max<int64_t>(1, cdiv(static_cast<int64_t>(kp.top_g) * kp.G, kAttBlockRows)));
+  r.forced_wgs = std::min(HGA_DECODE_FORCED_WGS, fblocks);
+  r.forced_bpw = static_cast<int>(cdiv(fblocks, r.forced_wgs));
+  r.routed_bpw = static_cast<int>(cdiv(rblocks, std::min(HGA_DECODE_ROUTED_WGS, rblocks)));
+  r.routed_wgs = static_cast<int>(cdiv(rblocks, r.routed_bpw));
+  if (r.forced_wgs + r.routed_wgs > kDecMaxParts) {  // the merge holds at most kDecMaxParts parts
+    r.use = false;
+    return r;
+  }
+  const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
+  r.units_per_xcd = static_cast<int>(cdiv(units, kXcds));
+  size_t off = base;
+  r.partials_off = off;
+  off = align256(off + static_cast<size_t>(units) * (r.forced_wgs + r.routed_wgs) * kp.gq * (kp.d + 2) *
+                           sizeof(float));
+  r.bytes = off - base;
+  return r;
+}
+
 struct IdxPlan {
   size_t ci_off, gi_off, bytes;
 };
@@ -192,6 +232,7 @@ IdxPlan plan_idx(const KParams& kp, int n_units, size_t base) {
 struct FullPlan {
   RoutePlan route;
   AttendPlan attend;
+  FusedPlan fused;
   IdxPlan idx;
   size_t bytes;
 };
@@ -212,6 +253,10 @@ FullPlan plan(const KParams& kp, int op, int64_t nq) {
   if (needs_attend) {
     f.attend = plan_attend(kp, nq, op == HGA_OP_DECODE_OFFLOAD, off);
     off += f.attend.bytes;
+  }
+  if (op == HGA_OP_DECODE) {
+    f.fused = plan_fused(kp, off);
+    off += f.fused.bytes;
   }
   if (needs_idx) {
     f.idx = plan_idx(kp, f.route.n_units, off);
@@ -480,6 +525,41 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
   const bool bf = p->qkv_dtype == HGA_BF16;
   int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
   int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
+  if (f.fused.use) {
+    const FusedPlan& fp = f.fused;
+    DecodeArgs da{};
+    da.kp = kp;
+    da.Q = Q;
+    da.seq_len = seq_len;
+    da.K = K;
+    da.V = V;
+    da.chunk_sum = chunk_sum;
+    da.group_sum = group_sum;
+    da.chunk_sum_w = chunk_sum;
+    da.group_sum_w = group_sum;
+    da.build_summary = 1;
+    da.chunk_idx = ci;
+    da.group_idx = gi;
+    da.O = O;
+    da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
+    da.forced_wgs = fp.forced_wgs;
+    da.forced_bpw = fp.forced_bpw;
+    da.parts_total = fp.forced_wgs + fp.routed_wgs;
+    da.units_per_xcd = fp.units_per_xcd;
+    da.partials = at<float>(ws, fp.partials_off);
+    HGA_TRY_HIP(launch_decode_route(da, bf, st), "decode route");
+    AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K, V, gi, 1, O, nullptr, p->out_dtype == HGA_BF16);
+    aa.part = 2;
+    aa.splits = fp.routed_wgs;
+    aa.tiles_per_split = fp.routed_bpw;
+    aa.part_offset = fp.forced_wgs;
+    aa.parts_total = da.parts_total;
+    aa.partials = da.partials;
+    aa.store_only = 1;
+    HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "decode attend");
+    HGA_TRY_HIP(launch_decode_merge(da, da.parts_total, st), "decode merge");
+    return ok();
+  }
   RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);
   ra.build_summary = 1;
   ra.ksrc.base = K;

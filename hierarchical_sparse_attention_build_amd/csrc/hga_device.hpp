@@ -10,6 +10,9 @@ namespace hga {
 
 constexpr int kWave = 64;
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave); }
+
 // ---------------------------------------------------------------- bf16 / f32
 struct bf16 {
   uint16_t bits;
@@ -89,6 +92,27 @@ __device__ __forceinline__ float movf(float v) {
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ int movi(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+// value of lane n of this lane's row of 16 (DPP row_share, n a constant)
+__device__ __forceinline__ float row_share(float v, int n) {
+  switch (n & 15) {
+    case 0: return movf<0x150>(v);
+    case 1: return movf<0x151>(v);
+    case 2: return movf<0x152>(v);
+    case 3: return movf<0x153>(v);
+    case 4: return movf<0x154>(v);
+    case 5: return movf<0x155>(v);
+    case 6: return movf<0x156>(v);
+    case 7: return movf<0x157>(v);
+    case 8: return movf<0x158>(v);
+    case 9: return movf<0x159>(v);
+    case 10: return movf<0x15A>(v);
+    case 11: return movf<0x15B>(v);
+    case 12: return movf<0x15C>(v);
+    case 13: return movf<0x15D>(v);
+    case 14: return movf<0x15E>(v);
+    default: return movf<0x15F>(v);
+  }
 }
 // value of the same lane in the paired row: xor 16 and xor 32 (results identical
 // in both rows of a pair, so "a + other" is the pair's reduction)

@@ -72,6 +72,31 @@ struct AttendArgs {
   int32_t parts_total;    // partial slots per (bh, row) over all launches
   float* partials;        // ws
   uint32_t* counters;     // ws [B*Hkv*nq]
+  int32_t store_only;     // 1: store the partial and leave the merge to a later launch
+};
+
+// A decode step (nq = 1) in two launches: routing, forced-window attention and
+// the summary update; then the routed rows' attention and the merge.
+struct DecodeArgs {
+  KParams kp;
+  const void* Q;             // [B, Hq, 1, d]
+  const int32_t* seq_len;    // [B]: the query sits at position seq_len[b] - 1
+  const void* K;             // [B, Hkv, n_cap, d]
+  const void* V;
+  const float* chunk_sum;    // [B, Hkv, n_chunks_cap, d]
+  const float* group_sum;    // [B, Hkv, n_chunks_cap * m, d]
+  float* chunk_sum_w;        // the same tables, written for the chunk the query completes
+  float* group_sum_w;
+  int32_t build_summary;
+  int32_t* chunk_idx;        // [B*Hkv, top_k]
+  int32_t* group_idx;        // [B*Hkv, top_g]
+  void* O;                   // [B, Hq, 1, d] (written here only for a position outside the cache)
+  int32_t out_bf16;
+  int32_t forced_wgs;        // forced-window workgroups per (b, kv head): partial slots 0 .. F-1
+  int32_t forced_bpw;        // 16-row blocks of forced rows per forced workgroup
+  int32_t parts_total;       // partial slots per (b, kv head): forced, then routed
+  int32_t units_per_xcd;     // ceil(B*Hkv / kXcds)
+  float* partials;           // ws [B*Hkv, parts_total, gq * (d + 2)]
 };
 
 struct GatherArgs {
@@ -88,6 +113,14 @@ hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st
 hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipStream_t st);
 hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
+// Decode routing launch (Hq/Hkv <= 4, d in {64, 128}, candidate and index limits).
+constexpr int kXcds = 8;             // accelerator dies; workgroups are dealt to them in turn
+constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per unit
+constexpr int kDecMaxParts = 16;     // partial results merged per (b, kv head)
+bool decode_fused_supported(const KParams& kp);
+hipError_t launch_decode_route(const DecodeArgs& a, bool bf16_in, hipStream_t st);
+// Merge of the parts_total partials of every (b, kv head) of a decode step into O.
+hipError_t launch_decode_merge(const DecodeArgs& a, int parts_total, hipStream_t st);
 // Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
 bool prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_attend_prefill_mfma(const AttendArgs& a, hipStream_t st);

@@ -1,0 +1,208 @@
+// Exact top-k selection by a bitwise search on ordered keys, done by whole
+// waves with ballots, without a barrier inside the search.
+//
+// Order of candidates: score descending, then position ascending (lower
+// position wins a tie); NaN ranks with -inf.  The selected positions come out
+// in ascending order, which is the order of the index lists the method hands
+// from one routing level to the next and to the attention step
+// [HGA technical summary (it), Meccanismo Core, item 2].
+//
+// A wave holds up to kSelMaxE keys per lane.  The k-th largest key T is found
+// bit by bit from the top: a candidate prefix is kept when at least k keys are
+// >= it (each count is a ballot and a population count per key slot, so the
+// search runs on the scalar unit once the compares are done).  The
+// selection is every key > T plus the lowest positions among the keys == T.
+// A workgroup first lets each wave select the best min(k, its share) of a
+// contiguous share of the list (a member of the overall top-k is in the
+// top-k of its share), then one wave selects among those.
+#pragma once
+
+#include "hga_device.hpp"
+
+namespace hga {
+
+constexpr int kSelMaxE = 16;   // keys per lane in one wave search
+constexpr int kSelMaxK = 256;  // largest k of the workgroup selection
+
+// number of set bits of m at lanes below this one
+__device__ __forceinline__ int bits_below(uint64_t m) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// Valid keys are order_key() values (always >= 0x007fffff); an empty slot holds 0.
+// Returns the largest T with #{keys >= T} >= k, for 1 <= k <= number of valid keys
+// (the k-th largest key, or a value with exactly k keys at or above it).
+template <int E>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[E], int k) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint64_t b[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) b[e] = ballot64(key[e] >= cand);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __popcll(b[e]);
+    // keep the search state in scalar registers
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c >= k) {
+      T = __builtin_amdgcn_readfirstlane(cand);
+      if (c == k) break;
+    }
+  }
+  return T;
+}
+
+// Emit the k selected slots (keys > T, then the first keys == T in slot order)
+// as out(rank, e) in ascending slot order, slot order being (e, lane).
+template <int E, typename OutFn>
+__device__ __forceinline__ void wave_emit(const uint32_t (&key)[E], int k, uint32_t T, OutFn out) {
+  int n_gt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) n_gt += __popcll(ballot64(key[e] > T));
+  int need = k - n_gt;
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool is_eq = key[e] == T;
+    const uint64_t eq = ballot64(is_eq);
+    const bool take = key[e] > T || (is_eq && bits_below(eq) < need);
+    const uint64_t tm = ballot64(take);
+    if (take) out(base + bits_below(tm), e);
+    base += __popcll(tm);
+    const int neq = __popcll(eq);
+    need -= need < neq ? need : neq;
+  }
+}
+
+// Emit every valid slot (key != 0) in slot order.
+template <int E, typename OutFn>
+__device__ __forceinline__ void wave_emit_all(const uint32_t (&key)[E], OutFn out) {
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool take = key[e] != 0u;
+    const uint64_t tm = ballot64(take);
+    if (take) out(base + bits_below(tm), e);
+    base += __popcll(tm);
+  }
+}
+
+// One wave: keys key_of(e) for slots (e, lane), e < E; emit the best k
+// (every valid key when all is set) through out(rank, e).
+template <int E, typename KeyFn, typename OutFn>
+__device__ __forceinline__ void wave_topk(KeyFn key_of, int k, bool all, OutFn out) {
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = key_of(e);
+  if (all) {
+    wave_emit_all(key, out);
+  } else if (k > 0) {
+    const uint32_t T = wave_kth_key(key, k);
+    wave_emit(key, k, T, out);
+  }
+}
+
+// wave_topk with the slot count rounded up to 1, 2, 4, 8 or 16 (at most kSelMaxE).
+template <typename KeyFn, typename OutFn>
+__device__ __forceinline__ void wave_topk_n(int slots, KeyFn key_of, int k, bool all, OutFn out) {
+  if (slots <= 0) return;
+  if (slots <= 1) wave_topk<1>(key_of, k, all, out);
+  else if (slots <= 2) wave_topk<2>(key_of, k, all, out);
+  else if (slots <= 4) wave_topk<4>(key_of, k, all, out);
+  else if (slots <= 8) wave_topk<8>(key_of, k, all, out);
+  else wave_topk<kSelMaxE>(key_of, k, all, out);
+}
+
+template <int NT>
+struct SelSmem {
+  static constexpr int NW = NT / kWave;
+  uint32_t key[NW * kSelMaxK];
+  int pos[NW * kSelMaxK];
+  int cnt[NW];
+};
+
+// True when block_select handles (n, k) for a workgroup of NT threads.
+template <int NT>
+__host__ __device__ constexpr bool block_select_fits(int n, int k) {
+  return k <= kSelMaxK && n <= NT * kSelMaxE && (NT / kWave) * k <= kWave * kSelMaxE;
+}
+
+// Exact selection of the min(n, k) best of sc(0..n) (sc reads LDS or memory);
+// the chosen positions go to sel[] (LDS) in ascending order.  Every thread of
+// the workgroup calls it; returns min(n, k) and ends with a barrier.
+// Requires block_select_fits<NT>(n, k).
+template <int NT, typename ScoreFn>
+__device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = wave_id();
+  if (n <= k) {
+    for (int i = tid; i < n; i += NT) sel[i] = i;
+    __syncthreads();
+    return n;
+  }
+  // key of position i (0 outside [0, hi)); the read index is clamped, so every
+  // lane reads and no lane branches
+  auto key_at = [&](int i, int hi) -> uint32_t {
+    const uint32_t kk = order_key(sc(min(i, hi - 1)));
+    return i < hi ? kk : 0u;
+  };
+  if (n <= 2 * kWave) {
+    // one wave, at most two keys per lane
+    if (wid == 0)
+      wave_topk_n((n + kWave - 1) / kWave, [&](int e) { return key_at(e * kWave + lane, n); }, k, false,
+                  [&](int r, int e) { sel[r] = e * kWave + lane; });
+    __syncthreads();
+    return k;
+  }
+
+  // phase 1: wave w selects among positions [w*q, min(n, (w+1)*q))
+  const int q = (n + NW - 1) / NW;
+  const int lo = wid * q;
+  const int hi = min(n, lo + q);
+  const int nw = max(0, hi - lo);
+  const int kw = min(k, nw);
+  wave_topk_n((nw + kWave - 1) / kWave, [&](int e) { return key_at(lo + e * kWave + lane, hi); }, kw, kw == nw,
+              [&](int r, int e) {
+                const int i = lo + e * kWave + lane;
+                sm.key[wid * k + r] = order_key(sc(i));
+                sm.pos[wid * k + r] = i;
+              });
+  if (lane == 0) sm.cnt[wid] = kw;
+  __syncthreads();
+
+  // phase 2: wave 0 selects k among the concatenated winners (ascending positions)
+  if (wid == 0) {
+    int n2 = 0;
+    int start[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      start[w] = n2;
+      n2 += sm.cnt[w];
+    }
+    // LDS offset of the jj-th winner
+    auto off_of = [&](int jj) {
+      int o = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (jj >= start[w]) o = w * k + (jj - start[w]);
+      return o;
+    };
+    wave_topk_n((n2 + kWave - 1) / kWave,
+                [&](int e) {
+                  const int jj = e * kWave + lane;
+                  const uint32_t kk = sm.key[off_of(min(jj, n2 - 1))];
+                  return jj < n2 ? kk : 0u;
+                },
+                k, n2 <= k, [&](int r, int e) { sel[r] = sm.pos[off_of(e * kWave + lane)]; });
+  }
+  __syncthreads();
+  return k;
+}
+
+}  // namespace hga
