@@ -6,14 +6,15 @@ A step is one decode step of the 32K-context workload (B=8, 32 query / 8 KV
 heads, d=128, C=64, G=16, sink 1, local 4, top-k 16, top-g 32, bf16): the
 library's hga_decode, which routes (summary scan + chunk top-k + group
 scoring + group top-g, and the summary update of the chunk the query
-completes) and attends over the gathered K/V.  Inputs are resident in HBM.
+completes) and attends over the gathered K/V, in two kernel launches.  Inputs are resident in HBM.
 Consecutive steps rotate over independent copies of the cache (as consecutive
 layers of a model would), so no step finds its working set in the 256 MB
 Infinity Cache; a warm-cache figure is reported separately.
 
 Printed: one JSON line with the throughput (query tokens/s), the roofline of
-the attention kernel (HIP events on the launch stream), the CPU oracle timed
-on a bounded sample, and the 32K prefill figures.
+the decode step (its two kernel launches, timed with HIP events on the launch
+stream), the CPU oracle timed on a bounded sample, and the 32K prefill
+figures.
 """
 from __future__ import annotations
 
@@ -67,13 +68,16 @@ def measured_traffic(kernel):
     return None
 
 
-def decode_bytes(s):
-    """Algorithmic HBM bytes of one decode step, split by kernel.
+def decode_bytes(s, forced_wgs=2):
+    """Algorithmic HBM bytes of one decode step, split by its two launches.
 
-    attention: gathered K and V rows of the visible set, Q in, O out (fp32),
-               group ids;
-    routing:   candidate chunk summaries, the group summaries of the routed
-               chunks, Q; plus the summary update of the completed chunk.
+    routing launch: the candidate chunk summaries, the group summaries of the
+        routed chunks, Q, the forced (sink + local + current) K and V rows, the
+        index lists, the forced partial results written, and the summary update
+        of the chunk the query completes (its C key rows read, 1 + m summaries
+        written);
+    attention launch: the routed K and V rows, Q, the group ids, the forced
+        partial results read back and O (fp32) written.
     """
     C, G, d = s.chunk_size, s.group_size, s.head_dim
     L = s.n_tokens
@@ -86,13 +90,15 @@ def decode_bytes(s):
     gq = s.n_q_heads // s.n_kv_heads
     units = s.batch * s.n_kv_heads
     e = 2 if s.dtype == "bf16" else 4
-    tokens = n_forced * C + n_groups * G
-    att = units * (tokens * d * e * 2 + gq * d * e + gq * d * 4 + s.top_g * 4)
-    route = units * ((n_cand + n_routed_chunks * m) * d * 4 + gq * d * e
-                     + (s.top_k + s.top_g) * 4)
-    if L % C == 0:  # summary update of the completed chunk: read C rows, write 1 + m summaries
+    forced_tok = n_forced * C
+    routed_tok = n_groups * G
+    partials = forced_wgs * gq * (d + 2) * 4
+    route = units * ((n_cand + n_routed_chunks * m) * d * 4 + gq * d * e + forced_tok * d * e * 2
+                     + (s.top_k + s.top_g) * 4 + partials)
+    if L % C == 0:
         route += units * (C * d * e + (1 + m) * d * 4)
-    return att, route, tokens
+    att = units * (routed_tok * d * e * 2 + gq * d * e + s.top_g * 4 + partials + gq * d * 4)
+    return route, att, forced_tok + routed_tok
 
 
 def main():
@@ -154,11 +160,8 @@ def main():
                          O=torch.empty((B, Hq, 1, d), device=dev),
                          gi=torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device=dev),
                          ci=torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device=dev),
-                         ws=hga.workspace(p, hga.OP_DECODE, 1, L, device=dev),
-                         wsr=hga.workspace(p, hga.OP_ROUTE, 1, L, device=dev),
-                         wsa=hga.workspace(p, hga.OP_ATTEND, 1, L, device=dev)))
+                         ws=hga.workspace(p, hga.OP_DECODE, 1, L, device=dev)))
     seq = torch.from_numpy(w.seq_len.astype(np.int32)).to(dev)
-    qpos = seq - 1
     torch.cuda.synchronize()
     log(f"[bench] {R} cache replicas resident; warmup {args.warmup}, steps {args.steps}")
 
@@ -166,14 +169,6 @@ def main():
         r = reps[i % R]
         hga.decode(p, r["Q"], r["K"], r["V"], L, seq, r["cs"], r["gs"], r["O"], r["ws"],
                    chunk_idx=r["ci"], group_idx=r["gi"])
-
-    def route_only(i):
-        r = reps[i % R]
-        hga.route(p, r["Q"], 1, qpos, r["cs"], r["gs"], L, r["ci"], r["gi"], r["wsr"])
-
-    def attend_only(i):
-        r = reps[i % R]
-        hga.attend(p, r["Q"], 1, qpos, r["K"], r["V"], L, r["gi"], r["O"], r["wsa"])
 
     # The timed work is replayed from HIP graphs: one graph holds one step per
     # cache replica, so the host issues one launch per R steps.
@@ -218,29 +213,20 @@ def main():
     torch.cuda.synchronize()
     warm_sec = (time.perf_counter() - t2) / steps
 
-    # per-kernel durations: HIP events on the launch stream around graph replays
-    # of back-to-back launches of one kernel (same launch configuration as in
-    # hga_decode), cycling over the cache replicas
-    def kernel_us(fn):
-        n = 4 * R
-        g = capture(fn, n)
-        g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps_ = max(1, args.steps // n)
-        st = torch.cuda.current_stream()
-        e0.record(st)
-        for _ in range(reps_):
-            g.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps_ * n)
-
-    route_us = kernel_us(route_only)
-    att_us = kernel_us(attend_only)
-    att_bytes, route_bytes, tokens = decode_bytes(s)
-    att_gbs = att_bytes / (att_us * 1e-6) / 1e9
-    route_gbs = route_bytes / (route_us * 1e-6) / 1e9
-    log(f"[bench] attend {att_us:.2f} us ({att_gbs:.0f} GB/s), route {route_us:.2f} us ({route_gbs:.0f} GB/s)")
+    # the roofline unit is the whole step (its two launches): HIP events on the
+    # launch stream around the same graph replays
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n_replay):
+        g_cold.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
+    route_bytes, att_bytes, tokens = decode_bytes(s)
+    step_bytes = route_bytes + att_bytes
+    step_gbs = step_bytes / (step_us * 1e-6) / 1e9
+    log(f"[bench] decode step (HIP events) {step_us:.2f} us: {step_bytes / 1e6:.2f} MB -> {step_gbs:.0f} GB/s")
 
     out = {
         "metric": METRIC,
@@ -259,15 +245,12 @@ def main():
                    "head_dim": d, "chunk": C, "group": G, "sink": s.n_sink, "local": s.n_local,
                    "top_k": s.top_k, "top_g": s.top_g, "rope_base": s.rope_base,
                    "tokens_attended": tokens, "cache_replicas": R},
-        "roofline": {"kernel": "attend_splitk_kernel<bf16,128,4>", "bound": "hbm",
-                     "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(att_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("attend_splitk_kernel<bf16,128,4>"),
-                     "bytes_per_launch": att_bytes, "avg_us": round(att_us, 3)},
-        "route": {"kernel": "route_scan_kernel<bf16,128>", "avg_us": round(route_us, 3),
-                  "bytes_per_launch": route_bytes, "achieved_gbs": round(route_gbs, 1),
-                  "frac": round(route_gbs / HBM_PEAK_GBS, 4)},
-        "step_hbm_frac": round((att_bytes + route_bytes) / sec_per_step / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "decode step = decode_route_kernel<bf16,128,4> + decode_attend_kernel<bf16,128,4,1>",
+                     "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_step"),
+                     "bytes_per_launch": step_bytes, "avg_us": round(step_us, 3),
+                     "bytes_by_launch": {"decode_route_kernel": route_bytes, "decode_attend_kernel": att_bytes}},
         "warm_cache": {"ms_per_step": round(warm_sec * 1e3, 6), "value": round(B / warm_sec, 1)},
     }
 

@@ -134,11 +134,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   }
   const int64_t row_id = static_cast<int64_t>(bh) * a.nq + qi;  // (b, kv head, query row)
   constexpr int stride = attn_part_stride<D, GQ>();
-  if (a.store_only) {
-    attn_store_partial<D, GQ, kAttWaves, kAttThreads>(
-        sm.mg, a.partials + (row_id * a.parts_total + a.part_offset + x) * stride);
-    return;
-  }
   attn_publish_and_merge<D, GQ, kAttWaves, kAttThreads>(sm.mg, a.partials + row_id * a.parts_total * stride,
                                                         a.part_offset + x, a.parts_total, &a.counters[row_id], out);
 }

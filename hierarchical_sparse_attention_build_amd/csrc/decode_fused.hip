@@ -1,8 +1,7 @@
 // The first launch of an HGA decode step: routing (steps 2-3) and attention
 // over the always-visible chunks (part of steps 4-5), plus the summary update
 // of the chunk the query completes (step 1).  The routed rows are attended by
-// the split-K attention launch that follows; a last small launch merges all
-// partial results into the output.
+// the second launch, which also merges in this launch's partial results.
 // [HGA technical summary (it), Meccanismo Core, items 1-4].
 //
 // Work of one (batch, KV head) unit, all on one XCD so that its summaries and
@@ -30,6 +29,10 @@ namespace hga {
 constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kForcedPF = 2;  // forced blocks in flight per wave
+constexpr int kRoutedPF = 4;  // routed blocks in flight per wave
+#ifndef HGA_DECODE_HEADS_PER_WG
+#define HGA_DECODE_HEADS_PER_WG 1  // query heads per routed-attention workgroup (of 4)
+#endif
 
 template <int GQ, int D>
 struct DecodeSmem {
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_route_kernel(DecodeArgs a)
   const bool routing = role == F;
   const int t = a.seq_len[b] - 1;
   constexpr int stride = attn_part_stride<D, GQ>();
-  float* parts = a.partials + static_cast<int64_t>(bh) * a.parts_total * stride;
+  float* parts = a.partials + static_cast<int64_t>(bh) * F * stride;
 
   __shared__ DecodeSmem<GQ, D> sm;
 
@@ -209,35 +212,87 @@ __global__ __launch_bounds__(kDecThreads) void decode_route_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Last launch: merge the partial softmax results of a unit (F forced-window
-// parts, then the routed parts of the split-K launch) into the output.
-template <int GQ, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int P) {
+// Second launch: workgroup (unit, hg) attends every routed group row of the
+// unit for query heads hg*HG .. hg*HG+HG-1 and merges the result with those
+// heads' forced-window partials from the first launch into the output.  The
+// GQ/HG workgroups of a unit read the same K/V rows, on the same XCD, so the
+// repeats are served by that XCD's L2.
+template <int GQ, int HG, int D>
+struct DecodeAttendSmem {
+  int gl[kSelMaxK];
+  AttnMergeSmem<HG, D, kDecWaves> mg;
+};
+
+template <typename T, int D, int GQ, int HG>
+__global__ __launch_bounds__(kDecThreads) void decode_attend_kernel(DecodeArgs a) {
+  constexpr int NHG = GQ / HG;
   const KParams& kp = a.kp;
-  const int bh = blockIdx.x;
+  const int F = a.forced_wgs;
+  // placement: the NHG workgroups of unit bh share blockIdx.x % 8 (one XCD)
+  const int x = blockIdx.x;
+  const int xcd = x % kXcds;
+  const int slot = x / kXcds;
+  const int hg = slot / a.units_per_xcd;
+  const int bh = (slot % a.units_per_xcd) * kXcds + xcd;
+  if (bh >= kp.B * kp.Hkv || hg >= NHG) return;
   const int b = bh / kp.Hkv;
   const int h = bh % kp.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = wave_id();
   const int t = a.seq_len[b] - 1;
   if (t < 0 || t >= kp.n_cap) return;  // NaN output written by the routing launch
+  const int head0 = h * GQ + hg * HG;   // first query head of this workgroup
+  const T* Qb = static_cast<const T*>(a.Q) + (static_cast<int64_t>(b) * kp.Hq + head0) * D;
+  const T* Kb = static_cast<const T*>(a.K) + static_cast<int64_t>(bh) * kp.n_cap * D;
+  const T* Vb = static_cast<const T*>(a.V) + static_cast<int64_t>(bh) * kp.n_cap * D;
   constexpr int stride = attn_part_stride<D, GQ>();
-  const float* parts = a.partials + static_cast<int64_t>(bh) * P * stride;
-  const AttnOut out{a.O, nullptr, a.out_bf16, static_cast<int64_t>(b) * kp.Hq + h * GQ, 1, 0};
-  for (int e = threadIdx.x; e < GQ * D; e += blockDim.x) {
-    const int hh = e / D;
-    // every part's (max, sum, value) loaded at once, then combined
+  const float* parts = a.partials + static_cast<int64_t>(bh) * F * stride;
+
+  __shared__ DecodeAttendSmem<GQ, HG, D> sm;
+  for (int i = tid; i < kp.top_g; i += kDecThreads) sm.gl[i] = a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i];
+  AttnLaneFor<T, D, HG> st;
+  st.init([&](int hh) { return Qb + static_cast<int64_t>(hh) * D; }, lane & 15);
+  __syncthreads();
+
+  const int nR = kp.top_g * kp.G;
+  const int nblk = (nR + kAttnBlock - 1) / kAttnBlock;
+  // masked slots point at the query's own row
+  auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
+    const int e = s >> kp.log2G;
+    const int g = s < nR ? sm.gl[e] : -1;
+    const int64_t tok = (static_cast<int64_t>(g) << kp.log2G) + (s & (kp.G - 1));
+    const bool ok = g >= 0 && tok <= t;
+    kr = Kb + (ok ? tok : t) * D;
+    vr = Vb + (ok ? tok : t) * D;
+    return ok;
+  };
+  st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
+  attn_merge_waves(st, sm.mg);
+
+  const AttnOut out{a.O, nullptr, a.out_bf16, static_cast<int64_t>(b) * kp.Hq + head0, 1, 0};
+  constexpr int kOut = (HG * D + kDecThreads - 1) / kDecThreads;
+#pragma unroll
+  for (int r = 0; r < kOut; ++r) {
+    const int e = tid + r * kDecThreads;
+    if (e >= HG * D) continue;
+    const int hh = e / D;               // head within this workgroup
+    const int gh = hg * HG + hh;        // head within the unit (forced partial layout)
     float mp[kDecMaxParts], lp[kDecMaxParts], op[kDecMaxParts];
 #pragma unroll
     for (int p = 0; p < kDecMaxParts; ++p) {
-      const bool in = p < P;
+      const bool in = p < F;
       const float* q = parts + (in ? p : 0) * stride;
-      mp[p] = in ? q[GQ * D + hh] : -__builtin_huge_valf();
-      lp[p] = q[GQ * D + GQ + hh];
-      op[p] = q[e];
+      mp[p] = in ? q[GQ * D + gh] : -__builtin_huge_valf();
+      lp[p] = q[GQ * D + GQ + gh];
+      op[p] = q[gh * D + e % D];
     }
-    float M = -__builtin_huge_valf();
+    float M = sm.mg.M[hh];
 #pragma unroll
     for (int p = 0; p < kDecMaxParts; ++p) M = fmaxf(M, mp[p]);
-    float num = 0.f, den = 0.f;
+    const float wo = sm.mg.M[hh] == -__builtin_huge_valf() ? 0.f : exp2f(sm.mg.M[hh] - M);
+    float num = attn_wg_value<D, HG, kDecWaves>(sm.mg, e) * wo;
+    float den = sm.mg.L[hh] * wo;
 #pragma unroll
     for (int p = 0; p < kDecMaxParts; ++p) {
       const float w = mp[p] == -__builtin_huge_valf() ? 0.f : exp2f(mp[p] - M);
@@ -279,20 +334,26 @@ hipError_t launch_decode_route(const DecodeArgs& a, bool bf16_in, hipStream_t st
   return a.kp.d == 64 ? launch_gq<float, 64>(a, st) : launch_gq<float, 128>(a, st);
 }
 
-template <int D, int GQ>
-static hipError_t launch_merge_t(const DecodeArgs& a, int P, hipStream_t st) {
-  decode_merge_kernel<GQ, D><<<static_cast<unsigned>(a.kp.B * a.kp.Hkv), 256, 0, st>>>(a, P);
+template <typename T, int D, int GQ, int HG>
+static hipError_t launch_att_t(const DecodeArgs& a, hipStream_t st) {
+  const unsigned n_wg = static_cast<unsigned>(kXcds) * a.units_per_xcd * (GQ / HG);
+  decode_attend_kernel<T, D, GQ, HG><<<n_wg, kDecThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_merge(const DecodeArgs& a, int P, hipStream_t st) {
-  const bool d64 = a.kp.d == 64;
+template <typename T, int D>
+static hipError_t launch_att_gq(const DecodeArgs& a, hipStream_t st) {
   switch (a.kp.gq) {
-    case 1: return d64 ? launch_merge_t<64, 1>(a, P, st) : launch_merge_t<128, 1>(a, P, st);
-    case 2: return d64 ? launch_merge_t<64, 2>(a, P, st) : launch_merge_t<128, 2>(a, P, st);
-    case 4: return d64 ? launch_merge_t<64, 4>(a, P, st) : launch_merge_t<128, 4>(a, P, st);
+    case 1: return launch_att_t<T, D, 1, 1>(a, st);
+    case 2: return launch_att_t<T, D, 2, 1>(a, st);
+    case 4: return launch_att_t<T, D, 4, HGA_DECODE_HEADS_PER_WG>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_attend(const DecodeArgs& a, bool bf16_in, hipStream_t st) {
+  if (bf16_in) return a.kp.d == 64 ? launch_att_gq<bf16, 64>(a, st) : launch_att_gq<bf16, 128>(a, st);
+  return a.kp.d == 64 ? launch_att_gq<float, 64>(a, st) : launch_att_gq<float, 128>(a, st);
 }
 
 }  // namespace hga

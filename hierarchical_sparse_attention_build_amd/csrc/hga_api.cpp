@@ -173,19 +173,16 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base
   return a;
 }
 
-// Decode step in three launches: F forced-window workgroups and one routing
-// workgroup per (b, kv head); R split-K workgroups per (b, kv head) over the
-// routed rows; the merge of the F + R partials.
+// Decode step in two launches: F forced-window workgroups and one routing
+// workgroup per (b, kv head); then one workgroup per (b, query head) for the
+// routed rows and the merge.
 #ifndef HGA_DECODE_FORCED_WGS
 #define HGA_DECODE_FORCED_WGS 2
-#endif
-#ifndef HGA_DECODE_ROUTED_WGS
-#define HGA_DECODE_ROUTED_WGS 8
 #endif
 
 struct FusedPlan {
   bool use;
-  int forced_wgs, forced_bpw, routed_wgs, routed_bpw, units_per_xcd;
+  int forced_wgs, forced_bpw, units_per_xcd;
   size_t partials_off, bytes;
 };
 
@@ -194,21 +191,13 @@ FusedPlan plan_fused(const KParams& kp, size_t base) {
   r.use = decode_fused_supported(kp);
   if (!r.use) return r;
   const int fblocks = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kAttBlockRows));
-  const int rblocks = static_cast<int>(std::max<int64_t>(1, cdiv(static_cast<int64_t>(kp.top_g) * kp.G, kAttBlockRows)));
-  r.forced_wgs = std::min(HGA_DECODE_FORCED_WGS, fblocks);
+  r.forced_wgs = std::min(std::min(HGA_DECODE_FORCED_WGS, fblocks), kDecMaxParts);
   r.forced_bpw = static_cast<int>(cdiv(fblocks, r.forced_wgs));
-  r.routed_bpw = static_cast<int>(cdiv(rblocks, std::min(HGA_DECODE_ROUTED_WGS, rblocks)));
-  r.routed_wgs = static_cast<int>(cdiv(rblocks, r.routed_bpw));
-  if (r.forced_wgs + r.routed_wgs > kDecMaxParts) {  // the merge holds at most kDecMaxParts parts
-    r.use = false;
-    return r;
-  }
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   r.units_per_xcd = static_cast<int>(cdiv(units, kXcds));
   size_t off = base;
   r.partials_off = off;
-  off = align256(off + static_cast<size_t>(units) * (r.forced_wgs + r.routed_wgs) * kp.gq * (kp.d + 2) *
-                           sizeof(float));
+  off = align256(off + static_cast<size_t>(units) * r.forced_wgs * kp.gq * (kp.d + 2) * sizeof(float));
   r.bytes = off - base;
   return r;
 }
@@ -544,20 +533,10 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
     da.forced_wgs = fp.forced_wgs;
     da.forced_bpw = fp.forced_bpw;
-    da.parts_total = fp.forced_wgs + fp.routed_wgs;
     da.units_per_xcd = fp.units_per_xcd;
     da.partials = at<float>(ws, fp.partials_off);
     HGA_TRY_HIP(launch_decode_route(da, bf, st), "decode route");
-    AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K, V, gi, 1, O, nullptr, p->out_dtype == HGA_BF16);
-    aa.part = 2;
-    aa.splits = fp.routed_wgs;
-    aa.tiles_per_split = fp.routed_bpw;
-    aa.part_offset = fp.forced_wgs;
-    aa.parts_total = da.parts_total;
-    aa.partials = da.partials;
-    aa.store_only = 1;
-    HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "decode attend");
-    HGA_TRY_HIP(launch_decode_merge(da, da.parts_total, st), "decode merge");
+    HGA_TRY_HIP(launch_decode_attend(da, bf, st), "decode attend");
     return ok();
   }
   RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);

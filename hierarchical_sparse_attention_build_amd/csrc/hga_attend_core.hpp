@@ -468,16 +468,6 @@ __device__ __forceinline__ void attn_write_final(const AttnMergeSmem<GQ, D, NWV>
   if (static_cast<int>(threadIdx.x) < GQ) out.put_lse(threadIdx.x, sm.M[threadIdx.x], sm.L[threadIdx.x]);
 }
 
-// Store this workgroup's partial [o | m | l] with plain stores (read by a later launch).
-template <int D, int GQ, int NWV, int NT>
-__device__ __forceinline__ void attn_store_partial(const AttnMergeSmem<GQ, D, NWV>& sm, float* dst) {
-  for (int e = threadIdx.x; e < GQ * D; e += NT) dst[e] = attn_wg_value<D, GQ, NWV>(sm, e);
-  if (static_cast<int>(threadIdx.x) < GQ) {
-    dst[GQ * D + threadIdx.x] = sm.M[threadIdx.x];
-    dst[GQ * D + GQ + threadIdx.x] = sm.L[threadIdx.x];
-  }
-}
-
 // Partial layout per (row, part): [o (GQ*D) | m (GQ) | l (GQ)].
 template <int D, int GQ>
 __host__ __device__ constexpr int attn_part_stride() { return GQ * (D + 2); }

@@ -72,7 +72,6 @@ struct AttendArgs {
   int32_t parts_total;    // partial slots per (bh, row) over all launches
   float* partials;        // ws
   uint32_t* counters;     // ws [B*Hkv*nq]
-  int32_t store_only;     // 1: store the partial and leave the merge to a later launch
 };
 
 // A decode step (nq = 1) in two launches: routing, forced-window attention and
@@ -92,11 +91,10 @@ struct DecodeArgs {
   int32_t* group_idx;        // [B*Hkv, top_g]
   void* O;                   // [B, Hq, 1, d] (written here only for a position outside the cache)
   int32_t out_bf16;
-  int32_t forced_wgs;        // forced-window workgroups per (b, kv head): partial slots 0 .. F-1
+  int32_t forced_wgs;        // forced-window workgroups per (b, kv head)
   int32_t forced_bpw;        // 16-row blocks of forced rows per forced workgroup
-  int32_t parts_total;       // partial slots per (b, kv head): forced, then routed
   int32_t units_per_xcd;     // ceil(B*Hkv / kXcds)
-  float* partials;           // ws [B*Hkv, parts_total, gq * (d + 2)]
+  float* partials;           // ws [B*Hkv, forced_wgs, gq * (d + 2)]: forced-window partials
 };
 
 struct GatherArgs {
@@ -119,8 +117,7 @@ constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per
 constexpr int kDecMaxParts = 16;     // partial results merged per (b, kv head)
 bool decode_fused_supported(const KParams& kp);
 hipError_t launch_decode_route(const DecodeArgs& a, bool bf16_in, hipStream_t st);
-// Merge of the parts_total partials of every (b, kv head) of a decode step into O.
-hipError_t launch_decode_merge(const DecodeArgs& a, int parts_total, hipStream_t st);
+hipError_t launch_decode_attend(const DecodeArgs& a, bool bf16_in, hipStream_t st);
 // Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
 bool prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_attend_prefill_mfma(const AttendArgs& a, hipStream_t st);
