@@ -73,9 +73,11 @@ __device__ __forceinline__ void scan_scores(const float* qs, int n, float scale,
 #pragma unroll
       for (int v = 0; v < NV; ++v) cur[k][v] = r ? r[v * L + piece] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // rounds in load order, so that each is computed as soon as it arrives
+    // rounds in load order, so that each is computed as soon as it arrives;
+    // rounds past the last row are skipped (a wave-uniform branch)
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
+      if (base + k * RPR >= n) break;
       float mx = -__builtin_huge_valf();
 #pragma unroll
       for (int qh = 0; qh < GQ; ++qh) {

@@ -46,10 +46,8 @@ __device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[E], int k
     int c = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) c += __popcll(b[e]);
-    // keep the search state in scalar registers
-    c = __builtin_amdgcn_readfirstlane(c);
     if (c >= k) {
-      T = __builtin_amdgcn_readfirstlane(cand);
+      T = cand;
       if (c == k) break;
     }
   }
