@@ -1,6 +1,6 @@
 """Benchmark of the HGA routed-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--no-secondary]
 
 A step is one decode step of the 32K-context workload (B=8, 32 query / 8 KV
 heads, d=128, C=64, G=16, sink 1, local 4, top-k 16, top-g 32, bf16): the
@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the 64K decode and the 128K cold-tier decode figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy, a known-size reference for HBM counters")
     args = ap.parse_args()
@@ -254,8 +256,13 @@ def main():
         "warm_cache": {"ms_per_step": round(warm_sec * 1e3, 6), "value": round(B / warm_sec, 1)},
     }
 
+    del reps, g_cold, g_warm
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args, dev)
+    if not args.no_secondary:
+        out["decode_64k"] = bench_decode_64k(args, dev)
+        out["offload_decode_128k"] = bench_offload(args, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(s, w)
@@ -352,6 +359,137 @@ def bench_prefill(args, dev):
                           "achieved_gbs": round(summ_bytes / (t_sum * 1e-6) / 1e9, 1)}}
 
 
+def bench_decode_64k(args, dev):
+    """The 64K decode workload (B=16, 32/8 heads): hga_decode step time from HIP
+    events around graph replays over 4 cache replicas, and its HBM roofline."""
+    import torch
+    from hierarchical_sparse_attention_build_amd import hga
+    from hierarchical_sparse_attention_build_amd import workloads as W
+    s = W.spec("decode_64k")
+    log(f"[bench] generating {s.name} (seed {s.seed})")
+    w = W.make(s)
+    B, Hq, H, d, L, C, G = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens, s.chunk_size, s.group_size
+    p = hga.params(B, Hq, H, d, C, G, s.n_sink, s.n_local, s.top_k, s.top_g, s.rope_base,
+                   s.hf_threshold, qkv_dtype=hga.HGA_BF16, out_dtype=hga.HGA_F32)
+    Q = W.to_torch(w.Q, s.dtype).to(dev)
+    K0 = W.to_torch(w.K, s.dtype).to(dev)
+    V0 = W.to_torch(w.V, s.dtype).to(dev)
+    del w
+    nC, m, jq = L // C, C // G, (L - 1) // C
+    R = 4
+    reps = []
+    for r in range(R):
+        K = K0 if r == 0 else K0.clone()
+        V = V0 if r == 0 else V0.clone()
+        cs = torch.zeros((B, H, nC, d), device=dev)
+        gs = torch.zeros((B, H, nC * m, d), device=dev)
+        hga.build_summaries(p, K, L, 0, jq, cs, gs)
+        reps.append(dict(K=K, V=V, cs=cs, gs=gs, O=torch.empty((B, Hq, 1, d), device=dev),
+                         ws=hga.workspace(p, hga.OP_DECODE, 1, L, device=dev)))
+    seq = torch.full((B,), L, dtype=torch.int32, device=dev)
+
+    def step(i):
+        r = reps[i % R]
+        hga.decode(p, Q, r["K"], r["V"], L, seq, r["cs"], r["gs"], r["O"], r["ws"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(R):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            step(i)
+    for _ in range(4):
+        g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, args.steps // R)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n_rep):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / (n_rep * R)
+    route_bytes, att_bytes, tokens = decode_bytes(s)
+    gbs = (route_bytes + att_bytes) / (step_us * 1e-6) / 1e9
+    log(f"[bench] decode_64k step {step_us:.2f} us -> {B / (step_us * 1e-6):.0f} query tokens/s, {gbs:.0f} GB/s")
+    del reps, g
+    torch.cuda.empty_cache()
+    return {"workload": "decode_64k", "batch": B, "context": L, "top_k": s.top_k, "top_g": s.top_g,
+            "ms_per_step": round(step_us / 1e3, 6), "query_tokens_per_s": round(B / (step_us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": route_bytes + att_bytes}}
+
+
+def bench_offload(args, dev):
+    """The 128K cold-tier decode workload: K/V in pinned host memory, summaries and
+    the hot windows in HBM, the routed groups copied over PCIe on a side stream by
+    hga_decode_offload.  Timed with HIP events on the launch stream; the rate of
+    the routed-group copies is reported as PCIe GB/s (whole step, PCIe-inclusive)."""
+    import torch
+    from hierarchical_sparse_attention_build_amd import hga
+    from hierarchical_sparse_attention_build_amd import workloads as W
+    s = W.spec("offload_decode_128k")
+    log(f"[bench] generating {s.name} (seed {s.seed})")
+    w = W.make(s)
+    B, Hq, H, d, L, C, G = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens, s.chunk_size, s.group_size
+    p = hga.params(B, Hq, H, d, C, G, s.n_sink, s.n_local, s.top_k, s.top_g, s.rope_base,
+                   s.hf_threshold, qkv_dtype=hga.HGA_BF16, out_dtype=hga.HGA_F32)
+    K_host = W.to_torch(w.K, s.dtype, pin=True)
+    V_host = W.to_torch(w.V, s.dtype, pin=True)
+    Q = W.to_torch(w.Q, s.dtype).to(dev)
+    nC, m, j = L // C, C // G, (L - 1) // C
+    cs = torch.zeros((B, H, nC, d), device=dev)
+    gs = torch.zeros((B, H, nC * m, d), device=dev)
+    K_dev = K_host.to(dev)
+    hga.build_summaries(p, K_dev, L, 0, j, cs, gs)
+    hot = s.n_sink + s.n_local + 1
+    K_hot = torch.zeros((B, H, hot * C, d), dtype=K_dev.dtype, device=dev)
+    V_hot = torch.zeros_like(K_hot)
+    V_dev = V_host.to(dev)
+    for c in list(range(s.n_sink)) + list(range(j - s.n_local, j + 1)):
+        sl = hga.hot_slot(c, s.n_sink, s.n_local)
+        K_hot[:, :, sl * C:(sl + 1) * C] = K_dev[:, :, c * C:(c + 1) * C]
+        V_hot[:, :, sl * C:(sl + 1) * C] = V_dev[:, :, c * C:(c + 1) * C]
+    del K_dev, V_dev, w
+    torch.cuda.empty_cache()
+    seq = torch.full((B,), L, dtype=torch.int32, device=dev)
+    O = torch.empty((B, Hq, 1, d), device=dev)
+    copy_bytes = B * H * s.top_g * G * d * 2 * 2
+    staging = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    ws = hga.workspace(p, hga.OP_DECODE_OFFLOAD, 1, L, device=dev)
+    copy_stream = torch.cuda.Stream()
+
+    def step():
+        hga.decode_offload(p, Q, K_host, V_host, K_hot, V_hot, L, seq, cs, gs, O, staging, ws,
+                           copy_stream=copy_stream.cuda_stream)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 10)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / n
+    pcie = copy_bytes / (step_us * 1e-6) / 1e9
+    log(f"[bench] offload_decode_128k step {step_us:.1f} us -> {B / (step_us * 1e-6):.0f} query tokens/s, "
+        f"routed groups over PCIe at {pcie:.1f} GB/s (step-inclusive)")
+    return {"workload": "offload_decode_128k", "batch": B, "context": L, "top_k": s.top_k, "top_g": s.top_g,
+            "ms_per_step": round(step_us / 1e3, 6), "query_tokens_per_s": round(B / (step_us * 1e-6), 1),
+            "host_to_hbm_bytes_per_step": copy_bytes, "pcie_gbs_step_inclusive": round(pcie, 2),
+            "bound": "host link (PCIe Gen5 x16, about 64 GB/s)"}
+
+
 def cpu_baseline(s, w):
     """The oracle timed on this host's cores, one decode step of all sequences
     (routing over prebuilt oracle summaries + exact attention), repeated."""
@@ -361,7 +499,8 @@ def cpu_baseline(s, w):
     from hierarchical_sparse_attention_build_amd import workloads as W
     log("[bench] cpu baseline: preparing oracle tables")
     cfg = O.HGAConfig(**W.hga_config_kwargs(s))
-    with threadpool_limits(limits=1):
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
         Kf = W.to_f64(w.K, s.dtype)
         Vf = W.to_f64(w.V, s.dtype)
         Qf = W.to_f64(w.Q, s.dtype)
@@ -378,10 +517,10 @@ def cpu_baseline(s, w):
                 break
     rate = s.batch * reps / el
     log(f"[bench] cpu oracle: {reps} steps in {el:.1f} s -> {rate:.1f} query tokens/s")
-    return {"value": round(rate, 2), "unit": "query tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(rate, 2), "unit": "query tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full decode steps of decode_32k (all {s.batch} sequences, 64 units; "
                       "routing over prebuilt oracle summary tables + exact attention), numpy float64, "
-                      "BLAS limited to 1 thread"}
+                      f"BLAS threads = {cores} (the host cores available to the process)"}
 
 
 if __name__ == "__main__":
