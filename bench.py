@@ -69,15 +69,15 @@ def measured_traffic(kernel):
 
 
 def decode_bytes(s, forced_wgs=2):
-    """Algorithmic HBM bytes of one decode step, split by its two launches.
+    """Algorithmic HBM bytes of one decode step (one launch), by part.
 
-    routing launch: the candidate chunk summaries, the group summaries of the
-        routed chunks, Q, the forced (sink + local + current) K and V rows, the
-        index lists, the forced partial results written, and the summary update
-        of the chunk the query completes (its C key rows read, 1 + m summaries
-        written);
-    attention launch: the routed K and V rows, Q, the group ids, the forced
-        partial results read back and O (fp32) written.
+    routing: the candidate chunk summaries, the group summaries of the routed
+        chunks, Q and the index lists written;
+    attention: the forced (sink + local + current) and routed K and V rows, the
+        forced partial results written and read back once, and O (fp32) written;
+    summary: when the query completes its chunk, its C key rows read and 1 + m
+        summaries written.
+    Returns (bytes by part, total bytes, attended tokens per unit).
     """
     C, G, d = s.chunk_size, s.group_size, s.head_dim
     L = s.n_tokens
@@ -93,12 +93,12 @@ def decode_bytes(s, forced_wgs=2):
     forced_tok = n_forced * C
     routed_tok = n_groups * G
     partials = forced_wgs * gq * (d + 2) * 4
-    route = units * ((n_cand + n_routed_chunks * m) * d * 4 + gq * d * e + forced_tok * d * e * 2
-                     + (s.top_k + s.top_g) * 4 + partials)
-    if L % C == 0:
-        route += units * (C * d * e + (1 + m) * d * 4)
-    att = units * (routed_tok * d * e * 2 + gq * d * e + s.top_g * 4 + partials + gq * d * 4)
-    return route, att, forced_tok + routed_tok
+    parts = {
+        "routing": units * ((n_cand + n_routed_chunks * m) * d * 4 + gq * d * e + (s.top_k + s.top_g) * 4),
+        "attention": units * ((forced_tok + routed_tok) * d * e * 2 + 2 * partials + gq * d * 4),
+        "summary": units * (C * d * e + (1 + m) * d * 4) if L % C == 0 else 0,
+    }
+    return parts, sum(parts.values()), forced_tok + routed_tok
 
 
 def main():
@@ -215,8 +215,8 @@ def main():
     torch.cuda.synchronize()
     warm_sec = (time.perf_counter() - t2) / steps
 
-    # the roofline unit is the whole step (its two launches): HIP events on the
-    # launch stream around the same graph replays
+    # the roofline unit is the step's one launch: HIP events on the launch
+    # stream around the same graph replays
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
@@ -225,8 +225,7 @@ def main():
     e1.record(st)
     torch.cuda.synchronize()
     step_us = e0.elapsed_time(e1) * 1e3 / steps
-    route_bytes, att_bytes, tokens = decode_bytes(s)
-    step_bytes = route_bytes + att_bytes
+    parts, step_bytes, tokens = decode_bytes(s)
     step_gbs = step_bytes / (step_us * 1e-6) / 1e9
     log(f"[bench] decode step (HIP events) {step_us:.2f} us: {step_bytes / 1e6:.2f} MB -> {step_gbs:.0f} GB/s")
 
@@ -247,12 +246,12 @@ def main():
                    "head_dim": d, "chunk": C, "group": G, "sink": s.n_sink, "local": s.n_local,
                    "top_k": s.top_k, "top_g": s.top_g, "rope_base": s.rope_base,
                    "tokens_attended": tokens, "cache_replicas": R},
-        "roofline": {"kernel": "decode step = decode_route_kernel<bf16,128,4> + decode_attend_kernel<bf16,128,4,1>",
+        "roofline": {"kernel": "decode_step_kernel<bf16,128,4>",
                      "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode_step"),
                      "bytes_per_launch": step_bytes, "avg_us": round(step_us, 3),
-                     "bytes_by_launch": {"decode_route_kernel": route_bytes, "decode_attend_kernel": att_bytes}},
+                     "bytes_by_part": parts},
         "warm_cache": {"ms_per_step": round(warm_sec * 1e3, 6), "value": round(B / warm_sec, 1)},
     }
 
@@ -415,15 +414,15 @@ def bench_decode_64k(args, dev):
     e1.record(st)
     torch.cuda.synchronize()
     step_us = e0.elapsed_time(e1) * 1e3 / (n_rep * R)
-    route_bytes, att_bytes, tokens = decode_bytes(s)
-    gbs = (route_bytes + att_bytes) / (step_us * 1e-6) / 1e9
+    _, step_bytes, tokens = decode_bytes(s)
+    gbs = step_bytes / (step_us * 1e-6) / 1e9
     log(f"[bench] decode_64k step {step_us:.2f} us -> {B / (step_us * 1e-6):.0f} query tokens/s, {gbs:.0f} GB/s")
     del reps, g
     torch.cuda.empty_cache()
     return {"workload": "decode_64k", "batch": B, "context": L, "top_k": s.top_k, "top_g": s.top_g,
             "ms_per_step": round(step_us / 1e3, 6), "query_tokens_per_s": round(B / (step_us * 1e-6), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": route_bytes + att_bytes}}
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes}}
 
 
 def bench_offload(args, dev):

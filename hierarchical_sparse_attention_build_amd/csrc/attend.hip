@@ -26,6 +26,7 @@ template <int GQ, int D>
 struct AttSmem {
   int gl[1024];
   AttnMergeSmem<GQ, D, kAttWaves> mg;
+  alignas(16) unsigned char ktile[kAttWaves * attn_ktile_bytes<D>()];
 };
 
 template <typename T, int D, int GQ>
@@ -62,6 +63,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   AttnLaneFor<T, D, GQ> st;
   st.init([&](int hh) { return Qb + ((static_cast<int64_t>(b) * kp.Hq + h * GQ + hh) * a.nq + qi) * D; },
           lane & 15);
+  st.set_tile(sm.ktile);
   __syncthreads();
 
   const Forced fc = forced_chunks(j, kp.n_sink, kp.n_local);

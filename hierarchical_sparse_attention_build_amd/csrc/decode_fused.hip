@@ -1,19 +1,19 @@
-// The first launch of an HGA decode step: routing (steps 2-3) and attention
-// over the always-visible chunks (part of steps 4-5), plus the summary update
-// of the chunk the query completes (step 1).  The routed rows are attended by
-// the second launch, which also merges in this launch's partial results.
+// An HGA decode step in one launch: routing (steps 2-3), attention over the
+// union of the routed groups with the sink, local and current chunks (steps
+// 4-5), and the summary update of the chunk the query completes (step 1)
 // [HGA technical summary (it), Meccanismo Core, items 1-4].
 //
 // Work of one (batch, KV head) unit, all on one XCD so that its summaries and
 // K/V rows are shared through that XCD's L2:
 //   * One routing workgroup scores every candidate chunk summary (all rows in
-//     flight at once), selects the top-k chunks, scores their groups and
-//     selects the top-g groups, and writes the index lists.
+//     flight at once), selects the top-k chunks, scores their groups, selects
+//     the top-g groups, writes the index lists, and attends the unit's query
+//     heads over the routed groups' rows, which it already holds in LDS.
 //   * F forced workgroups attend shares of the sink, local and current chunks
-//     (known before routing) while the routing workgroup works and store their
-//     partial softmax (max, sum, output).  Forced workgroup 0 then summarises
-//     the chunk that the query completes.
-// No workgroup waits for another.
+//     (known before routing) while the routing workgroup works.  Forced
+//     workgroup 0 then summarises the chunk that the query completes.
+// The F + 1 partial softmax results (max, sum, output) are merged by the last
+// of them to finish; no workgroup waits for another.
 //
 // The score of a chunk or group is the max over the unit's query heads of
 // q . s / sqrt(d); selection is exact (score descending, index ascending).
@@ -29,10 +29,7 @@ namespace hga {
 constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kForcedPF = 2;  // forced blocks in flight per wave
-constexpr int kRoutedPF = 4;  // routed blocks in flight per wave
-#ifndef HGA_DECODE_HEADS_PER_WG
-#define HGA_DECODE_HEADS_PER_WG 1  // query heads per routed-attention workgroup (of 4)
-#endif
+constexpr int kRoutedPF = 2;  // routed blocks in flight per wave
 
 template <int GQ, int D>
 struct DecodeSmem {
@@ -40,157 +37,292 @@ struct DecodeSmem {
   float sc[kDecMaxScores];      // chunk scores, then group scores
   int selc[kSelMaxK];           // selected chunk positions (ascending)
   int selg[kSelMaxK];           // selected group positions (ascending)
+  int gl[kSelMaxK];             // routed group ids
+  int early;                    // the routing workgroup arrived early
   SelSmem<kDecThreads> sel;
   AttnMergeSmem<GQ, D, kDecWaves> mg;
+  alignas(16) unsigned char ktile[kDecWaves * attn_ktile_bytes<D>()];
 };
 
-// out[i] = max over the GQ query rows in qs of q . row(i) * scale, i in [0, n).
-// Eight lanes share one fp32 summary row (each holds D/8 values of it and of
-// every query row); a batch of 8 rounds x 64 rows is loaded at once and each
-// round is computed as soon as it arrives.
-template <int D, int GQ, typename RowFn>
-__device__ __forceinline__ void scan_scores(const float* qs, int n, float scale, RowFn row, float* out) {
-  constexpr int L = 8;                       // lanes per row
-  constexpr int NV = D / 32;                 // float4 pieces per lane per row
-  constexpr int RPR = kDecThreads / L;       // rows per round
-  constexpr int KR = 8;                      // rounds per batch
-  constexpr int BATCH = RPR * KR;
+// Scans: out[i] = max over the GQ query rows in qs of q . row(i) * scale, i in
+// [0, n).  Eight lanes share one fp32 summary row (each holds D/8 values of it
+// and of every query row); a batch of 8 rounds x 64 rows is loaded at once and
+// each round is computed as soon as it arrives.
+constexpr int kScanL = 8;                         // lanes per row
+constexpr int kScanKR = 8;                        // rounds per batch
+constexpr int kScanRPR = kDecThreads / kScanL;    // rows per round
+constexpr int kScanBatch = kScanRPR * kScanKR;
+
+template <int D>
+struct ScanBatch {
+  float4 v[kScanKR][D / 32];
+};
+
+// This lane's pieces of rows base + k * kScanRPR + (its row), those < n.
+template <int D, typename RowFn>
+__device__ __forceinline__ void scan_load(int base, int n, RowFn row, ScanBatch<D>& b) {
+  constexpr int NV = D / 32;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  const int piece = lane % L;
-  const int rw = wid * (kWave / L) + lane / L;
+  const int piece = lane % kScanL;
+  const int rw = wave_id() * (kWave / kScanL) + lane / kScanL;
+#pragma unroll
+  for (int k = 0; k < kScanKR; ++k) {
+    const int i = base + k * kScanRPR + rw;
+    const float4* r = i < n ? reinterpret_cast<const float4*>(row(i)) : nullptr;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) b.v[k][v] = r ? r[v * kScanL + piece] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// With FIRST, the batch at 0 was loaded beforehand (scan_load(0, n0, ...) with
+// n0 >= min(n, kScanBatch)) and is passed in `first`.
+template <int D, int GQ, bool FIRST = false, typename RowFn>
+__device__ __forceinline__ void scan_scores(const float* qs, int n, float scale, RowFn row, float* out,
+                                            const ScanBatch<D>& first = ScanBatch<D>{}) {
+  constexpr int NV = D / 32;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int piece = lane % kScanL;
+  const int rw = wave_id() * (kWave / kScanL) + lane / kScanL;
   float4 q[GQ][NV];
 #pragma unroll
   for (int qh = 0; qh < GQ; ++qh)
 #pragma unroll
     for (int v = 0; v < NV; ++v) q[qh][v] = *reinterpret_cast<const float4*>(qs + qh * D + v * 32 + piece * 4);
-  for (int base = 0; base < n; base += BATCH) {
-    float4 cur[KR][NV];
+  // rounds in load order, so that each is computed as soon as it arrives;
+  // rounds past the last row are skipped (a wave-uniform branch)
+  auto compute = [&](int base, const ScanBatch<D>& cur) {
 #pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      const int i = base + k * RPR + rw;
-      const float4* r = i < n ? reinterpret_cast<const float4*>(row(i)) : nullptr;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) cur[k][v] = r ? r[v * L + piece] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    // rounds in load order, so that each is computed as soon as it arrives;
-    // rounds past the last row are skipped (a wave-uniform branch)
-#pragma unroll
-    for (int k = 0; k < KR; ++k) {
-      if (base + k * RPR >= n) break;
+    for (int k = 0; k < kScanKR; ++k) {
+      if (base + k * kScanRPR >= n) break;
       float mx = -__builtin_huge_valf();
 #pragma unroll
       for (int qh = 0; qh < GQ; ++qh) {
         float acc = 0.f;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          acc = fmaf(q[qh][v].x, cur[k][v].x, acc);
-          acc = fmaf(q[qh][v].y, cur[k][v].y, acc);
-          acc = fmaf(q[qh][v].z, cur[k][v].z, acc);
-          acc = fmaf(q[qh][v].w, cur[k][v].w, acc);
+          acc = fmaf(q[qh][v].x, cur.v[k][v].x, acc);
+          acc = fmaf(q[qh][v].y, cur.v[k][v].y, acc);
+          acc = fmaf(q[qh][v].z, cur.v[k][v].z, acc);
+          acc = fmaf(q[qh][v].w, cur.v[k][v].w, acc);
         }
         mx = fmaxf(mx, sum8(acc));
       }
-      const int i = base + k * RPR + rw;
+      const int i = base + k * kScanRPR + rw;
       if (i < n && piece == 0) out[i] = mx * scale;
     }
+  };
+  int base = 0;
+  if (FIRST) {
+    if (n > 0) compute(0, first);
+    base = kScanBatch;
+  }
+  for (; base < n; base += kScanBatch) {
+    ScanBatch<D> cur;
+    scan_load<D>(base, n, row, cur);
+    compute(base, cur);
   }
 }
 
-template <typename T, int D, int GQ>
-__global__ __launch_bounds__(kDecThreads) void decode_route_kernel(DecodeArgs a) {
-  const KParams& kp = a.kp;
-  const int F = a.forced_wgs;
-  // Placement: consecutive workgroups go to consecutive XCDs, so all
-  // workgroups of unit bh carry the same blockIdx.x % 8; the forced roles
-  // (0 .. F-1) come before the routing role (F) in blockIdx order.
-  const int x = blockIdx.x;
-  const int xcd = x % kXcds;
-  const int slot = x / kXcds;
-  const int role = slot / a.units_per_xcd;
-  const int bh = (slot % a.units_per_xcd) * kXcds + xcd;
-  if (bh >= kp.B * kp.Hkv || role > F) return;
-  const int b = bh / kp.Hkv;
-  const int h = bh % kp.Hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = wave_id();
-  const bool routing = role == F;
-  const int t = a.seq_len[b] - 1;
+// ---------------------------------------------------------------------------
+// Forced-window partials and the final merge.  Part slots of a unit: forced
+// workgroup f in slot f, the routing workgroup in slot F.  Every workgroup of
+// a unit counts its arrival once its slot is written; the last arriver merges
+// the other slots with its own result (still in LDS) into O.  The routing
+// workgroup normally arrives last: it checks the count early, and when every
+// forced workgroup has arrived it arrives at once and prefetches their slots
+// while it still routes and attends.  Nobody waits for anybody.
+
+// This thread's output element e = threadIdx.x (GQ * D <= kDecThreads) of the
+// part slots in `want` (bit p: slot p), loaded with plain loads.
+struct PartRegs {
+  float m[kDecMaxForced + 1], l[kDecMaxForced + 1], o[kDecMaxForced + 1];
+};
+
+template <int D, int GQ>
+__device__ __forceinline__ void load_parts(const float* parts, uint32_t want, PartRegs& r) {
   constexpr int stride = attn_part_stride<D, GQ>();
-  float* parts = a.partials + static_cast<int64_t>(bh) * F * stride;
-
-  __shared__ DecodeSmem<GQ, D> sm;
-
-  // a position outside the cache: empty index lists and NaN output (the
-  // attention launch then does nothing for this unit)
-  if (t < 0 || t >= kp.n_cap) {
-    if (routing) {
-      for (int i = tid; i < kp.top_k; i += kDecThreads) a.chunk_idx[static_cast<int64_t>(bh) * kp.top_k + i] = -1;
-      for (int i = tid; i < kp.top_g; i += kDecThreads) a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = -1;
-      const AttnOut out{a.O, nullptr, a.out_bf16, static_cast<int64_t>(b) * kp.Hq + h * GQ, 1, 0};
-      out.put_nan<D, kDecThreads>(GQ);
-    }
-    return;
+  const int e = min(static_cast<int>(threadIdx.x), GQ * D - 1);
+  const int hh = e / D;
+#pragma unroll
+  for (int p = 0; p <= kDecMaxForced; ++p) {
+    const bool in = (want >> p) & 1u;
+    const float* q = parts + (in ? p : 0) * stride;
+    r.m[p] = in ? q[GQ * D + hh] : -__builtin_huge_valf();
+    r.l[p] = q[GQ * D + GQ + hh];
+    r.o[p] = q[e];
   }
+}
+
+// Park this thread's loaded forced slots in LDS (stash[kDecMaxForced * 3 *
+// kDecThreads] floats) and take them back; slots p >= n come back empty.
+template <int D, int GQ>
+__device__ __forceinline__ void stash_parts(const PartRegs& r, float* stash) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < kDecMaxForced; ++p) {
+    stash[(3 * p) * kDecThreads + t] = r.m[p];
+    stash[(3 * p + 1) * kDecThreads + t] = r.l[p];
+    stash[(3 * p + 2) * kDecThreads + t] = r.o[p];
+  }
+}
+template <int D, int GQ>
+__device__ __forceinline__ void unstash_parts(const float* stash, int n, PartRegs& r) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < kDecMaxForced; ++p) {
+    r.m[p] = p < n ? stash[(3 * p) * kDecThreads + t] : -__builtin_huge_valf();
+    r.l[p] = stash[(3 * p + 1) * kDecThreads + t];
+    r.o[p] = stash[(3 * p + 2) * kDecThreads + t];
+  }
+  r.m[kDecMaxForced] = -__builtin_huge_valf();
+  r.l[kDecMaxForced] = 0.f;
+  r.o[kDecMaxForced] = 0.f;
+}
+static_assert(kDecMaxForced * 3 * kDecThreads <= kDecMaxScores, "stash fits the score array");
+
+// O[e] from this workgroup's merged waves (sm) and the loaded slots.
+template <int D, int GQ>
+__device__ __forceinline__ void merge_store(const AttnMergeSmem<GQ, D, kDecWaves>& mg, const PartRegs& r,
+                                            const AttnOut& out) {
+  const int e = threadIdx.x;
+  if (e >= GQ * D) return;
+  const int hh = e / D;
+  float M = mg.M[hh];
+#pragma unroll
+  for (int p = 0; p <= kDecMaxForced; ++p) M = fmaxf(M, r.m[p]);
+  const float wo = mg.M[hh] == -__builtin_huge_valf() ? 0.f : exp2f(mg.M[hh] - M);
+  float num = attn_wg_value<D, GQ, kDecWaves>(mg, e) * wo;
+  float den = mg.L[hh] * wo;
+#pragma unroll
+  for (int p = 0; p <= kDecMaxForced; ++p) {
+    const float w = r.m[p] == -__builtin_huge_valf() ? 0.f : exp2f(r.m[p] - M);
+    num = fmaf(w, r.o[p], num);
+    den = fmaf(w, r.l[p], den);
+  }
+  out.put<D>(hh, e % D, num / den);
+}
+
+// Write this workgroup's merged waves into part slot `slot` (device-coherent
+// stores), count the arrival and return true in every thread of the last
+// arriver of the unit's F + 1 workgroups.
+template <int D, int GQ>
+__device__ __forceinline__ bool publish_arrive(const DecodeArgs& a, int bh, int slot, AttnMergeSmem<GQ, D, kDecWaves>& mg) {
+  constexpr int stride = attn_part_stride<D, GQ>();
+  const int tid = threadIdx.x;
+  float* mine = a.partials + (static_cast<int64_t>(bh) * (a.forced_wgs + 1) + slot) * stride;
+  for (int e = tid; e < GQ * D; e += kDecThreads) st_agent(mine + e, attn_wg_value<D, GQ, kDecWaves>(mg, e));
+  if (tid < GQ) {
+    st_agent(mine + GQ * D + tid, mg.M[tid]);
+    st_agent(mine + GQ * D + GQ + tid, mg.L[tid]);
+  }
+  return arrive_last(a.sync + 4 * static_cast<int64_t>(bh), static_cast<uint32_t>(a.forced_wgs + 1), &mg.is_last);
+}
+
+__device__ __forceinline__ AttnOut unit_out(const DecodeArgs& a, int bh, int gq) {
+  const KParams& kp = a.kp;
+  return AttnOut{a.O, nullptr, a.out_bf16, static_cast<int64_t>(bh / kp.Hkv) * kp.Hq + (bh % kp.Hkv) * gq, 1, 0};
+}
+
+// Attention of the unit's GQ query heads over the sink, local and current
+// chunks, blocks [f * bpw, (f + 1) * bpw) of them.
+template <typename T, int D, int GQ>
+__device__ __forceinline__ void forced_role(const DecodeArgs& a, int bh, int f, int t, DecodeSmem<GQ, D>& sm) {
+  const KParams& kp = a.kp;
+  const int b = bh / kp.Hkv, h = bh % kp.Hkv;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
   const int j = t / kp.C;
   const T* Qb = static_cast<const T*>(a.Q) + (static_cast<int64_t>(b) * kp.Hq + h * GQ) * D;
   const T* Kb = static_cast<const T*>(a.K) + static_cast<int64_t>(bh) * kp.n_cap * D;
   const T* Vb = static_cast<const T*>(a.V) + static_cast<int64_t>(bh) * kp.n_cap * D;
-
   AttnLaneFor<T, D, GQ> st;
-  auto init_q = [&]() { st.init([&](int hh) { return Qb + static_cast<int64_t>(hh) * D; }, lane & 15); };
+  st.init([&](int hh) { return Qb + static_cast<int64_t>(hh) * D; }, lane & 15);
+  st.set_tile(sm.ktile);
+  const Forced fc = forced_chunks(j, kp.n_sink, kp.n_local);
+  const int nF = fc.n * kp.C;
+  const int nblk = (nF + kAttnBlock - 1) / kAttnBlock;
+  const int bb = min(nblk, f * a.forced_bpw);
+  const int be = min(nblk, bb + a.forced_bpw);
+  // masked slots point at the query's own row
+  auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
+    const int fi = s >> kp.log2C;
+    const int off = s & (kp.C - 1);
+    const int64_t tok = s < nF ? static_cast<int64_t>(forced_chunk_at(fc, fi)) * kp.C + off : t;
+    const bool ok = s < nF && tok <= t;
+    kr = Kb + (ok ? tok : t) * D;
+    vr = Vb + (ok ? tok : t) * D;
+    return ok;
+  };
+  st.template run<kForcedPF>(0, bb + wid, be, kDecWaves, kp.scale_log2, row);
+  attn_merge_waves(st, sm.mg);
+  if (publish_arrive<D, GQ>(a, bh, f, sm.mg)) {
+    // last arriver (rare): merge the other F slots, the routing one included
+    PartRegs r;
+    const uint32_t all = (2u << a.forced_wgs) - 1u;
+    load_parts<D, GQ>(a.partials + static_cast<int64_t>(bh) * (a.forced_wgs + 1) * attn_part_stride<D, GQ>(),
+                      all & ~(1u << f), r);
+    merge_store<D, GQ>(sm.mg, r, unit_out(a, bh, GQ));
+  }
+  // ---- the query completes chunk j: summarise it for the next steps' routing
+  if (f == 0 && a.build_summary && (t + 1) % kp.C == 0) {
+    summarize_chunk<T, D>(Kb + static_cast<int64_t>(j) * kp.C * D, j, kp, true, nullptr,
+                          a.chunk_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap + j) * D,
+                          a.group_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m +
+                                           static_cast<int64_t>(j) * kp.m) * D);
+  }
+}
 
-  if (!routing) {
-    // ---- a share of the forced (sink, local, current) chunk rows
-    const int f = role;
-    init_q();
-    const Forced fc = forced_chunks(j, kp.n_sink, kp.n_local);
-    const int nF = fc.n * kp.C;
-    const int nblk = (nF + kAttnBlock - 1) / kAttnBlock;
-    const int bb = min(nblk, f * a.forced_bpw);
-    const int be = min(nblk, bb + a.forced_bpw);
-    // masked slots point at the query's own row
-    auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
-      const int fi = s >> kp.log2C;
-      const int off = s & (kp.C - 1);
-      const int64_t tok = s < nF ? static_cast<int64_t>(forced_chunk_at(fc, fi)) * kp.C + off : t;
-      const bool ok = s < nF && tok <= t;
-      kr = Kb + (ok ? tok : t) * D;
-      vr = Vb + (ok ? tok : t) * D;
-      return ok;
-    };
-    st.template run<kForcedPF>(0, bb + wid, be, kDecWaves, kp.scale_log2, row);
-    attn_merge_waves(st, sm.mg);
-    // publish [o | m | l]; the attention launch that follows reads it
-    float* mine = parts + static_cast<int64_t>(f) * stride;
-    for (int e = tid; e < GQ * D; e += kDecThreads) mine[e] = attn_wg_value<D, GQ, kDecWaves>(sm.mg, e);
-    if (tid < GQ) {
-      mine[GQ * D + tid] = sm.mg.M[tid];
-      mine[GQ * D + GQ + tid] = sm.mg.L[tid];
-    }
-
-    // ---- the query completes chunk j: summarise it for the next steps' routing
-    if (f == 0 && a.build_summary && (t + 1) % kp.C == 0) {
-      summarize_chunk<T, D>(Kb + static_cast<int64_t>(j) * kp.C * D, j, kp, true, nullptr,
-                            a.chunk_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap + j) * D,
-                            a.group_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m +
-                                             static_cast<int64_t>(j) * kp.m) * D);
-    }
+// Routing of the unit (chunk top-k, then group top-g) and attention of its GQ
+// query heads over the routed groups' rows, merged with the forced partials.
+template <typename T, int D, int GQ>
+__device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, DecodeSmem<GQ, D>& sm) {
+  const KParams& kp = a.kp;
+  const int F = a.forced_wgs;
+  const int b = bh / kp.Hkv, h = bh % kp.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = wave_id();
+  const T* Qb = static_cast<const T*>(a.Q) + (static_cast<int64_t>(b) * kp.Hq + h * GQ) * D;
+  const T* Kb = static_cast<const T*>(a.K) + static_cast<int64_t>(bh) * kp.n_cap * D;
+  const T* Vb = static_cast<const T*>(a.V) + static_cast<int64_t>(bh) * kp.n_cap * D;
+  const float* parts = a.partials + static_cast<int64_t>(bh) * (F + 1) * attn_part_stride<D, GQ>();
+  uint32_t* counter = a.sync + 4 * static_cast<int64_t>(bh);
+  const float* ctab = a.chunk_sum + (static_cast<int64_t>(bh) * kp.n_chunks_cap + kp.n_sink) * D;
+  auto crow = [&](int i) { return ctab + static_cast<int64_t>(i) * D; };
+  // ---- loads that do not depend on the position go out together with it:
+  // the query rows and the first batch of candidate summaries (bounded by
+  // the table, masked once the candidate count is known)
+  ScanBatch<D> first;
+  scan_load<D>(0, min(kScanBatch, kp.n_chunks_cap - kp.n_sink), crow, first);
+  for (int e = tid; e < GQ * D; e += kDecThreads) sm.qs[e] = elem<T>::get(Qb, e);
+  const int t = a.seq_len[b] - 1;
+  if (t < 0 || t >= kp.n_cap) {
+    // a position outside the cache: empty index lists and NaN output
+    for (int i = tid; i < kp.top_k; i += kDecThreads) a.chunk_idx[static_cast<int64_t>(bh) * kp.top_k + i] = -1;
+    for (int i = tid; i < kp.top_g; i += kDecThreads) a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = -1;
+    unit_out(a, bh, GQ).put_nan<D, kDecThreads>(GQ);
     return;
   }
-
-  // ---- level 1: score every candidate chunk, keep the top-k
-  for (int e = tid; e < GQ * D; e += kDecThreads) sm.qs[e] = elem<T>::get(Qb, e);
+  const int j = t / kp.C;
   __syncthreads();
+  // ---- level 1: score every candidate chunk, keep the top-k
   const int nM = max(0, j - kp.n_local - kp.n_sink);
-  const float* ctab = a.chunk_sum + (static_cast<int64_t>(bh) * kp.n_chunks_cap + kp.n_sink) * D;
-  scan_scores<D, GQ>(sm.qs, nM, kp.inv_sqrt_d, [&](int i) { return ctab + static_cast<int64_t>(i) * D; }, sm.sc);
+  scan_scores<D, GQ, true>(sm.qs, nM, kp.inv_sqrt_d, crow, sm.sc, first);
   __syncthreads();
   const int cnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nM, kp.top_k, sm.selc, sm.sel);
+  // ---- have all forced workgroups arrived?  Then this one is the last: it
+  // arrives now (resetting the count) and prefetches their slots below.
+  if (tid == 0) {
+    int early = 0;
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(F)) {
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      early = 1;
+    }
+    sm.early = early;
+  }
   int32_t* ci = a.chunk_idx + static_cast<int64_t>(bh) * kp.top_k;
   for (int i = tid; i < kp.top_k; i += kDecThreads) ci[i] = i < cnt ? kp.n_sink + sm.selc[i] : -1;
-
   // ---- level 2: score the groups of the routed chunks, keep the top-g
   const int m = kp.m;
   const int nG = cnt * m;
@@ -202,106 +334,85 @@ __global__ __launch_bounds__(kDecThreads) void decode_route_kernel(DecodeArgs a)
                      },
                      sm.sc);
   __syncthreads();
+  const bool early = sm.early != 0;
+  PartRegs pr;
+  if (early) load_parts<D, GQ>(parts, (1u << F) - 1u, pr);
   const int gcnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nG, kp.top_g, sm.selg, sm.sel);
+  // the prefetched slots wait in LDS (the scores are no longer needed)
+  if (early) stash_parts<D, GQ>(pr, sm.sc);
   for (int i = tid; i < kp.top_g; i += kDecThreads) {
     int32_t v = -1;
     if (i < gcnt) {
       const int sg = sm.selg[i];
       v = (kp.n_sink + sm.selc[sg / m]) * m + sg % m;
+      sm.gl[i] = v;
     }
     a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = v;
   }
+  __syncthreads();
+  // ---- attention over the routed groups' rows (all visible: routed chunks
+  // end before the local window)
+  AttnLaneFor<T, D, GQ> st;
+  st.init([&](int hh) { return Qb + static_cast<int64_t>(hh) * D; }, lane & 15);
+  st.set_tile(sm.ktile);
+  const int nR = gcnt * kp.G;
+  const int nblk = (nR + kAttnBlock - 1) / kAttnBlock;
+  if (kp.log2G >= 4) {
+    // groups of whole blocks: every fetched slot is a routed row, so no slot is
+    // masked (and the list reads of a block have no branch around them)
+    auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
+      const int64_t tok = (static_cast<int64_t>(sm.gl[s >> kp.log2G]) << kp.log2G) + (s & (kp.G - 1));
+      kr = Kb + tok * D;
+      vr = Vb + tok * D;
+      return true;
+    };
+    st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
+  } else {
+    // masked slots point at the query's own row
+    auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
+      const bool ok = s < nR;
+      const int64_t tok =
+          ok ? (static_cast<int64_t>(sm.gl[min(s >> kp.log2G, kSelMaxK - 1)]) << kp.log2G) + (s & (kp.G - 1)) : t;
+      kr = Kb + tok * D;
+      vr = Vb + tok * D;
+      return ok;
+    };
+    st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
+  }
+  attn_merge_waves(st, sm.mg);
+  if (early) {
+    unstash_parts<D, GQ>(sm.sc, F, pr);
+    merge_store<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
+  } else if (publish_arrive<D, GQ>(a, bh, F, sm.mg)) {
+    load_parts<D, GQ>(parts, (1u << F) - 1u, pr);
+    merge_store<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
+  }
 }
 
-// ---------------------------------------------------------------------------
-// Second launch: workgroup (unit, hg) attends every routed group row of the
-// unit for query heads hg*HG .. hg*HG+HG-1 and merges the result with those
-// heads' forced-window partials from the first launch into the output.  The
-// GQ/HG workgroups of a unit read the same K/V rows, on the same XCD, so the
-// repeats are served by that XCD's L2.
-template <int GQ, int HG, int D>
-struct DecodeAttendSmem {
-  int gl[kSelMaxK];
-  AttnMergeSmem<HG, D, kDecWaves> mg;
-};
-
-template <typename T, int D, int GQ, int HG>
-__global__ __launch_bounds__(kDecThreads) void decode_attend_kernel(DecodeArgs a) {
-  constexpr int NHG = GQ / HG;
-  const KParams& kp = a.kp;
-  const int F = a.forced_wgs;
-  // placement: the NHG workgroups of unit bh share blockIdx.x % 8 (one XCD)
+// Unit bh of the workgroup at blockIdx.x: consecutive workgroups go to
+// consecutive XCDs, so all workgroups of a unit share blockIdx.x % 8 and its
+// summaries and rows are shared through one L2; roles in blockIdx order.
+__device__ __forceinline__ void unit_of(const DecodeArgs& a, int& bh, int& role) {
   const int x = blockIdx.x;
-  const int xcd = x % kXcds;
   const int slot = x / kXcds;
-  const int hg = slot / a.units_per_xcd;
-  const int bh = (slot % a.units_per_xcd) * kXcds + xcd;
-  if (bh >= kp.B * kp.Hkv || hg >= NHG) return;
-  const int b = bh / kp.Hkv;
-  const int h = bh % kp.Hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = wave_id();
-  const int t = a.seq_len[b] - 1;
-  if (t < 0 || t >= kp.n_cap) return;  // NaN output written by the routing launch
-  const int head0 = h * GQ + hg * HG;   // first query head of this workgroup
-  const T* Qb = static_cast<const T*>(a.Q) + (static_cast<int64_t>(b) * kp.Hq + head0) * D;
-  const T* Kb = static_cast<const T*>(a.K) + static_cast<int64_t>(bh) * kp.n_cap * D;
-  const T* Vb = static_cast<const T*>(a.V) + static_cast<int64_t>(bh) * kp.n_cap * D;
-  constexpr int stride = attn_part_stride<D, GQ>();
-  const float* parts = a.partials + static_cast<int64_t>(bh) * F * stride;
+  role = slot / a.units_per_xcd;
+  bh = (slot % a.units_per_xcd) * kXcds + x % kXcds;
+}
 
-  __shared__ DecodeAttendSmem<GQ, HG, D> sm;
-  for (int i = tid; i < kp.top_g; i += kDecThreads) sm.gl[i] = a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i];
-  AttnLaneFor<T, D, HG> st;
-  st.init([&](int hh) { return Qb + static_cast<int64_t>(hh) * D; }, lane & 15);
-  __syncthreads();
-
-  const int nR = kp.top_g * kp.G;
-  const int nblk = (nR + kAttnBlock - 1) / kAttnBlock;
-  // masked slots point at the query's own row
-  auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
-    const int e = s >> kp.log2G;
-    const int g = s < nR ? sm.gl[e] : -1;
-    const int64_t tok = (static_cast<int64_t>(g) << kp.log2G) + (s & (kp.G - 1));
-    const bool ok = g >= 0 && tok <= t;
-    kr = Kb + (ok ? tok : t) * D;
-    vr = Vb + (ok ? tok : t) * D;
-    return ok;
-  };
-  st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
-  attn_merge_waves(st, sm.mg);
-
-  const AttnOut out{a.O, nullptr, a.out_bf16, static_cast<int64_t>(b) * kp.Hq + head0, 1, 0};
-  constexpr int kOut = (HG * D + kDecThreads - 1) / kDecThreads;
-#pragma unroll
-  for (int r = 0; r < kOut; ++r) {
-    const int e = tid + r * kDecThreads;
-    if (e >= HG * D) continue;
-    const int hh = e / D;               // head within this workgroup
-    const int gh = hg * HG + hh;        // head within the unit (forced partial layout)
-    float mp[kDecMaxParts], lp[kDecMaxParts], op[kDecMaxParts];
-#pragma unroll
-    for (int p = 0; p < kDecMaxParts; ++p) {
-      const bool in = p < F;
-      const float* q = parts + (in ? p : 0) * stride;
-      mp[p] = in ? q[GQ * D + gh] : -__builtin_huge_valf();
-      lp[p] = q[GQ * D + GQ + gh];
-      op[p] = q[gh * D + e % D];
-    }
-    float M = sm.mg.M[hh];
-#pragma unroll
-    for (int p = 0; p < kDecMaxParts; ++p) M = fmaxf(M, mp[p]);
-    const float wo = sm.mg.M[hh] == -__builtin_huge_valf() ? 0.f : exp2f(sm.mg.M[hh] - M);
-    float num = attn_wg_value<D, HG, kDecWaves>(sm.mg, e) * wo;
-    float den = sm.mg.L[hh] * wo;
-#pragma unroll
-    for (int p = 0; p < kDecMaxParts; ++p) {
-      const float w = mp[p] == -__builtin_huge_valf() ? 0.f : exp2f(mp[p] - M);
-      num += w * op[p];
-      den += w * lp[p];
-    }
-    out.put<D>(hh, e % D, num / den);
+// One launch per step.  Roles: 0 routing and routed attention, 1..F forced.
+template <typename T, int D, int GQ>
+__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeArgs a) {
+  int bh, role;
+  unit_of(a, bh, role);
+  const KParams& kp = a.kp;
+  if (bh >= kp.B * kp.Hkv || role > a.forced_wgs) return;
+  __shared__ DecodeSmem<GQ, D> sm;
+  if (role == 0) {
+    routing_role<T, D, GQ>(a, bh, sm);
+  } else {
+    const int t = a.seq_len[bh / kp.Hkv] - 1;
+    if (t < 0 || t >= kp.n_cap) return;  // NaN output written by the routing role
+    forced_role<T, D, GQ>(a, bh, role - 1, t, sm);
   }
 }
 
@@ -316,8 +427,8 @@ bool decode_fused_supported(const KParams& kp) {
 
 template <typename T, int D, int GQ>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-  const unsigned n_wg = static_cast<unsigned>(kXcds) * a.units_per_xcd * (a.forced_wgs + 1);
-  decode_route_kernel<T, D, GQ><<<n_wg, kDecThreads, 0, st>>>(a);
+  const unsigned per_role = static_cast<unsigned>(kXcds) * a.units_per_xcd;
+  decode_step_kernel<T, D, GQ><<<per_role * (1 + a.forced_wgs), kDecThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -331,31 +442,10 @@ static hipError_t launch_gq(const DecodeArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_decode_route(const DecodeArgs& a, bool bf16_in, hipStream_t st) {
+hipError_t launch_decode_step(const DecodeArgs& a, bool bf16_in, hipStream_t st) {
+  if (a.forced_wgs < 1 || a.forced_wgs > kDecMaxForced) return hipErrorInvalidValue;
   if (bf16_in) return a.kp.d == 64 ? launch_gq<bf16, 64>(a, st) : launch_gq<bf16, 128>(a, st);
   return a.kp.d == 64 ? launch_gq<float, 64>(a, st) : launch_gq<float, 128>(a, st);
-}
-
-template <typename T, int D, int GQ, int HG>
-static hipError_t launch_att_t(const DecodeArgs& a, hipStream_t st) {
-  const unsigned n_wg = static_cast<unsigned>(kXcds) * a.units_per_xcd * (GQ / HG);
-  decode_attend_kernel<T, D, GQ, HG><<<n_wg, kDecThreads, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_att_gq(const DecodeArgs& a, hipStream_t st) {
-  switch (a.kp.gq) {
-    case 1: return launch_att_t<T, D, 1, 1>(a, st);
-    case 2: return launch_att_t<T, D, 2, 1>(a, st);
-    case 4: return launch_att_t<T, D, 4, HGA_DECODE_HEADS_PER_WG>(a, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_decode_attend(const DecodeArgs& a, bool bf16_in, hipStream_t st) {
-  if (bf16_in) return a.kp.d == 64 ? launch_att_gq<bf16, 64>(a, st) : launch_att_gq<bf16, 128>(a, st);
-  return a.kp.d == 64 ? launch_att_gq<float, 64>(a, st) : launch_att_gq<float, 128>(a, st);
 }
 
 }  // namespace hga

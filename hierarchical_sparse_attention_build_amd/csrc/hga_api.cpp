@@ -173,9 +173,8 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base
   return a;
 }
 
-// Decode step in two launches: F forced-window workgroups and one routing
-// workgroup per (b, kv head); then one workgroup per (b, query head) for the
-// routed rows and the merge.
+// Decode step in one launch: per (b, kv head), one workgroup routes and
+// attends the routed rows, F attend the forced window; the last merges.
 #ifndef HGA_DECODE_FORCED_WGS
 #define HGA_DECODE_FORCED_WGS 2
 #endif
@@ -183,7 +182,7 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base
 struct FusedPlan {
   bool use;
   int forced_wgs, forced_bpw, units_per_xcd;
-  size_t partials_off, bytes;
+  size_t sync_off, partials_off, bytes;
 };
 
 FusedPlan plan_fused(const KParams& kp, size_t base) {
@@ -191,13 +190,15 @@ FusedPlan plan_fused(const KParams& kp, size_t base) {
   r.use = decode_fused_supported(kp);
   if (!r.use) return r;
   const int fblocks = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kAttBlockRows));
-  r.forced_wgs = std::min(std::min(HGA_DECODE_FORCED_WGS, fblocks), kDecMaxParts);
+  r.forced_wgs = std::min(std::min(HGA_DECODE_FORCED_WGS, fblocks), kDecMaxForced);
   r.forced_bpw = static_cast<int>(cdiv(fblocks, r.forced_wgs));
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   r.units_per_xcd = static_cast<int>(cdiv(units, kXcds));
   size_t off = base;
+  r.sync_off = off;
+  off = align256(off + static_cast<size_t>(units) * 4 * sizeof(uint32_t));
   r.partials_off = off;
-  off = align256(off + static_cast<size_t>(units) * r.forced_wgs * kp.gq * (kp.d + 2) * sizeof(float));
+  off = align256(off + static_cast<size_t>(units) * (r.forced_wgs + 1) * kp.gq * (kp.d + 2) * sizeof(float));
   r.bytes = off - base;
   return r;
 }
@@ -535,8 +536,8 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
     da.forced_bpw = fp.forced_bpw;
     da.units_per_xcd = fp.units_per_xcd;
     da.partials = at<float>(ws, fp.partials_off);
-    HGA_TRY_HIP(launch_decode_route(da, bf, st), "decode route");
-    HGA_TRY_HIP(launch_decode_attend(da, bf, st), "decode attend");
+    da.sync = at<uint32_t>(ws, fp.sync_off);
+    HGA_TRY_HIP(launch_decode_step(da, bf, st), "decode step");
     return ok();
   }
   RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);

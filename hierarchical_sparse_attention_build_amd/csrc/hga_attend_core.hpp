@@ -111,7 +111,8 @@ struct AttnLane {
     const int lane = threadIdx.x & (kWave - 1);
     const int rg = lane >> 4;
     const int cc = lane & 15;
-    const int n = first < end ? (end - first + step - 1) / step : 0;  // blocks of this wave
+    // blocks of this wave (wave-uniform, so that the block loop branches on the scalar unit)
+    const int n = __builtin_amdgcn_readfirstlane(first < end ? (end - first + step - 1) / step : 0);
     RawVec<RB> kb[PF][4], vb[PF][4];
     bool okb[PF][4];
     auto fetch = [&](int blkid, RawVec<RB>* kr, RawVec<RB>* vr, bool* ok) {
@@ -209,28 +210,76 @@ struct AttnLane {
         for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(s[i][hh], vf[e], o[hh][e]);
     }
   }
+
+  // (no LDS staging on this path)
+  __device__ __forceinline__ void set_tile(unsigned char*) {}
+
+  // This wave's unnormalised output, ow[hh * D + d] for every head hh < GQ:
+  // the four row groups are summed first.
+  __device__ __forceinline__ void store_o(float* ow) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int rg = lane >> 4;
+    const int cc = lane & 15;
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[hh][e] = sum_rows(o[hh][e]);
+    if (rg == 0) {
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ow[hh * D + cc * EPL + e] = o[hh][e];
+    }
+  }
 };
 
-// The same per-wave attention for bf16 inputs with QK^T on the matrix cores.
-// A 16-row block's scores come from v_mfma_f32_16x16x32_bf16 with the K rows
-// as the A operand (lane l loads 16 bytes of row l%16, straight from memory)
-// and the query heads as the B operand (head l%16, padded with zeros to 16
-// heads).  The result holds S[row 4g+i][head h] in lane (g, h) = (l/16, l%16),
-// item i.  The softmax runs in that layout; the weights reach the PV layout
-// (lane (g, c): rows 4g..4g+3, the c-th sixteenth of every row) by DPP
-// broadcasts within each 16-lane row, and PV stays on the vector ALUs.  The
-// running (max, sum, output) have the same meaning and layout as in AttnLane.
+// The same per-wave attention for bf16 inputs on the matrix cores, two
+// 16-row blocks at a time.
+//   S = K Q^T   v_mfma_f32_16x16x32_bf16 per block, the K rows as the A operand
+//               and the query heads as the B operand (head l%16, zero-padded
+//               to 16): lane (g, h) = (l/16, l%16) gets S[row 4g+i][head h],
+//               item i.  K rows are loaded like V rows (each load instruction
+//               covers four whole rows, so every cache line is fetched once
+//               and in full) and pass through a per-wave LDS tile to reach the
+//               operand layout (lane l: 16 bytes of row l%16).
+//   O += P V    v_mfma_f32_16x16x32_bf16 with the 32 rows of the block pair as
+//               the reduction index, ordered k = 8g + 4b + i for row 4g+i of
+//               block b.  In that order lane (g, h) already holds the A
+//               operand P[h][k] (its own scores), and lane (g, c) the B
+//               operand for output column d = c*(D/16) + e: element e of the
+//               rows 4g..4g+3 it loaded from each block (one v_perm_b32 per
+//               pair of rows).  P (<= 1) enters as the sum of two bf16 values,
+//               hi = bf16(p) and lo = bf16(p - hi), so it keeps 16 significant
+//               bits; V is bf16 already, and the products accumulate in fp32.
+// O lands as O[head 4g+i][column c*(D/16)+e] in lane (g, c), item i of
+// accumulator e.  The softmax statistics are per head as in AttnLane.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS bytes per wave for the matrix-core path's K tile (16 rows of D bf16, padded)
+template <int D>
+__host__ __device__ constexpr int attn_ktile_bytes() { return 16 * (D + 8) * 2; }
+
+// two floats rounded to bf16 (to nearest even), packed low first
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 template <int D, int GQ>
 struct AttnLaneMfma {
   static_assert(GQ <= 16, "at most 16 query heads per KV head");
-  static constexpr int EPL = D / 16;  // PV layout: elements of a row per lane
-  static constexpr int RB = EPL * 2;  // bytes of a row per lane
-  static constexpr int KS = D / 32;   // MFMA steps over the head dimension
+  static constexpr int EPL = D / 16;  // output columns per lane
+  static constexpr int RB = EPL * 2;  // bytes of a V row per lane
+  static constexpr int KS = D / 32;   // MFMA steps of QK^T over the head dimension
+  static constexpr int KROWB = (D + 8) * 2;  // bytes per LDS tile row (padded against bank conflicts)
   bf16x8_t qb[KS];
-  float m_run[GQ], l_run[GQ], o[GQ][EPL];
+  float m_run[GQ], l_run[GQ];
+  f32x4_t acc[EPL];
+  unsigned char* kt;  // this wave's LDS tile of 16 K rows
+
+  // base: an LDS area of attn_ktile_bytes<D>() bytes per wave of the workgroup
+  __device__ __forceinline__ void set_tile(unsigned char* base) { kt = base + wave_id() * 16 * KROWB; }
 
   template <typename QFn>
   __device__ __forceinline__ void init(QFn q, int /*cc*/) {
@@ -247,14 +296,14 @@ struct AttnLaneMfma {
     for (int hh = 0; hh < GQ; ++hh) {
       m_run[hh] = -__builtin_huge_valf();
       l_run[hh] = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   struct Buf {
-    uint4 k[KS];           // MFMA A fragments of row l%16
-    RawVec<RB> v[4];       // rows 4g+i, the lane's sixteenth
+    RawVec<RB> k[4];       // K rows 4g+i, the lane's columns
+    RawVec<RB> v[4];       // V rows 4g+i, the lane's columns
     uint32_t ok;           // bit r: row r of the block is visible
   };
 
@@ -264,50 +313,85 @@ struct AttnLaneMfma {
     const int g = lane >> 4;
     const int cc = lane & 15;
     const int s0 = R0 + blkid * kAttnBlock;
-    const bf16* kp;
-    const bf16* vp;
-    const bool okk = row(s0 + (lane & 15), kp, vp);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b.k[ks] = *reinterpret_cast<const uint4*>(kp + ks * 32 + g * 8);
-    b.ok = static_cast<uint32_t>(__ballot(okk)) & 0xffffu;
+    uint32_t okm = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      row(s0 + 4 * g + i, kp, vp);
+      const bf16* kp;
+      const bf16* vp;
+      const bool ok = row(s0 + 4 * g + i, kp, vp);
+      b.k[i] = load_raw<RB>(kp + cc * EPL);
       b.v[i] = load_raw<RB>(vp + cc * EPL);
+      // row 4g+i is visible iff lane 16g saw ok
+      const uint64_t m = __ballot(ok);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) okm |= static_cast<uint32_t>((m >> (16 * gg)) & 1u) << (4 * gg + i);
     }
+    b.ok = okm;
   }
 
-  // Blocks blk = first, first + step, ... < end, in rounds of PF: the loads of
-  // a round's blocks are all issued before its first block is computed.
+  // S[row 4g+i][head h] (raw dot products) of one block: its K rows go
+  // through the tile into the A operand layout.
+  __device__ __forceinline__ f32x4_t scores(const Buf& b) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4;
+    const int cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<RawVec<RB>*>(kt + (4 * g + i) * KROWB + cc * RB) = b.k[i];
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(kt + cc * KROWB + (ks * 32 + g * 8) * 2);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], s, 0, 0, 0);
+    }
+    return s;
+  }
+
+  // Blocks blk = first, first + step, ... < end, in rounds of PF (even): the
+  // loads of a round's blocks are all issued before its first pair is computed.
   template <int PF = 2, typename RowFn>
   __device__ __forceinline__ void run(int R0, int first, int end, int step, float scale_log2, RowFn row) {
-    const int n = first < end ? (end - first + step - 1) / step : 0;  // blocks of this wave
+    static_assert(PF % 2 == 0, "blocks are computed in pairs");
+    // blocks of this wave (wave-uniform, so that the block loop branches on the scalar unit)
+    const int n = __builtin_amdgcn_readfirstlane(first < end ? (end - first + step - 1) / step : 0);
     for (int c0 = 0; c0 < n; c0 += PF) {
       Buf buf[PF];
 #pragma unroll
       for (int p = 0; p < PF; ++p)
         if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row);
 #pragma unroll
-      for (int p = 0; p < PF; ++p)
-        if (c0 + p < n) block(buf[p], scale_log2);
+      for (int p = 0; p < PF; p += 2) {
+        if (c0 + p >= n) break;
+        const bool has1 = c0 + p + 1 < n;
+        if (!has1) {
+          buf[p + 1].ok = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) buf[p + 1].v[i] = zero_raw<RB>();
+        }
+        pair(buf[p], buf[p + 1], has1, scale_log2);
+      }
     }
   }
 
-  __device__ __forceinline__ void block(const Buf& b, float scale_log2) {
+  __device__ __forceinline__ void pair(const Buf& b0, const Buf& b1, bool has1, float scale_log2) {
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane >> 4;
     const int h = lane & 15;
-    // ---- S[row 4g+i][head h], base 2, masked rows -inf
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- S of both blocks, base 2, masked rows -inf
+    const f32x4_t s0 = scores(b0);
+    f32x4_t s1 = {0.f, 0.f, 0.f, 0.f};
+    if (has1) s1 = scores(b1);
+    float sv[8];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b.k[ks]), qb[ks], acc, 0, 0, 0);
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = (b.ok >> (4 * g + i)) & 1u ? acc[i] * scale_log2 : -__builtin_huge_valf();
-    // ---- block max of head h (same in the 4 lanes of the head), then per head
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (b0.ok >> (4 * g + i)) & 1u ? s0[i] * scale_log2 : -__builtin_huge_valf();
+      sv[4 + i] = (b1.ok >> (4 * g + i)) & 1u ? s1[i] * scale_log2 : -__builtin_huge_valf();
+    }
+    // ---- pair max of head h (same in the 4 lanes of the head), then per head
     // in scalar registers: rescale only when the running max rises
-    const float bm_lane = max_rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    float bm_lane = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) bm_lane = fmaxf(bm_lane, sv[i]);
+    bm_lane = max_rows(bm_lane);
     float mh = 0.f;
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
@@ -315,16 +399,18 @@ struct AttnLaneMfma {
       if (bm > m_run[hh]) {
         const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - bm);  // 0 when m_run = -inf
         l_run[hh] *= alpha;
+        // head hh sits in item hh%4 of the lanes with g = hh/4
+        const float al = GQ <= 4 || g == (hh >> 2) ? alpha : 1.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[hh][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) acc[e][hh & 3] *= al;
         m_run[hh] = bm;
       }
       const float mref = m_run[hh] == -__builtin_huge_valf() ? 0.f : m_run[hh];
       mh = h == hh ? mref : mh;
     }
-    float p[4], ps = 0.f;
+    float p[8], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       p[i] = __builtin_amdgcn_exp2f(sv[i] - mh);  // 0 for a masked row
       ps += p[i];
     }
@@ -332,23 +418,48 @@ struct AttnLaneMfma {
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh)
       l_run[hh] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps), hh));
-    // ---- PV: lane (g, c) takes the weights of rows 4g+i from lane (g, hh)
+    // ---- P as hi + lo bf16 pairs (A operand, k = 8g + 4b + i)
+    uint4 phi, plo;
+    uint32_t* hw = reinterpret_cast<uint32_t*>(&phi);
+    uint32_t* lw = reinterpret_cast<uint32_t*>(&plo);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vf[EPL];
-#pragma unroll
-      for (int w = 0; w < EPL / 2; ++w) {
-        const uint32_t x2 = word(b.v[i], w);
-        vf[2 * w] = bf16lo(x2);
-        vf[2 * w + 1] = bf16hi(x2);
-      }
-#pragma unroll
-      for (int hh = 0; hh < GQ; ++hh) {
-        const float w = dpp::row_share(p[i], hh);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(w, vf[e], o[hh][e]);
-      }
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = pack_bf16x2(p[2 * w], p[2 * w + 1]);
+      hw[w] = x;
+      lw[w] = pack_bf16x2(p[2 * w] - __uint_as_float(x << 16), p[2 * w + 1] - __uint_as_float(x & 0xffff0000u));
     }
+    const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, phi);
+    const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, plo);
+    // ---- PV: B operand of column e = element e of the lane's rows (k order)
+    uint4 vb[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+      const int wi = e >> 1;
+      vb[e].x = __builtin_amdgcn_perm(word(b0.v[1], wi), word(b0.v[0], wi), sel);
+      vb[e].y = __builtin_amdgcn_perm(word(b0.v[3], wi), word(b0.v[2], wi), sel);
+      vb[e].z = __builtin_amdgcn_perm(word(b1.v[1], wi), word(b1.v[0], wi), sel);
+      vb[e].w = __builtin_amdgcn_perm(word(b1.v[3], wi), word(b1.v[2], wi), sel);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, __builtin_bit_cast(bf16x8_t, vb[e]), acc[e], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, __builtin_bit_cast(bf16x8_t, vb[e]), acc[e], 0, 0, 0);
+  }
+
+  // This wave's unnormalised output, ow[hh * D + d] for every head hh < GQ.
+  __device__ __forceinline__ void store_o(float* ow) const {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4;
+    const int c = lane & 15;
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh)
+      if (g == (hh >> 2)) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ow[hh * D + c * EPL + e] = acc[e][hh & 3];
+      }
   }
 };
 
@@ -412,15 +523,8 @@ struct AttnOut {
 // unnormalised output element e (head e / D), sm.M / sm.L its max and sum.
 template <typename Lane, int D, int GQ, int NWV>
 __device__ __forceinline__ void attn_merge_waves(Lane& st, AttnMergeSmem<GQ, D, NWV>& sm) {
-  constexpr int EPL = D / 16;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  const int rg = lane >> 4;
-  const int cc = lane & 15;
-#pragma unroll
-  for (int hh = 0; hh < GQ; ++hh)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) st.o[hh][e] = sum_rows(st.o[hh][e]);
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
@@ -428,12 +532,7 @@ __device__ __forceinline__ void attn_merge_waves(Lane& st, AttnMergeSmem<GQ, D, 
       sm.wl[wid][hh] = st.l_run[hh];
     }
   }
-  if (rg == 0) {
-#pragma unroll
-    for (int hh = 0; hh < GQ; ++hh)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm.ow[wid][hh * D + cc * EPL + e] = st.o[hh][e];
-  }
+  st.store_o(sm.ow[wid]);
   __syncthreads();
   if (static_cast<int>(threadIdx.x) < GQ) {
     const int hh = threadIdx.x;

@@ -74,8 +74,8 @@ struct AttendArgs {
   uint32_t* counters;     // ws [B*Hkv*nq]
 };
 
-// A decode step (nq = 1) in two launches: routing, forced-window attention and
-// the summary update; then the routed rows' attention and the merge.
+// A decode step (nq = 1) in one launch: routing and the routed rows' attention,
+// forced-window attention and the summary update, and the merge of the parts.
 struct DecodeArgs {
   KParams kp;
   const void* Q;             // [B, Hq, 1, d]
@@ -94,7 +94,8 @@ struct DecodeArgs {
   int32_t forced_wgs;        // forced-window workgroups per (b, kv head)
   int32_t forced_bpw;        // 16-row blocks of forced rows per forced workgroup
   int32_t units_per_xcd;     // ceil(B*Hkv / kXcds)
-  float* partials;           // ws [B*Hkv, forced_wgs, gq * (d + 2)]: forced-window partials
+  float* partials;           // ws [B*Hkv, forced_wgs + 1, gq * (d + 2)]: partial results
+  uint32_t* sync;            // ws [B*Hkv, 4]: arrival counter of each unit (zero between calls)
 };
 
 struct GatherArgs {
@@ -114,10 +115,9 @@ hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
 // Decode routing launch (Hq/Hkv <= 4, d in {64, 128}, candidate and index limits).
 constexpr int kXcds = 8;             // accelerator dies; workgroups are dealt to them in turn
 constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per unit
-constexpr int kDecMaxParts = 16;     // partial results merged per (b, kv head)
+constexpr int kDecMaxForced = 2;    // forced-window workgroups per (b, kv head)
 bool decode_fused_supported(const KParams& kp);
-hipError_t launch_decode_route(const DecodeArgs& a, bool bf16_in, hipStream_t st);
-hipError_t launch_decode_attend(const DecodeArgs& a, bool bf16_in, hipStream_t st);
+hipError_t launch_decode_step(const DecodeArgs& a, bool bf16_in, hipStream_t st);
 // Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
 bool prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_attend_prefill_mfma(const AttendArgs& a, hipStream_t st);
