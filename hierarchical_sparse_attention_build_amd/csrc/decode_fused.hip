@@ -46,10 +46,10 @@ struct DecodeSmem {
 
 // Scans: out[i] = max over the GQ query rows in qs of q . row(i) * scale, i in
 // [0, n).  Eight lanes share one fp32 summary row (each holds D/8 values of it
-// and of every query row); a batch of 8 rounds x 64 rows is loaded at once and
-// each round is computed as soon as it arrives.
+// and of every query row).  Rows go in batches of 2 rounds x 64 rows, two
+// batches in flight: a CU with more loads outstanding streams slower here.
 constexpr int kScanL = 8;                         // lanes per row
-constexpr int kScanKR = 8;                        // rounds per batch
+constexpr int kScanKR = 2;                        // rounds per batch (more in flight is slower)
 constexpr int kScanRPR = kDecThreads / kScanL;    // rows per round
 constexpr int kScanBatch = kScanRPR * kScanKR;
 
@@ -111,15 +111,16 @@ __device__ __forceinline__ void scan_scores(const float* qs, int n, float scale,
       if (i < n && piece == 0) out[i] = mx * scale;
     }
   };
-  int base = 0;
-  if (FIRST) {
-    if (n > 0) compute(0, first);
-    base = kScanBatch;
-  }
-  for (; base < n; base += kScanBatch) {
-    ScanBatch<D> cur;
-    scan_load<D>(base, n, row, cur);
+  // two batches in flight: the next batch's loads go out before the current
+  // batch is computed
+  ScanBatch<D> cur;
+  if (FIRST) cur = first;
+  else scan_load<D>(0, n, row, cur);
+  for (int base = 0; base < n; base += kScanBatch) {
+    ScanBatch<D> nxt;
+    if (base + kScanBatch < n) scan_load<D>(base + kScanBatch, n, row, nxt);
     compute(base, cur);
+    cur = nxt;
   }
 }
 

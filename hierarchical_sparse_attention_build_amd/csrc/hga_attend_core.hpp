@@ -353,11 +353,7 @@ struct AttnLaneMfma {
     static_assert(PF % 2 == 0, "blocks are computed in pairs");
     // blocks of this wave (wave-uniform, so that the block loop branches on the scalar unit)
     const int n = __builtin_amdgcn_readfirstlane(first < end ? (end - first + step - 1) / step : 0);
-    for (int c0 = 0; c0 < n; c0 += PF) {
-      Buf buf[PF];
-#pragma unroll
-      for (int p = 0; p < PF; ++p)
-        if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row);
+    auto compute = [&](int c0, Buf (&buf)[PF]) {
 #pragma unroll
       for (int p = 0; p < PF; p += 2) {
         if (c0 + p >= n) break;
@@ -369,6 +365,16 @@ struct AttnLaneMfma {
         }
         pair(buf[p], buf[p + 1], has1, scale_log2);
       }
+    };
+    auto load = [&](int c0, Buf (&buf)[PF]) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p)
+        if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row);
+    };
+    for (int c0 = 0; c0 < n; c0 += PF) {
+      Buf buf[PF];
+      load(c0, buf);
+      compute(c0, buf);
     }
   }
 
