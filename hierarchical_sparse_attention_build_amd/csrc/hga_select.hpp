@@ -55,7 +55,7 @@ __device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[E], int k
 }
 
 // Emit the k selected slots (keys > T, then the first keys == T in slot order)
-// as out(rank, e) in ascending slot order, slot order being (e, lane).
+// as out(rank, e, key) in ascending slot order, slot order being (e, lane).
 template <int E, typename OutFn>
 __device__ __forceinline__ void wave_emit(const uint32_t (&key)[E], int k, uint32_t T, OutFn out) {
   int n_gt = 0;
@@ -69,14 +69,14 @@ __device__ __forceinline__ void wave_emit(const uint32_t (&key)[E], int k, uint3
     const uint64_t eq = ballot64(is_eq);
     const bool take = key[e] > T || (is_eq && bits_below(eq) < need);
     const uint64_t tm = ballot64(take);
-    if (take) out(base + bits_below(tm), e);
+    if (take) out(base + bits_below(tm), e, key[e]);
     base += __popcll(tm);
     const int neq = __popcll(eq);
     need -= need < neq ? need : neq;
   }
 }
 
-// Emit every valid slot (key != 0) in slot order.
+// Emit every valid slot (key != 0) in slot order, as out(rank, e, key).
 template <int E, typename OutFn>
 __device__ __forceinline__ void wave_emit_all(const uint32_t (&key)[E], OutFn out) {
   int base = 0;
@@ -84,13 +84,13 @@ __device__ __forceinline__ void wave_emit_all(const uint32_t (&key)[E], OutFn ou
   for (int e = 0; e < E; ++e) {
     const bool take = key[e] != 0u;
     const uint64_t tm = ballot64(take);
-    if (take) out(base + bits_below(tm), e);
+    if (take) out(base + bits_below(tm), e, key[e]);
     base += __popcll(tm);
   }
 }
 
 // One wave: keys key_of(e) for slots (e, lane), e < E; emit the best k
-// (every valid key when all is set) through out(rank, e).
+// (every valid key when all is set) through out(rank, e, key).
 template <int E, typename KeyFn, typename OutFn>
 __device__ __forceinline__ void wave_topk(KeyFn key_of, int k, bool all, OutFn out) {
   uint32_t key[E];
@@ -120,7 +120,6 @@ struct SelSmem {
   static constexpr int NW = NT / kWave;
   uint32_t key[NW * kSelMaxK];
   int pos[NW * kSelMaxK];
-  int cnt[NW];
 };
 
 // True when block_select handles (n, k) for a workgroup of NT threads.
@@ -154,50 +153,38 @@ __device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm)
     // one wave, at most two keys per lane
     if (wid == 0)
       wave_topk_n((n + kWave - 1) / kWave, [&](int e) { return key_at(e * kWave + lane, n); }, k, false,
-                  [&](int r, int e) { sel[r] = e * kWave + lane; });
+                  [&](int r, int e, uint32_t) { sel[r] = e * kWave + lane; });
     __syncthreads();
     return k;
   }
 
-  // phase 1: wave w selects among positions [w*q, min(n, (w+1)*q))
+  // phase 1: wave w selects min(k, its share) among positions [w*q, min(n, (w+1)*q))
+  // and writes them, in ascending position order, after the earlier waves'
+  // winners (their counts are known to every wave), so the winners lie end to end
   const int q = (n + NW - 1) / NW;
   const int lo = wid * q;
   const int hi = min(n, lo + q);
   const int nw = max(0, hi - lo);
   const int kw = min(k, nw);
+  // with n > 128 and at most 16 waves, every wave but the last has a full share q
+  const int start = min(k, q) * wid;
   wave_topk_n((nw + kWave - 1) / kWave, [&](int e) { return key_at(lo + e * kWave + lane, hi); }, kw, kw == nw,
-              [&](int r, int e) {
-                const int i = lo + e * kWave + lane;
-                sm.key[wid * k + r] = order_key(sc(i));
-                sm.pos[wid * k + r] = i;
+              [&](int r, int e, uint32_t kk) {
+                sm.key[start + r] = kk;
+                sm.pos[start + r] = lo + e * kWave + lane;
               });
-  if (lane == 0) sm.cnt[wid] = kw;
   __syncthreads();
 
-  // phase 2: wave 0 selects k among the concatenated winners (ascending positions)
+  // phase 2: wave 0 selects k among the winners (ascending positions)
   if (wid == 0) {
-    int n2 = 0;
-    int start[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      start[w] = n2;
-      n2 += sm.cnt[w];
-    }
-    // LDS offset of the jj-th winner
-    auto off_of = [&](int jj) {
-      int o = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-        if (jj >= start[w]) o = w * k + (jj - start[w]);
-      return o;
-    };
+    const int n2 = min(k, q) * (NW - 1) + min(k, max(0, n - (NW - 1) * q));
     wave_topk_n((n2 + kWave - 1) / kWave,
                 [&](int e) {
                   const int jj = e * kWave + lane;
-                  const uint32_t kk = sm.key[off_of(min(jj, n2 - 1))];
+                  const uint32_t kk = sm.key[min(jj, n2 - 1)];
                   return jj < n2 ? kk : 0u;
                 },
-                k, n2 <= k, [&](int r, int e) { sel[r] = sm.pos[off_of(e * kWave + lane)]; });
+                k, n2 <= k, [&](int r, int e, uint32_t) { sel[r] = sm.pos[e * kWave + lane]; });
   }
   __syncthreads();
   return k;
