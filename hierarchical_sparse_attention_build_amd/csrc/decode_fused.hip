@@ -203,6 +203,35 @@ __device__ __forceinline__ void merge_store(const AttnMergeSmem<GQ, D, kDecWaves
   out.put<D>(hh, e % D, num / den);
 }
 
+// The same straight from the waves' raw results (attn_waves_to_lds), every
+// thread weighting the waves of its head itself: one barrier fewer.
+template <int D, int GQ>
+__device__ __forceinline__ void merge_store_waves(const AttnMergeSmem<GQ, D, kDecWaves>& mg, const PartRegs& r,
+                                                  const AttnOut& out) {
+  const int e = threadIdx.x;
+  if (e >= GQ * D) return;
+  const int hh = e / D;
+  float M = -__builtin_huge_valf();
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mg.wm[w][hh]);
+#pragma unroll
+  for (int p = 0; p <= kDecMaxForced; ++p) M = fmaxf(M, r.m[p]);
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    const float wt = mg.wm[w][hh] == -__builtin_huge_valf() ? 0.f : exp2f(mg.wm[w][hh] - M);
+    num = fmaf(wt, mg.ow[w][e], num);
+    den = fmaf(wt, mg.wl[w][hh], den);
+  }
+#pragma unroll
+  for (int p = 0; p <= kDecMaxForced; ++p) {
+    const float w = r.m[p] == -__builtin_huge_valf() ? 0.f : exp2f(r.m[p] - M);
+    num = fmaf(w, r.o[p], num);
+    den = fmaf(w, r.l[p], den);
+  }
+  out.put<D>(hh, e % D, num / den);
+}
+
 // Write this workgroup's merged waves into part slot `slot` (device-coherent
 // stores), count the arrival and return true in every thread of the last
 // arriver of the unit's F + 1 workgroups.
@@ -380,11 +409,14 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
     };
     st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
   }
-  attn_merge_waves(st, sm.mg);
+  attn_waves_to_lds(st, sm.mg);
   if (early) {
     unstash_parts<D, GQ>(sm.sc, F, pr);
-    merge_store<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
-  } else if (publish_arrive<D, GQ>(a, bh, F, sm.mg)) {
+    merge_store_waves<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
+    return;
+  }
+  attn_merge_waves_rest(sm.mg);
+  if (publish_arrive<D, GQ>(a, bh, F, sm.mg)) {
     load_parts<D, GQ>(parts, (1u << F) - 1u, pr);
     merge_store<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
   }

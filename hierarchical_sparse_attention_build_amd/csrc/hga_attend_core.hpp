@@ -527,8 +527,10 @@ struct AttnOut {
 
 // Merge the waves of the workgroup: after it, wg_value(e) is the workgroup's
 // unnormalised output element e (head e / D), sm.M / sm.L its max and sum.
+// Each wave's raw (max, sum, unnormalised output) into sm.wm / wl / ow, then a
+// barrier.
 template <typename Lane, int D, int GQ, int NWV>
-__device__ __forceinline__ void attn_merge_waves(Lane& st, AttnMergeSmem<GQ, D, NWV>& sm) {
+__device__ __forceinline__ void attn_waves_to_lds(Lane& st, AttnMergeSmem<GQ, D, NWV>& sm) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   if (lane == 0) {
@@ -540,6 +542,11 @@ __device__ __forceinline__ void attn_merge_waves(Lane& st, AttnMergeSmem<GQ, D, 
   }
   st.store_o(sm.ow[wid]);
   __syncthreads();
+}
+
+// After attn_waves_to_lds: the per-head max, sum and wave weights.
+template <int D, int GQ, int NWV>
+__device__ __forceinline__ void attn_merge_waves_rest(AttnMergeSmem<GQ, D, NWV>& sm) {
   if (static_cast<int>(threadIdx.x) < GQ) {
     const int hh = threadIdx.x;
     float M = -__builtin_huge_valf();
@@ -555,6 +562,12 @@ __device__ __forceinline__ void attn_merge_waves(Lane& st, AttnMergeSmem<GQ, D, 
     sm.L[hh] = L;
   }
   __syncthreads();
+}
+
+template <typename Lane, int D, int GQ, int NWV>
+__device__ __forceinline__ void attn_merge_waves(Lane& st, AttnMergeSmem<GQ, D, NWV>& sm) {
+  attn_waves_to_lds(st, sm);
+  attn_merge_waves_rest(sm);
 }
 
 template <int D, int GQ, int NWV>
