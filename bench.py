@@ -249,7 +249,7 @@ def main():
         "roofline": {"kernel": "decode_step_kernel<bf16,128,4>",
                      "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("decode_step"),
+                     "traffic": measured_traffic("decode_step_kernel<bf16,128,4>"),
                      "bytes_per_launch": step_bytes, "avg_us": round(step_us, 3),
                      "bytes_by_part": parts},
         "warm_cache": {"ms_per_step": round(warm_sec * 1e3, 6), "value": round(B / warm_sec, 1)},
