@@ -261,6 +261,7 @@ def main():
         out["prefill"] = bench_prefill(args, dev)
     if not args.no_secondary:
         out["decode_64k"] = bench_decode_64k(args, dev)
+        out.update(bench_reuse_and_streaming(args, dev))
         out["offload_decode_128k"] = bench_offload(args, dev)
 
     if not args.no_cpu_baseline:
@@ -423,6 +424,96 @@ def bench_decode_64k(args, dev):
             "ms_per_step": round(step_us / 1e3, 6), "query_tokens_per_s": round(B / (step_us * 1e-6), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes}}
+
+
+def bench_reuse_and_streaming(args, dev):
+    """Two variants of the decode_32k step, HIP events around graph replays over
+    4 cache replicas:
+    - route once, attend many: hga_attend over group lists routed by an earlier
+      decode step (as a layer reusing another layer's routing would), against the
+      full step; the difference is the routing share that reuse saves;
+    - streaming heads: top_k = top_g = 0, only the sink, local and current
+      chunks."""
+    import torch
+    from hierarchical_sparse_attention_build_amd import hga
+    from hierarchical_sparse_attention_build_amd import workloads as W
+    s = W.spec("decode_32k")
+    log(f"[bench] generating {s.name} (seed {s.seed}) for route reuse and streaming heads")
+    w = W.make(s)
+    B, Hq, H, d, L, C, G = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens, s.chunk_size, s.group_size
+    mk = lambda top_k, top_g: hga.params(B, Hq, H, d, C, G, s.n_sink, s.n_local, top_k, top_g, s.rope_base,
+                                         s.hf_threshold, qkv_dtype=hga.HGA_BF16, out_dtype=hga.HGA_F32)
+    p, p0 = mk(s.top_k, s.top_g), mk(0, 0)
+    Q = W.to_torch(w.Q, s.dtype).to(dev)
+    K0 = W.to_torch(w.K, s.dtype).to(dev)
+    V0 = W.to_torch(w.V, s.dtype).to(dev)
+    del w
+    nC, m, jq = L // C, C // G, (L - 1) // C
+    R = 4
+    reps = []
+    for r in range(R):
+        K = K0 if r == 0 else K0.clone()
+        V = V0 if r == 0 else V0.clone()
+        cs = torch.zeros((B, H, nC, d), device=dev)
+        gs = torch.zeros((B, H, nC * m, d), device=dev)
+        hga.build_summaries(p, K, L, 0, jq, cs, gs)
+        reps.append(dict(K=K, V=V, cs=cs, gs=gs, O=torch.empty((B, Hq, 1, d), device=dev),
+                         gi=torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device=dev),
+                         ws=hga.workspace(p, hga.OP_DECODE, 1, L, device=dev),
+                         wa=hga.workspace(p, hga.OP_ATTEND, 1, L, device=dev),
+                         w0=hga.workspace(p0, hga.OP_DECODE, 1, L, device=dev)))
+    seq = torch.full((B,), L, dtype=torch.int32, device=dev)
+    qpos = seq - 1
+
+    def full(i):
+        r = reps[i % R]
+        hga.decode(p, Q, r["K"], r["V"], L, seq, r["cs"], r["gs"], r["O"], r["ws"], group_idx=r["gi"])
+
+    def reuse(i):
+        r = reps[i % R]
+        hga.attend(p, Q, 1, qpos, r["K"], r["V"], L, r["gi"], r["O"], r["wa"])
+
+    def streaming(i):
+        r = reps[i % R]
+        hga.decode(p0, Q, r["K"], r["V"], L, seq, r["cs"], r["gs"], r["O"], r["w0"])
+
+    def timed(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                fn(i)
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, args.steps // R)
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(n_rep):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (n_rep * R)
+
+    full_us = timed(full)     # also leaves every replica's group lists in place
+    reuse_us = timed(reuse)
+    stream_us = timed(streaming)
+    log(f"[bench] decode_32k full step {full_us:.2f} us, attend over reused lists {reuse_us:.2f} us, "
+        f"streaming heads {stream_us:.2f} us")
+    del reps
+    torch.cuda.empty_cache()
+    return {"route_once_attend_many": {"workload": "decode_32k", "full_step_us": round(full_us, 3),
+                                       "attend_reused_lists_us": round(reuse_us, 3),
+                                       "share_saved": round(1 - reuse_us / full_us, 4)},
+            "streaming_heads": {"workload": "decode_32k with top_k = top_g = 0", "step_us": round(stream_us, 3),
+                                "query_tokens_per_s": round(B / (stream_us * 1e-6), 1)}}
 
 
 def bench_offload(args, dev):

@@ -38,7 +38,7 @@ struct DecodeSmem {
   int selc[kSelMaxK];           // selected chunk positions (ascending)
   int selg[kSelMaxK];           // selected group positions (ascending)
   int gl[kSelMaxK];             // routed group ids
-  int early;                    // the routing workgroup arrived early
+  int early;                    // the routing workgroup arrived early (given lists: their length)
   SelSmem<kDecThreads> sel;
   AttnMergeSmem<GQ, D, kDecWaves> mg;
   alignas(16) unsigned char ktile[kDecWaves * attn_ktile_bytes<D>()];
@@ -319,24 +319,51 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
   uint32_t* counter = a.sync + 4 * static_cast<int64_t>(bh);
   const float* ctab = a.chunk_sum + (static_cast<int64_t>(bh) * kp.n_chunks_cap + kp.n_sink) * D;
   auto crow = [&](int i) { return ctab + static_cast<int64_t>(i) * D; };
+  const bool given = a.routes_in != nullptr;  // the group list is an input (no routing)
   // ---- loads that do not depend on the position go out together with it:
   // the query rows and the first batch of candidate summaries (bounded by
   // the table, masked once the candidate count is known)
   ScanBatch<D> first;
-  scan_load<D>(0, min(kScanBatch, kp.n_chunks_cap - kp.n_sink), crow, first);
-  for (int e = tid; e < GQ * D; e += kDecThreads) sm.qs[e] = elem<T>::get(Qb, e);
-  const int t = a.seq_len[b] - 1;
+  if (!given && kp.top_k > 0) {
+    scan_load<D>(0, min(kScanBatch, kp.n_chunks_cap - kp.n_sink), crow, first);
+    for (int e = tid; e < GQ * D; e += kDecThreads) sm.qs[e] = elem<T>::get(Qb, e);
+  }
+  const int t = a.seq_len[b] + a.pos_offset;
   if (t < 0 || t >= kp.n_cap) {
     // a position outside the cache: empty index lists and NaN output
-    for (int i = tid; i < kp.top_k; i += kDecThreads) a.chunk_idx[static_cast<int64_t>(bh) * kp.top_k + i] = -1;
-    for (int i = tid; i < kp.top_g; i += kDecThreads) a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = -1;
+    if (a.chunk_idx)
+      for (int i = tid; i < kp.top_k; i += kDecThreads) a.chunk_idx[static_cast<int64_t>(bh) * kp.top_k + i] = -1;
+    if (a.group_idx)
+      for (int i = tid; i < kp.top_g; i += kDecThreads) a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = -1;
     unit_out(a, bh, GQ).put_nan<D, kDecThreads>(GQ);
     return;
   }
   const int j = t / kp.C;
+  int gcnt = 0;
+  bool early = false;
+  PartRegs pr;
+  if (given) {
+    // ---- the given list: its entries in [0, n_cap / G), in order, without holes
+    if (wid == 0) {
+      const int n_groups_cap = static_cast<int>(kp.n_cap >> kp.log2G);
+      const int32_t* gin = a.routes_in + static_cast<int64_t>(bh) * kp.top_g;
+      int base = 0;
+      for (int i0 = 0; i0 < kp.top_g; i0 += kWave) {
+        const int g = i0 + lane < kp.top_g ? gin[i0 + lane] : -1;
+        const bool ok = g >= 0 && g < n_groups_cap;
+        const uint64_t mk = __ballot(ok);
+        if (ok) sm.gl[base + bits_below(mk)] = g;
+        base += __popcll(mk);
+      }
+      if (lane == 0) sm.early = base;
+    }
+    __syncthreads();
+    gcnt = sm.early;
+  } else {
   __syncthreads();
-  // ---- level 1: score every candidate chunk, keep the top-k
-  const int nM = max(0, j - kp.n_local - kp.n_sink);
+  // ---- level 1: score every candidate chunk, keep the top-k (none to score
+  // when top_k = 0: a streaming head sees its sink and local windows only)
+  const int nM = kp.top_k > 0 ? max(0, j - kp.n_local - kp.n_sink) : 0;
   scan_scores<D, GQ, true>(sm.qs, nM, kp.inv_sqrt_d, crow, sm.sc, first);
   __syncthreads();
   const int cnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nM, kp.top_k, sm.selc, sm.sel);
@@ -364,10 +391,9 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
                      },
                      sm.sc);
   __syncthreads();
-  const bool early = sm.early != 0;
-  PartRegs pr;
+  early = sm.early != 0;
   if (early) load_parts<D, GQ>(parts, (1u << F) - 1u, pr);
-  const int gcnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nG, kp.top_g, sm.selg, sm.sel);
+  gcnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nG, kp.top_g, sm.selg, sm.sel);
   // the prefetched slots wait in LDS (the scores are no longer needed)
   if (early) stash_parts<D, GQ>(pr, sm.sc);
   for (int i = tid; i < kp.top_g; i += kDecThreads) {
@@ -380,14 +406,15 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
     a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = v;
   }
   __syncthreads();
-  // ---- attention over the routed groups' rows (all visible: routed chunks
-  // end before the local window)
+  }  // routing
+  // ---- attention over the routed groups' rows (routed chunks end before the
+  // local window, so all their rows are visible)
   AttnLaneFor<T, D, GQ> st;
   st.init([&](int hh) { return Qb + static_cast<int64_t>(hh) * D; }, lane & 15);
   st.set_tile(sm.ktile);
   const int nR = gcnt * kp.G;
   const int nblk = (nR + kAttnBlock - 1) / kAttnBlock;
-  if (kp.log2G >= 4) {
+  if (kp.log2G >= 4 && !given) {
     // groups of whole blocks: every fetched slot is a routed row, so no slot is
     // masked (and the list reads of a block have no branch around them)
     auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
@@ -398,13 +425,14 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
     };
     st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
   } else {
-    // masked slots point at the query's own row
+    // slots past the list and rows after the query are masked and point at
+    // the query's own row
     auto row = [&](int s, const T*& kr, const T*& vr) -> bool {
-      const bool ok = s < nR;
       const int64_t tok =
-          ok ? (static_cast<int64_t>(sm.gl[min(s >> kp.log2G, kSelMaxK - 1)]) << kp.log2G) + (s & (kp.G - 1)) : t;
-      kr = Kb + tok * D;
-      vr = Vb + tok * D;
+          (static_cast<int64_t>(sm.gl[min(s >> kp.log2G, kSelMaxK - 1)]) << kp.log2G) + (s & (kp.G - 1));
+      const bool ok = s < nR && tok <= t;
+      kr = Kb + (ok ? tok : t) * D;
+      vr = Vb + (ok ? tok : t) * D;
       return ok;
     };
     st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
@@ -443,7 +471,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeArgs a) 
   if (role == 0) {
     routing_role<T, D, GQ>(a, bh, sm);
   } else {
-    const int t = a.seq_len[bh / kp.Hkv] - 1;
+    const int t = a.seq_len[bh / kp.Hkv] + a.pos_offset;
     if (t < 0 || t >= kp.n_cap) return;  // NaN output written by the routing role
     forced_role<T, D, GQ>(a, bh, role - 1, t, sm);
   }

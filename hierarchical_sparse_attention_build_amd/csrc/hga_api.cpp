@@ -244,7 +244,7 @@ FullPlan plan(const KParams& kp, int op, int64_t nq) {
     f.attend = plan_attend(kp, nq, op == HGA_OP_DECODE_OFFLOAD, off);
     off += f.attend.bytes;
   }
-  if (op == HGA_OP_DECODE) {
+  if (op == HGA_OP_DECODE || (op == HGA_OP_ATTEND && nq == 1)) {
     f.fused = plan_fused(kp, off);
     off += f.fused.bytes;
   }
@@ -438,9 +438,32 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
   FullPlan f = plan(kp, HGA_OP_ATTEND, nq);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   const int n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
+  const bool bf = p->qkv_dtype == HGA_BF16;
+  if (nq == 1 && f.fused.use && !lse_out && kp.top_g > 0) {
+    // one query per sequence: the decode step's kernel with the lists given
+    // (route once, attend many: e.g. one layer's routing reused by the next)
+    const FusedPlan& fp = f.fused;
+    DecodeArgs da{};
+    da.kp = kp;
+    da.Q = Q;
+    da.seq_len = q_pos;
+    da.pos_offset = 0;
+    da.K = K;
+    da.V = V;
+    da.build_summary = 0;
+    da.routes_in = group_idx;
+    da.O = O;
+    da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
+    da.forced_wgs = fp.forced_wgs;
+    da.forced_bpw = fp.forced_bpw;
+    da.units_per_xcd = fp.units_per_xcd;
+    da.partials = at<float>(ws, fp.partials_off);
+    da.sync = at<uint32_t>(ws, fp.sync_off);
+    HGA_TRY_HIP(launch_decode_step(da, bf, static_cast<hipStream_t>(stream)), "attend (decode step)");
+    return ok();
+  }
   AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, group_idx, n_units, O, lse_out,
                              p->out_dtype == HGA_BF16);
-  const bool bf = p->qkv_dtype == HGA_BF16;
   if (prefill_mfma_supported(kp, bf, nq))
     HGA_TRY_HIP(launch_attend_prefill_mfma(a, static_cast<hipStream_t>(stream)), "attend (mfma)");
   else
@@ -537,6 +560,7 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
     da.units_per_xcd = fp.units_per_xcd;
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);
+    da.pos_offset = -1;
     HGA_TRY_HIP(launch_decode_step(da, bf, st), "decode step");
     return ok();
   }

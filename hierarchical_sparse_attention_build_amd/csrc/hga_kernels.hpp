@@ -79,7 +79,7 @@ struct AttendArgs {
 struct DecodeArgs {
   KParams kp;
   const void* Q;             // [B, Hq, 1, d]
-  const int32_t* seq_len;    // [B]: the query sits at position seq_len[b] - 1
+  const int32_t* seq_len;    // [B]: the query sits at position seq_len[b] + pos_offset
   const void* K;             // [B, Hkv, n_cap, d]
   const void* V;
   const float* chunk_sum;    // [B, Hkv, n_chunks_cap, d]
@@ -96,6 +96,9 @@ struct DecodeArgs {
   int32_t units_per_xcd;     // ceil(B*Hkv / kXcds)
   float* partials;           // ws [B*Hkv, forced_wgs + 1, gq * (d + 2)]: partial results
   uint32_t* sync;            // ws [B*Hkv, 4]: arrival counter of each unit (zero between calls)
+  const int32_t* routes_in;  // nullable [B*Hkv, top_g]: given group lists (no routing; chunk_idx,
+                             // group_idx, chunk_sum and group_sum unused)
+  int32_t pos_offset;        // the query position is seq_len[b] + pos_offset
 };
 
 struct GatherArgs {

@@ -511,6 +511,39 @@ def test_attend_masks_holes_in_group_list(hga):
     assert e <= TOL[s.dtype]
 
 
+def test_route_once_attend_many(hga):
+    """Route once, attend many: the group lists that a decode step routes for
+    one layer are reused by hga_attend for another layer (its own Q, K, V).
+    The second layer's output is the exact attention of its queries over the
+    union of its forced windows and the first layer's routed groups."""
+    s0 = W.spec("decode_32k", batch=2, n_tokens=4096)
+    s1 = W.spec("decode_32k", batch=2, n_tokens=4096, seed=s0.seed + 1)
+    say(f"[route once, attend many] seeds={s0.seed},{s1.seed}")
+    w0, w1 = W.make(s0), W.make(s1)
+    cfg = cfg_of(s1)
+    p = params_of(s0)
+    n = s0.n_tokens
+    seq = torch.from_numpy(w0.seq_len).cuda()
+    K0 = dev(w0.K, s0.dtype)
+    cs, gs = _summ_tables(s0)
+    hga.build_summaries(p, K0, n, 0, n // s0.chunk_size, cs, gs)
+    gi = torch.full((s0.batch, s0.n_kv_heads, 1, s0.top_g), -7, dtype=torch.int32, device="cuda")
+    out0 = torch.empty((s0.batch, s0.n_q_heads, 1, s0.head_dim), device="cuda")
+    hga.decode(p, dev(w0.Q, s0.dtype), K0, dev(w0.V, s0.dtype), n, seq, cs, gs, out0,
+               hga.workspace(p, hga.OP_DECODE, 1, n), group_idx=gi)
+    out1 = torch.empty_like(out0)
+    hga.attend(p, dev(w1.Q, s1.dtype), 1, seq - 1, dev(w1.K, s1.dtype), dev(w1.V, s1.dtype), n, gi, out1,
+               hga.workspace(p, hga.OP_ATTEND, 1, n))
+    torch.cuda.synchronize()
+    gin = gi.cpu().numpy()
+    assert (gin >= 0).sum() > 0
+    Oo, _ = O.attend(f64(w1.Q, s1.dtype), (w1.seq_len - 1).astype(np.int32), f64(w1.K, s1.dtype),
+                     f64(w1.V, s1.dtype), gin, cfg, s1.n_kv_heads)
+    e = max_abs(out1.cpu().numpy(), Oo)
+    say(f"  layer-1 O max-abs {e:.3e}")
+    assert e <= TOL[s1.dtype]
+
+
 def test_prefill_full_size_32k(hga):
     """The benchmarked prefill workload at full size (32K tokens, 32/8 heads),
     checked on a sample of units spread over the sequence and the heads."""
