@@ -396,6 +396,57 @@ def attend_unit_block(Q, q_pos, K, V, group_idx, cfg: HGAConfig, n_kv_heads: int
 
 
 # --------------------------------------------------------------------------- #
+# warm tier: a bounded LRU of recently routed groups
+# --------------------------------------------------------------------------- #
+def warm_lru_step(tags, stamps, clock: int, group_ids, n_groups_cap: int):
+    """One step of the warm tier of one (batch, KV head) unit.
+
+    [HGA-it, Architettura della Memoria: a bounded LRU cache in device memory
+    holds the recently routed chunks; the full K/V history lives in host
+    memory.]  Readings:
+    * the cached unit is the routed group, the unit the cold tier copies;
+    * a step's routed groups are used together (one time stamp per step);
+    * a group already cached keeps its slot (a hit; the lowest such slot);
+    * the missing groups take the least recently used slots that this step has
+      not used: smallest stamp first (an empty slot has stamp 0), the lower slot
+      on equal stamps; the j-th missing group in list order gets the j-th of
+      those slots in slot order;
+    * list entries outside [0, n_groups_cap) are ignored.
+
+    tags[s]: group held by slot s, or -1; stamps[s]: the last step that used it;
+    clock: the steps so far.  Requires len(tags) >= the number of valid
+    entries.  Returns (slot_of, misses, tags, stamps, clock) after the step:
+    slot_of[i] is the slot of entry i (-1 if ignored); misses lists the
+    (slot, group) pairs to copy in from host memory, in list order.
+    """
+    tags = [int(x) for x in tags]
+    stamps = [int(x) for x in stamps]
+    now = int(clock) + 1
+    slot_of = [-1] * len(group_ids)
+    pending = []
+    for i, g in enumerate(int(x) for x in group_ids):
+        if not 0 <= g < n_groups_cap:
+            continue
+        if g in tags:
+            s = tags.index(g)
+            slot_of[i] = s
+            stamps[s] = now
+        else:
+            pending.append((i, g))
+    # evict: the len(pending) least recently used slots not used by this step
+    order = sorted((stamps[s], s) for s in range(len(tags)) if stamps[s] != now)
+    victims = sorted(s for _, s in order[:len(pending)])
+    assert len(victims) == len(pending), "more groups than slots"
+    misses = []
+    for (i, g), s in zip(pending, victims):
+        tags[s] = g
+        stamps[s] = now
+        slot_of[i] = s
+        misses.append((s, g))
+    return slot_of, misses, tags, stamps, now
+
+
+# --------------------------------------------------------------------------- #
 # whole passes
 # --------------------------------------------------------------------------- #
 def prefill(Q, K, V, cfg: HGAConfig, n_kv_heads: int):

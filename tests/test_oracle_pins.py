@@ -379,3 +379,84 @@ def test_forced_chunks_enumeration():
     assert O.chunk_candidates(6, cf).tolist() == [2]
     assert O.chunk_candidates(5, cf).tolist() == []
     assert O.chunk_candidates(10, cf).tolist() == [2, 3, 4, 5, 6]
+
+
+# --------------------------------------------------------------------------- #
+# warm tier: bounded LRU of routed groups
+# --------------------------------------------------------------------------- #
+def _lru_run(steps, slots, n_groups_cap=1 << 20):
+    tags, stamps, clock = [-1] * slots, [0] * slots, 0
+    out = []
+    for g in steps:
+        so, mi, tags, stamps, clock = O.warm_lru_step(tags, stamps, clock, g, n_groups_cap)
+        out.append((so, mi, list(tags), list(stamps)))
+    return out
+
+
+def test_warm_lru_textbook_sequence():
+    """Two slots, one group per step, accesses 5 7 5 9: least recently used is
+    evicted, so 9 replaces 7 (a FIFO cache would replace 5)."""
+    r = _lru_run([[5], [7], [5], [9]], 2)
+    assert [m for _, m, _, _ in r] == [[(0, 5)], [(1, 7)], [], [(1, 9)]]
+    assert sorted(r[-1][2]) == [5, 9]
+    assert r[2][0] == [0]          # the hit keeps its slot
+
+
+def test_warm_lru_matches_recency_list_one_group_per_step():
+    """With one group per step every stamp is distinct, and the cached set after
+    each step is the textbook LRU set: the `slots` most recently used distinct
+    groups (kept here as a plain recency list)."""
+    rng = np.random.default_rng(11)
+    for slots in (1, 3, 8):
+        seq = rng.integers(0, 12, size=300)
+        r = _lru_run([[int(g)] for g in seq], slots)
+        recency = []
+        hits = 0
+        for g, (so, mi, tags, _) in zip(seq, r):
+            g = int(g)
+            hit = g in recency
+            hits += hit
+            if hit:
+                recency.remove(g)
+            recency.insert(0, g)
+            del recency[slots:]
+            assert (mi == []) == hit
+            assert sorted(t for t in tags if t >= 0) == sorted(recency)
+            assert tags[so[0]] == g
+        assert 0 < hits < len(seq)
+
+
+def test_warm_lru_invariants_many_groups_per_step():
+    """Several groups per step: every routed group is cached after its step, only
+    missing groups are copied (each into a slot nobody in the step uses), hits
+    keep their slots, and an evicted slot was never more recently used than a
+    slot that survives."""
+    rng = np.random.default_rng(12)
+    slots, per_step, cap = 12, 5, 40
+    tags, stamps, clock = [-1] * slots, [0] * slots, 0
+    for _ in range(400):
+        g = rng.choice(cap, per_step, replace=False).tolist()
+        g[rng.integers(per_step)] = -1 if rng.random() < 0.3 else g[0]  # holes and a repeat
+        g = [x if x != g[0] or i == 0 else -1 for i, x in enumerate(g)]   # keep entries distinct
+        before_tags, before_stamps = list(tags), list(stamps)
+        so, mi, tags, stamps, clock = O.warm_lru_step(tags, stamps, clock, g, cap)
+        valid = [x for x in g if 0 <= x < cap]
+        for i, x in enumerate(g):
+            if 0 <= x < cap:
+                assert tags[so[i]] == x and stamps[so[i]] == clock
+            else:
+                assert so[i] == -1
+        missing = [x for x in valid if x not in before_tags]
+        assert [x for _, x in mi] == missing
+        assert len({s for s, _ in mi} | {so[i] for i, x in enumerate(g) if x in before_tags and x >= 0}) == len(valid)
+        evicted = [s for s, _ in mi]
+        kept = [s for s in range(slots) if s not in evicted and stamps[s] != clock]
+        for s in evicted:
+            for k in kept:
+                assert (before_stamps[s], s) <= (before_stamps[k], k) or before_tags[s] == -1
+
+
+def test_warm_lru_ignores_out_of_range_entries():
+    so, mi, tags, stamps, clock = O.warm_lru_step([-1] * 4, [0] * 4, 0, [3, -1, 99, 2], 10)
+    assert so[1] == -1 and so[2] == -1
+    assert [g for _, g in mi] == [3, 2] and clock == 1
