@@ -574,10 +574,53 @@ def bench_offload(args, dev):
     pcie = copy_bytes / (step_us * 1e-6) / 1e9
     log(f"[bench] offload_decode_128k step {step_us:.1f} us -> {B / (step_us * 1e-6):.0f} query tokens/s, "
         f"routed groups over PCIe at {pcie:.1f} GB/s (step-inclusive)")
+
+    # warm tier: an LRU of 2 * top_g routed groups per (b, kv head) in HBM; only
+    # missing groups cross the host link.  Two query sequences: the same query
+    # every step (routed sets repeat), and a random walk of the query (each step
+    # adds N(0, 0.25^2) to every component, so routed sets drift).
+    slots = 2 * s.top_g
+    group_bytes = G * d * 2 * 2  # K and V rows of one group (bf16)
+    rng = np.random.default_rng(s.seed + 17)
+    q0 = Q.float().cpu().numpy()
+    n_w = max(5, args.steps // 10)
+    walk = [q0]
+    for _ in range(5 + n_w - 1):
+        walk.append(walk[-1] + 0.25 * rng.standard_normal(q0.shape).astype(np.float32))
+    Q_walk = [W.to_torch(W.bf16_bits(q), "bf16").to(dev) for q in walk]
+    warm_out = {"slots_per_kv_head": slots, "group_bytes": group_bytes}
+    for name, qs in (("repeat", [Q] * (5 + n_w)), ("drift", Q_walk)):
+        warm = hga.warm_state(p, slots, device=dev)
+        hits = torch.zeros((5 + n_w, B, H), dtype=torch.int32, device=dev)
+        miss = torch.zeros_like(hits)
+        wsw = hga.workspace(p, hga.OP_DECODE_OFFLOAD, 1, L, device=dev)
+
+        def wstep(i):
+            warm["hits"], warm["misses"] = hits[i], miss[i]
+            hga.decode_offload_warm(p, qs[i], K_host, V_host, K_hot, V_hot, L, seq, cs, gs, O, warm, wsw,
+                                    copy_stream=copy_stream.cuda_stream)
+
+        for i in range(5):
+            wstep(i)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for i in range(5, 5 + n_w):
+            wstep(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        w_us = e0.elapsed_time(e1) * 1e3 / n_w
+        h, mi = hits[5:].sum().item(), miss[5:].sum().item()
+        rate = h / max(1, h + mi)
+        wbytes = mi * group_bytes / n_w
+        log(f"[bench] offload_decode_128k warm tier ({name}): step {w_us:.1f} us, hit rate {rate:.3f}, "
+            f"{wbytes / 1e6:.2f} MB over the host link per step (vs {copy_bytes / 1e6:.2f} MB without)")
+        warm_out[name] = {"ms_per_step": round(w_us / 1e3, 6), "hit_rate": round(rate, 4),
+                          "host_to_hbm_bytes_per_step": int(wbytes),
+                          "pcie_gbs_step_inclusive": round(wbytes / (w_us * 1e-6) / 1e9, 2)}
     return {"workload": "offload_decode_128k", "batch": B, "context": L, "top_k": s.top_k, "top_g": s.top_g,
             "ms_per_step": round(step_us / 1e3, 6), "query_tokens_per_s": round(B / (step_us * 1e-6), 1),
             "host_to_hbm_bytes_per_step": copy_bytes, "pcie_gbs_step_inclusive": round(pcie, 2),
-            "bound": "host link (PCIe Gen5 x16, about 64 GB/s)"}
+            "bound": "host link (PCIe Gen5 x16, about 64 GB/s)", "warm_tier": warm_out}
 
 
 def cpu_baseline(s, w):

@@ -25,6 +25,7 @@ static_assert(kAttnBlock == kAttBlockRows && kAttnMaxParts == kAttMaxParts, "blo
 template <int GQ, int D>
 struct AttSmem {
   int gl[1024];
+  int sl[1024];  // staged slot of each routed entry (warm tier)
   AttnMergeSmem<GQ, D, kAttWaves> mg;
   alignas(16) unsigned char ktile[kAttWaves * attn_ktile_bytes<D>()];
 };
@@ -58,6 +59,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   // ---- routed group list of the unit (entries outside [0, n_cap/G) are masked)
   const int32_t* glg = a.group_idx + (static_cast<int64_t>(bh) * a.n_units + u) * kp.top_g;
   for (int e = tid; e < kp.top_g; e += kAttThreads) sm.gl[e] = glg[e];
+  if (a.stage_slot)
+    for (int e = tid; e < kp.top_g; e += kAttThreads)
+      sm.sl[e] = a.stage_slot[(static_cast<int64_t>(bh) * a.n_units + u) * kp.top_g + e];
 
   const T* Qb = static_cast<const T*>(a.Q);
   AttnLaneFor<T, D, GQ> st;
@@ -115,7 +119,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
     if (g < 0 || g >= n_groups_cap) return false;
     const int64_t tok = static_cast<int64_t>(g) * kp.G + (rs - e * kp.G);
     if (tok > t) return false;
-    if (staged_routed) {
+    if (staged_routed && a.stage_slot) {
+      ro = ((static_cast<int64_t>(bh) * a.stage_slots + sm.sl[e]) * kp.G + (rs - e * kp.G)) * D;
+      kr = Ks + ro;
+      vr = Vs + ro;
+    } else if (staged_routed) {
       ro = (static_cast<int64_t>(bh) * kp.top_g * kp.G + rs) * D;
       kr = Ks + ro;
       vr = Vs + ro;

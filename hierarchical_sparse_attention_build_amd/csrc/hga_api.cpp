@@ -219,10 +219,32 @@ IdxPlan plan_idx(const KParams& kp, int n_units, size_t base) {
   return r;
 }
 
+// Warm-tier lists of a cold-tier decode step: slot of each routed entry, the
+// (slot, group) pairs to copy in, their count.
+struct WarmPlan {
+  size_t slot_off, miss_off, count_off, bytes;
+};
+
+WarmPlan plan_warm(const KParams& kp, size_t base) {
+  WarmPlan r{};
+  const size_t units = static_cast<size_t>(kp.B) * kp.Hkv;
+  const size_t tg = static_cast<size_t>(std::max(1, kp.top_g));
+  size_t off = base;
+  r.slot_off = off;
+  off = align256(off + units * tg * sizeof(int32_t));
+  r.miss_off = off;
+  off = align256(off + units * tg * 2 * sizeof(int32_t));
+  r.count_off = off;
+  off = align256(off + units * sizeof(int32_t));
+  r.bytes = off - base;
+  return r;
+}
+
 struct FullPlan {
   RoutePlan route;
   AttendPlan attend;
   FusedPlan fused;
+  WarmPlan warm;
   IdxPlan idx;
   size_t bytes;
 };
@@ -247,6 +269,10 @@ FullPlan plan(const KParams& kp, int op, int64_t nq) {
   if (op == HGA_OP_DECODE || (op == HGA_OP_ATTEND && nq == 1)) {
     f.fused = plan_fused(kp, off);
     off += f.fused.bytes;
+  }
+  if (op == HGA_OP_DECODE_OFFLOAD) {
+    f.warm = plan_warm(kp, off);
+    off += f.warm.bytes;
   }
   if (needs_idx) {
     f.idx = plan_idx(kp, f.route.n_units, off);
@@ -577,11 +603,15 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
   return ok();
 }
 
-hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_host, const void* V_host,
-                              const void* K_hot, const void* V_hot, int64_t n_cap, const int32_t* seq_len,
-                              float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx,
-                              int32_t* group_idx, void* staging, size_t staging_bytes, void* ws,
-                              size_t ws_bytes, void* stream, void* copy_stream) {
+namespace {
+
+// Cold-tier decode step with either a staging buffer (every routed group copied
+// each step) or the warm tier (only the missing groups copied).
+hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K_host, const void* V_host,
+                               const void* K_hot, const void* V_hot, int64_t n_cap, const int32_t* seq_len,
+                               float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx,
+                               int32_t* group_idx, void* staging, size_t staging_bytes, const hga_warm* warm,
+                               void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
   KParams kp;
   hga_status s = build_kparams(p, n_cap, kp);
   if (s != HGA_OK) return s;
@@ -593,13 +623,33 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
   HGA_CHECK_PTR(O);
   HGA_CHECK_PTR(chunk_sum);
   HGA_CHECK_PTR(group_sum);
-  HGA_CHECK_PTR(staging);
   if (!seq_len) return fail(HGA_ERR_ARG, "seq_len is null");
   if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
   if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
-  const size_t half = static_cast<size_t>(kp.B) * kp.Hkv * std::max(1, kp.top_g) * kp.G * kp.d * elem_bytes(p);
-  if (staging_bytes < 2 * half)
-    return fail(HGA_ERR_WORKSPACE, "staging has %zu bytes, need %zu", staging_bytes, 2 * half);
+  void* Kst;
+  void* Vst;
+  if (warm) {
+    HGA_CHECK_PTR(warm->K);
+    HGA_CHECK_PTR(warm->V);
+    HGA_CHECK_PTR(warm->tags);
+    HGA_CHECK_PTR(warm->stamps);
+    HGA_CHECK_PTR(warm->clock);
+    if (warm->slots < std::max(1, kp.top_g) || warm->slots > kWarmMaxSlots)
+      return fail(HGA_ERR_ARG, "warm slots %d out of [max(1, top_g), %d]", warm->slots, kWarmMaxSlots);
+    if (kp.top_g > kWarmMaxList)
+      return fail(HGA_ERR_ARG, "top_g %d above %d with the warm tier", kp.top_g, kWarmMaxList);
+    if (!aligned16(warm->K) || !aligned16(warm->V)) return fail(HGA_ERR_ALIGN, "warm K/V not 16-byte aligned");
+    Kst = warm->K;
+    Vst = warm->V;
+  } else {
+    HGA_CHECK_PTR(staging);
+    const size_t half =
+        static_cast<size_t>(kp.B) * kp.Hkv * std::max(1, kp.top_g) * kp.G * kp.d * elem_bytes(p);
+    if (staging_bytes < 2 * half)
+      return fail(HGA_ERR_WORKSPACE, "staging has %zu bytes, need %zu", staging_bytes, 2 * half);
+    Kst = staging;
+    Vst = static_cast<char*>(staging) + half;
+  }
   FullPlan f = plan(kp, HGA_OP_DECODE_OFFLOAD, 1);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -607,8 +657,6 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
   const bool bf = p->qkv_dtype == HGA_BF16;
   int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
   int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
-  void* Kst = staging;
-  void* Vst = static_cast<char*>(staging) + half;
 
   // events ordering the copy stream between routing and the routed attention
   thread_local hipEvent_t ev_routed = nullptr, ev_copied = nullptr;
@@ -626,20 +674,45 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
   ra.chunk_sum_w = chunk_sum;
   ra.group_sum_w = group_sum;
   HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
+  WarmArgs wa{};
+  if (warm) {
+    wa.kp = kp;
+    wa.group_idx = gi;
+    wa.K_host = K_host;
+    wa.V_host = V_host;
+    wa.K = warm->K;
+    wa.V = warm->V;
+    wa.tags = warm->tags;
+    wa.stamps = warm->stamps;
+    wa.clock = warm->clock;
+    wa.hits = warm->hits;
+    wa.misses = warm->misses;
+    wa.slot_of = at<int32_t>(ws, f.warm.slot_off);
+    wa.miss_list = at<int32_t>(ws, f.warm.miss_off);
+    wa.miss_count = at<int32_t>(ws, f.warm.count_off);
+    wa.slots = warm->slots;
+    wa.elem_bytes = static_cast<int32_t>(elem_bytes(p));
+    HGA_TRY_HIP(launch_warm_lookup(wa, st), "warm lookup");
+  }
   HGA_TRY_HIP(hipEventRecord(ev_routed, st), "event record");
   HGA_TRY_HIP(hipStreamWaitEvent(cst, ev_routed, 0), "stream wait");
-  GatherArgs ga{};
-  ga.kp = kp;
-  ga.K_host = K_host;
-  ga.V_host = V_host;
-  ga.group_idx = gi;
-  ga.K_stage = Kst;
-  ga.V_stage = Vst;
-  ga.elem_bytes = static_cast<int32_t>(elem_bytes(p));
-  HGA_TRY_HIP(launch_gather_groups(ga, cst), "gather");
+  if (warm) {
+    HGA_TRY_HIP(launch_warm_fill(wa, cst), "warm fill");
+  } else {
+    GatherArgs ga{};
+    ga.kp = kp;
+    ga.K_host = K_host;
+    ga.V_host = V_host;
+    ga.group_idx = gi;
+    ga.K_stage = Kst;
+    ga.V_stage = Vst;
+    ga.elem_bytes = static_cast<int32_t>(elem_bytes(p));
+    HGA_TRY_HIP(launch_gather_groups(ga, cst), "gather");
+  }
   HGA_TRY_HIP(hipEventRecord(ev_copied, cst), "event record");
 
   // forced (hot) slots overlap the copy; routed slots read the staging buffer
+  // or the warm slots
   AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K_hot, V_hot, gi, 1, O, nullptr,
                               p->out_dtype == HGA_BF16);
   aa.kv.base = K_hot;
@@ -647,6 +720,10 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
   aa.kv.ring = 1;
   aa.K_stage = Kst;
   aa.V_stage = Vst;
+  if (warm) {
+    aa.stage_slot = wa.slot_of;
+    aa.stage_slots = warm->slots;
+  }
   aa.part = 1;
   aa.splits = f.attend.splits1;
   aa.part_offset = 0;
@@ -657,6 +734,28 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
   aa.part_offset = f.attend.splits1;
   HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend (routed)");
   return ok();
+}
+
+}  // namespace
+
+hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_host, const void* V_host,
+                              const void* K_hot, const void* V_hot, int64_t n_cap, const int32_t* seq_len,
+                              float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx,
+                              int32_t* group_idx, void* staging, size_t staging_bytes, void* ws,
+                              size_t ws_bytes, void* stream, void* copy_stream) {
+  return decode_offload_impl(p, Q, K_host, V_host, K_hot, V_hot, n_cap, seq_len, chunk_sum, group_sum, O,
+                             chunk_idx, group_idx, staging, staging_bytes, nullptr, ws, ws_bytes, stream,
+                             copy_stream);
+}
+
+hga_status hga_decode_offload_warm(const hga_params* p, const void* Q, const void* K_host, const void* V_host,
+                                   const void* K_hot, const void* V_hot, int64_t n_cap, const int32_t* seq_len,
+                                   float* chunk_sum, float* group_sum, void* O, int32_t* chunk_idx,
+                                   int32_t* group_idx, const hga_warm* warm, void* ws, size_t ws_bytes,
+                                   void* stream, void* copy_stream) {
+  if (!warm) return fail(HGA_ERR_ARG, "warm is null");
+  return decode_offload_impl(p, Q, K_host, V_host, K_hot, V_hot, n_cap, seq_len, chunk_sum, group_sum, O,
+                             chunk_idx, group_idx, nullptr, 0, warm, ws, ws_bytes, stream, copy_stream);
 }
 
 }  // extern "C"

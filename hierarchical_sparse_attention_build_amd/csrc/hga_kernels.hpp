@@ -72,6 +72,8 @@ struct AttendArgs {
   int32_t parts_total;    // partial slots per (bh, row) over all launches
   float* partials;        // ws
   uint32_t* counters;     // ws [B*Hkv*nq]
+  const int32_t* stage_slot;  // nullable [B*Hkv, top_g]: routed entry -> slot of K_stage/V_stage
+  int32_t stage_slots;        // slots per (b, kv head) of K_stage/V_stage when stage_slot is set
 };
 
 // A decode step (nq = 1) in one launch: routing and the routed rows' attention,
@@ -111,10 +113,34 @@ struct GatherArgs {
   int32_t elem_bytes;
 };
 
+// Warm tier: per (b, kv head) a bounded LRU of routed groups in device memory.
+struct WarmArgs {
+  KParams kp;
+  const int32_t* group_idx;  // [B*Hkv, top_g] this step's routed groups
+  const void* K_host;        // pinned host [B, Hkv, n_cap, d]
+  const void* V_host;
+  void* K;                   // [B*Hkv, slots, G, d] cached rows
+  void* V;
+  int32_t* tags;             // [B*Hkv, slots] group of each slot, -1 empty
+  int32_t* stamps;           // [B*Hkv, slots] last step that used each slot
+  int32_t* clock;            // [B*Hkv] steps taken
+  int32_t* hits;             // nullable [B*Hkv]
+  int32_t* misses;           // nullable [B*Hkv]
+  int32_t* slot_of;          // ws [B*Hkv, top_g]: slot of each list entry, -1 ignored
+  int32_t* miss_list;        // ws [B*Hkv, top_g, 2]: (slot, group) to copy in
+  int32_t* miss_count;       // ws [B*Hkv]
+  int32_t slots;
+  int32_t elem_bytes;
+};
+constexpr int kWarmMaxSlots = 1024;
+constexpr int kWarmMaxList = 256;   // top_g limit with the warm tier
+
 hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipStream_t st);
 hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
+hipError_t launch_warm_lookup(const WarmArgs& a, hipStream_t st);
+hipError_t launch_warm_fill(const WarmArgs& a, hipStream_t st);
 // Decode routing launch (Hq/Hkv <= 4, d in {64, 128}, candidate and index limits).
 constexpr int kXcds = 8;             // accelerator dies; workgroups are dealt to them in turn
 constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per unit

@@ -10,6 +10,9 @@
 // group ids come straight from the routing kernel's output in device memory,
 // so no host round trip is needed.  Bound by the host link, not by HBM.
 #include "hga_kernels.hpp"
+#include "hga_select.hpp"
+
+static_assert(hga::kWarmMaxList <= hga::kSelMaxK, "victim selection limit");
 
 namespace hga {
 
@@ -48,6 +51,168 @@ hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st) {
   if (a.kp.top_g <= 0) return hipSuccess;
   dim3 grid((a.kp.top_g + kGroupsPerBlock - 1) / kGroupsPerBlock, a.kp.B * a.kp.Hkv);
   gather_groups_kernel<<<grid, kGatherThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Warm tier [HGA technical summary (it), Architettura della Memoria: a bounded
+// LRU cache in device memory holds the recently routed chunks].  The cached
+// unit is the routed group.  One workgroup per (b, kv head):
+//   * a routed group already cached keeps its slot (a hit; the lowest slot
+//     holding it) and the slot's stamp is renewed to this step;
+//   * the missing groups take the least recently used slots that this step
+//     does not use: the largest keys ~stamp (an empty slot has stamp 0) by
+//     the exact ballot selection, which breaks ties towards the lower slot and
+//     emits the slots in ascending order; the j-th missing group in list order
+//     gets the j-th of them;
+//   * list entries outside [0, n_cap / G) are ignored.
+constexpr int kWarmThreads = 256;
+
+__global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
+  const KParams& kp = a.kp;
+  const int64_t bh = blockIdx.x;
+  const int S = a.slots;
+  const int TG = kp.top_g;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = wave_id();
+  const int n_groups_cap = static_cast<int>(kp.n_cap / kp.G);
+  __shared__ int tags[kWarmMaxSlots];
+  __shared__ int stamps[kWarmMaxSlots];
+  __shared__ int entry[kWarmMaxList];   // routed group of each list entry (-1 ignored)
+  __shared__ int slot[kWarmMaxList];    // its slot: >= 0 hit or assigned, -1 ignored, -2 missing
+  __shared__ int victim[kWarmMaxList];  // slots taken by the missing groups, ascending
+  __shared__ int n_hit, n_miss;
+
+  int32_t* gtags = a.tags + bh * S;
+  int32_t* gstamps = a.stamps + bh * S;
+  const int now = a.clock[bh] + 1;
+  for (int s = tid; s < S; s += kWarmThreads) {
+    tags[s] = gtags[s];
+    stamps[s] = gstamps[s];
+  }
+  for (int i = tid; i < TG; i += kWarmThreads) {
+    const int g = a.group_idx[bh * TG + i];
+    entry[i] = g >= 0 && g < n_groups_cap ? g : -1;
+  }
+  __syncthreads();
+  // ---- hits against the slots as they were before this step
+  for (int i = tid; i < TG; i += kWarmThreads) {
+    const int g = entry[i];
+    int found = -2;
+    if (g < 0) {
+      found = -1;
+    } else {
+      for (int s = 0; s < S; ++s)
+        if (tags[s] == g) {
+          found = s;
+          break;
+        }
+    }
+    slot[i] = found;
+  }
+  __syncthreads();
+  for (int i = tid; i < TG; i += kWarmThreads)
+    if (slot[i] >= 0) stamps[slot[i]] = now;
+  __syncthreads();
+  // ---- wave 0: count, then take the least recently used free slots
+  if (wid == 0) {
+    int hits = 0, misses = 0;
+    for (int i0 = 0; i0 < TG; i0 += kWave) {
+      const int i = i0 + lane;
+      const int sl = i < TG ? slot[i] : -1;
+      hits += __popcll(__ballot(sl >= 0));
+      misses += __popcll(__ballot(sl == -2));
+    }
+    if (misses > 0) {
+      // key of slot s: ~stamp, or 0 (never taken) for a slot this step uses
+      wave_topk_n((S + kWave - 1) / kWave,
+                  [&](int e) {
+                    const int s = e * kWave + lane;
+                    const int st = stamps[min(s, S - 1)];
+                    return s < S && st != now ? ~static_cast<uint32_t>(st) : 0u;
+                  },
+                  misses, false, [&](int r, int e, uint32_t) { victim[r] = e * kWave + lane; });
+    }
+    if (lane == 0) {
+      n_hit = hits;
+      n_miss = misses;
+    }
+  }
+  __syncthreads();
+  // ---- wave 0: the j-th missing entry (list order) takes victim j
+  if (wid == 0) {
+    int base = 0;
+    for (int i0 = 0; i0 < TG; i0 += kWave) {
+      const int i = i0 + lane;
+      const bool miss = i < TG && slot[i] == -2;
+      const uint64_t m = __ballot(miss);
+      if (miss) {
+        const int j = base + bits_below(m);
+        const int v = victim[j];
+        slot[i] = v;
+        tags[v] = entry[i];
+        stamps[v] = now;
+        a.miss_list[(bh * TG + j) * 2] = v;
+        a.miss_list[(bh * TG + j) * 2 + 1] = entry[i];
+      }
+      base += __popcll(m);
+    }
+  }
+  __syncthreads();
+  for (int s = tid; s < S; s += kWarmThreads) {
+    gtags[s] = tags[s];
+    gstamps[s] = stamps[s];
+  }
+  for (int i = tid; i < TG; i += kWarmThreads) a.slot_of[bh * TG + i] = slot[i];
+  if (tid == 0) {
+    a.clock[bh] = now;
+    a.miss_count[bh] = n_miss;
+    if (a.hits) a.hits[bh] = n_hit;
+    if (a.misses) a.misses[bh] = n_miss;
+  }
+}
+
+// Copy the missing groups' rows from host memory into their slots.
+__global__ __launch_bounds__(kGatherThreads) void warm_fill_kernel(WarmArgs a) {
+  const KParams& kp = a.kp;
+  const int64_t bh = blockIdx.y;
+  const int j0 = blockIdx.x * kGroupsPerBlock;
+  const int nm = a.miss_count[bh];
+  if (j0 >= nm) return;
+  const int64_t vec_per_group = static_cast<int64_t>(kp.G) * kp.d * a.elem_bytes / 16;
+  const int64_t vec_per_row = static_cast<int64_t>(kp.d) * a.elem_bytes / 16;
+  const uint4* Kh = static_cast<const uint4*>(a.K_host);
+  const uint4* Vh = static_cast<const uint4*>(a.V_host);
+  uint4* Kw = static_cast<uint4*>(a.K);
+  uint4* Vw = static_cast<uint4*>(a.V);
+  const int64_t total = kGroupsPerBlock * vec_per_group;
+  for (int64_t e = threadIdx.x; e < total; e += kGatherThreads) {
+    const int j = j0 + static_cast<int>(e / vec_per_group);
+    if (j >= nm) break;
+    const int v = a.miss_list[(bh * kp.top_g + j) * 2];
+    const int g = a.miss_list[(bh * kp.top_g + j) * 2 + 1];
+    const int64_t w = e % vec_per_group;
+    const int64_t src = (bh * kp.n_cap + static_cast<int64_t>(g) * kp.G) * vec_per_row + w;
+    const int64_t dst = (bh * a.slots + v) * vec_per_group + w;
+    const uint4 kv = Kh[src];
+    const uint4 vv = Vh[src];
+    Kw[dst] = kv;
+    Vw[dst] = vv;
+  }
+}
+
+hipError_t launch_warm_lookup(const WarmArgs& a, hipStream_t st) {
+  if (a.kp.top_g <= 0) return hipSuccess;
+  if (a.slots < a.kp.top_g || a.slots > kWarmMaxSlots || a.kp.top_g > kWarmMaxList) return hipErrorInvalidValue;
+  warm_lookup_kernel<<<a.kp.B * a.kp.Hkv, kWarmThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_warm_fill(const WarmArgs& a, hipStream_t st) {
+  if (a.kp.top_g <= 0) return hipSuccess;
+  dim3 grid((a.kp.top_g + kGroupsPerBlock - 1) / kGroupsPerBlock, a.kp.B * a.kp.Hkv);
+  warm_fill_kernel<<<grid, kGatherThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

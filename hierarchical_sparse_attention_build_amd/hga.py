@@ -20,7 +20,7 @@ STATUS = {0: "HGA_OK", -1: "HGA_ERR_ARG", -2: "HGA_ERR_SHAPE", -3: "HGA_ERR_ALIG
           -4: "HGA_ERR_WORKSPACE", -5: "HGA_ERR_UNSUPPORTED", -6: "HGA_ERR_HIP"}
 
 EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_route", "hga_attend", "hga_prefill",
-           "hga_decode", "hga_decode_offload", "hga_last_error", "hga_version")
+           "hga_decode", "hga_decode_offload", "hga_decode_offload_warm", "hga_last_error", "hga_version")
 
 
 class HGAError(RuntimeError):
@@ -35,6 +35,12 @@ class HGAParams(ctypes.Structure):
                 ("n_sink", c_int32), ("n_local", c_int32), ("top_k", c_int32), ("top_g", c_int32),
                 ("rope_base", c_double), ("hf_threshold", c_double), ("qkv_dtype", c_int32),
                 ("out_dtype", c_int32)]
+
+
+class HGAWarm(ctypes.Structure):
+    """``hga_warm``: the warm tier's device buffers (see ``warm_state``)."""
+    _fields_ = [("K", c_void_p), ("V", c_void_p), ("tags", c_void_p), ("stamps", c_void_p),
+                ("clock", c_void_p), ("hits", c_void_p), ("misses", c_void_p), ("slots", c_int32)]
 
 
 _lib = None
@@ -59,6 +65,8 @@ def lib():
             "hga_decode": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "hga_decode_offload": (i32, [P, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp, sz, vp, vp]),
+            "hga_decode_offload_warm": (i32, [P, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
+                                              ctypes.POINTER(HGAWarm), vp, sz, vp, vp]),
             "hga_last_error": (c_char_p, []),
             "hga_version": (c_char_p, []),
         }
@@ -162,6 +170,34 @@ def decode_offload(p, Q, K_host, V_host, K_hot, V_hot, n_cap, seq_len, chunk_sum
                                     _ptr(chunk_sum), _ptr(group_sum), _ptr(O), _ptr(chunk_idx),
                                     _ptr(group_idx), _ptr(staging), _nbytes(staging), _ptr(ws),
                                     _nbytes(ws), _stream(stream), c_void_p(copy_stream)))
+
+
+def warm_state(p, slots: int, device="cuda"):
+    """Fresh warm-tier buffers for ``slots`` groups per (b, kv head): K and V
+    rows, tags (-1), stamps (0), clock (0) and the per-step hit and miss counts."""
+    import torch
+    B, H, G, d = p.batch, p.n_kv_heads, p.group_size, p.head_dim
+    dt = torch.bfloat16 if p.qkv_dtype == HGA_BF16 else torch.float32
+    i32 = dict(dtype=torch.int32, device=device)
+    return {"K": torch.zeros((B, H, slots, G, d), dtype=dt, device=device),
+            "V": torch.zeros((B, H, slots, G, d), dtype=dt, device=device),
+            "tags": torch.full((B, H, slots), -1, **i32), "stamps": torch.zeros((B, H, slots), **i32),
+            "clock": torch.zeros((B, H), **i32), "hits": torch.zeros((B, H), **i32),
+            "misses": torch.zeros((B, H), **i32), "slots": slots}
+
+
+def decode_offload_warm(p, Q, K_host, V_host, K_hot, V_hot, n_cap, seq_len, chunk_sum, group_sum, O,
+                        warm, ws, chunk_idx=None, group_idx=None, stream=None, copy_stream=None):
+    """hga_decode_offload_warm; ``warm`` is a dict from ``warm_state``."""
+    if copy_stream is None:
+        raise HGAError(-1, "decode_offload_warm needs a copy stream")
+    w = HGAWarm(_ptr(warm["K"]), _ptr(warm["V"]), _ptr(warm["tags"]), _ptr(warm["stamps"]),
+                _ptr(warm["clock"]), _ptr(warm.get("hits")), _ptr(warm.get("misses")), warm["slots"])
+    _check(lib().hga_decode_offload_warm(ctypes.byref(p), _ptr(Q), _ptr(K_host), _ptr(V_host),
+                                         _ptr(K_hot), _ptr(V_hot), n_cap, _ptr(seq_len),
+                                         _ptr(chunk_sum), _ptr(group_sum), _ptr(O), _ptr(chunk_idx),
+                                         _ptr(group_idx), ctypes.byref(w), _ptr(ws), _nbytes(ws),
+                                         _stream(stream), c_void_p(copy_stream)))
 
 
 def hot_slot(c: int, n_sink: int, n_local: int) -> int:

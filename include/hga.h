@@ -167,8 +167,9 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
  * sits in slot n_sink + (c - n_sink) % (n_local + 1).  The hot windows must
  * hold the sink chunks, the n_local chunks before the current one and the
  * current chunk's tokens up to the query.  Routing runs on device-resident
- * summaries; the routed chunks are then copied from host into `staging`
- * (device, >= B*Hkv*top_k*C*d*elem bytes) by a copy kernel on `copy_stream`,
+ * summaries; the routed groups are then copied from host into `staging`
+ * (device, >= 2*B*Hkv*top_g*G*d*elem bytes: K rows, then V rows) by a copy
+ * kernel on `copy_stream`,
  * ordered after routing and before attention by events; attention reads only
  * device memory (the hot-window part of it overlaps the copy).  Like
  * hga_decode, a step whose query completes its chunk also writes that chunk's
@@ -179,6 +180,45 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
                               float* group_sum, void* O, int32_t* chunk_idx,
                               int32_t* group_idx, void* staging, size_t staging_bytes,
                               void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/* Warm tier of hga_decode_offload_warm [HGA-it, Architettura della Memoria:
+ * a bounded LRU cache in device memory holds the recently routed chunks].
+ * The cached unit is the routed group, the unit the cold tier copies.  Every
+ * buffer is device memory owned by the caller and kept from step to step:
+ *   K, V:    [B, Hkv, slots, G, d] (qkv dtype): the cached groups' rows;
+ *   tags:    [B, Hkv, slots] int32: the group each slot holds, -1 if empty;
+ *   stamps:  [B, Hkv, slots] int32: the last step that used each slot;
+ *   clock:   [B, Hkv] int32: steps taken.
+ * Before the first step tags must be all -1 and stamps and clock all 0 (K and
+ * V may hold anything).  hits, misses (nullable) [B, Hkv] int32 receive, per
+ * step, the routed groups found cached and the ones copied in from host. */
+typedef struct hga_warm {
+  void* K;
+  void* V;
+  int32_t* tags;
+  int32_t* stamps;
+  int32_t* clock;
+  int32_t* hits;
+  int32_t* misses;
+  int32_t slots;  /* slots per (b, kv head), top_g <= slots <= 1024 */
+} hga_warm;
+
+/* hga_decode_offload with the warm tier in place of the staging buffer.
+ * After routing, a lookup kernel maps each routed group of a (b, kv head) to a
+ * slot: a group already cached keeps its slot (a hit, the slot's stamp is
+ * renewed); the missing groups take the least recently used slots that this
+ * step does not use (smallest stamp first, the lower slot on equal stamps; the
+ * j-th missing group in list order gets the j-th of those slots in slot
+ * order).  Only the missing groups are copied from host memory, on
+ * `copy_stream`; attention reads the routed rows from their slots.  The
+ * output equals hga_decode_offload's.  Steps that share one `warm` must be
+ * ordered (same stream or events). */
+hga_status hga_decode_offload_warm(const hga_params* p, const void* Q, const void* K_host,
+                                   const void* V_host, const void* K_hot, const void* V_hot,
+                                   int64_t n_cap, const int32_t* seq_len, float* chunk_sum,
+                                   float* group_sum, void* O, int32_t* chunk_idx,
+                                   int32_t* group_idx, const hga_warm* warm, void* ws,
+                                   size_t ws_bytes, void* stream, void* copy_stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* hga_last_error(void);

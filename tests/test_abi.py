@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", hga.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (hga_\w+)", out))
@@ -112,3 +112,20 @@ def test_workspace_sizes_grow_with_problem(L):
     assert 0 < c < hga.workspace_size(p, hga.OP_PREFILL, 8192, 8192)
     assert hga.workspace_size(p, hga.OP_ROUTE, 1, 4096) < a
     assert hga.lib().hga_workspace_size(ctypes.byref(p), 9, 1, 4096) == 0
+
+
+def test_warm_tier_argument_errors(L):
+    """The warm-tier entry point rejects a missing state and a slot count below
+    top_g (or above the limit) before launching anything."""
+    p = good()
+    fake = 0x10000
+    P = ctypes.byref(p)
+    args = (fake, fake, fake, fake, fake, 4096, fake, fake, fake, fake, None, None)
+    assert L.hga_decode_offload_warm(P, *args, None, fake, 1 << 30, None, None) == -1
+    assert "warm" in hga.last_error()
+    for slots in (p.top_g - 1, 4096):
+        w = hga.HGAWarm(fake, fake, fake, fake, fake, None, None, slots)
+        assert L.hga_decode_offload_warm(P, *args, ctypes.byref(w), fake, 1 << 30, None, None) == -1
+        assert "slots" in hga.last_error()
+    w = hga.HGAWarm(None, fake, fake, fake, fake, None, None, p.top_g)
+    assert L.hga_decode_offload_warm(P, *args, ctypes.byref(w), fake, 1 << 30, None, None) == -1

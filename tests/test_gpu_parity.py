@@ -401,6 +401,80 @@ def test_offload_decode(hga):
     assert max_abs(cs.cpu().numpy()[:, :, j], ocs[:, :, j]) < 1e-5
 
 
+def test_offload_warm_tier_steps(hga):
+    """Warm tier over several decode steps with drifting queries: per step the
+    output equals the staging path's bit for bit, the LRU state (tags, stamps,
+    clock) and the hit and miss counts equal the oracle's LRU fed with the same
+    routed lists, and every cached slot holds its group's rows."""
+    s = W.spec("offload_decode_128k", batch=2, n_tokens=16384)
+    say(f"[offload warm tier] seed={s.seed}")
+    w = W.make(s)
+    p = params_of(s)
+    B, H, n, C, G, d = s.batch, s.n_kv_heads, s.n_tokens, s.chunk_size, s.group_size, s.head_dim
+    K_host = W.to_torch(w.K, s.dtype, pin=True)
+    V_host = W.to_torch(w.V, s.dtype, pin=True)
+    hot_chunks = s.n_sink + s.n_local + 1
+    Kt, Vt = W.to_torch(w.K, s.dtype), W.to_torch(w.V, s.dtype)
+    K_hot = torch.zeros((B, H, hot_chunks * C, d), dtype=Kt.dtype)
+    V_hot = torch.zeros_like(K_hot)
+    j = (n - 1) // C
+    for c in list(range(s.n_sink)) + list(range(j - s.n_local, j + 1)):
+        sl = hga.hot_slot(c, s.n_sink, s.n_local)
+        K_hot[:, :, sl * C:(sl + 1) * C] = Kt[:, :, c * C:(c + 1) * C]
+        V_hot[:, :, sl * C:(sl + 1) * C] = Vt[:, :, c * C:(c + 1) * C]
+    K_hot, V_hot = K_hot.cuda(), V_hot.cuda()
+    cs, gs = _summ_tables(s)
+    hga.build_summaries(p, dev(w.K, s.dtype), n, 0, j, cs, gs)
+    slots = s.top_g + 8
+    warm = hga.warm_state(p, slots)
+    ws_w = hga.workspace(p, hga.OP_DECODE_OFFLOAD, 1, n)
+    ws_s = hga.workspace(p, hga.OP_DECODE_OFFLOAD, 1, n)
+    staging = torch.empty(2 * B * H * s.top_g * G * d * 2, dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    gi = torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device="cuda")
+    out_w = torch.empty((B, s.n_q_heads, 1, d), device="cuda")
+    out_s = torch.empty_like(out_w)
+    state = {(b, h): ([-1] * slots, [0] * slots, 0) for b in range(B) for h in range(H)}
+    rng = np.random.default_rng(5)
+    Q0 = W.to_f64(w.Q, s.dtype).astype(np.float32)
+    n_groups_cap = n // G
+    tot_hits = tot_miss = 0
+    for step in range(6):
+        q = Q0 + 0.5 * rng.standard_normal(Q0.shape).astype(np.float32)
+        Qs = W.to_torch(W.bf16_bits(q), "bf16").cuda()
+        seq = torch.full((B,), n - 5 + step, dtype=torch.int32, device="cuda")  # positions inside chunk j
+        say(f"  step {step}")
+        hga.decode_offload_warm(p, Qs, K_host, V_host, K_hot, V_hot, n, seq, cs, gs, out_w, warm, ws_w,
+                                group_idx=gi, copy_stream=copy_stream.cuda_stream)
+        hga.decode_offload(p, Qs, K_host, V_host, K_hot, V_hot, n, seq, cs, gs, out_s, staging, ws_s,
+                           copy_stream=copy_stream.cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(out_w, out_s)
+        g_np = gi.cpu().numpy()
+        tags, stamps, clock = warm["tags"].cpu().numpy(), warm["stamps"].cpu().numpy(), warm["clock"].cpu().numpy()
+        hits, misses = warm["hits"].cpu().numpy(), warm["misses"].cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                t0, s0, c0 = state[(b, h)]
+                so, mi, t1, s1, c1 = O.warm_lru_step(t0, s0, c0, g_np[b, h, 0], n_groups_cap)
+                state[(b, h)] = (t1, s1, c1)
+                assert tags[b, h].tolist() == t1 and stamps[b, h].tolist() == s1 and clock[b, h] == c1
+                n_valid = sum(1 for x in g_np[b, h, 0] if 0 <= x < n_groups_cap)
+                assert misses[b, h] == len(mi) and hits[b, h] == n_valid - len(mi)
+                tot_hits += int(hits[b, h])
+                tot_miss += int(misses[b, h])
+    # every cached slot holds its group's K and V rows
+    Kw, Vw = warm["K"].cpu(), warm["V"].cpu()
+    for b in range(B):
+        for h in range(H):
+            for sl, g in enumerate(state[(b, h)][0]):
+                if g >= 0:
+                    assert torch.equal(Kw[b, h, sl], Kt[b, h, g * G:(g + 1) * G])
+                    assert torch.equal(Vw[b, h, sl], Vt[b, h, g * G:(g + 1) * G])
+    say(f"  hits {tot_hits} misses {tot_miss}")
+    assert tot_hits > 0 and tot_miss > B * H * s.top_g  # both paths taken, evictions included
+
+
 def test_nan_summaries_after_routing_leave_output_unchanged(hga):
     """No summary value enters the output: poisoning the tables after routing
     changes nothing in a second attention pass."""
