@@ -96,20 +96,19 @@ __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
     entry[i] = g >= 0 && g < n_groups_cap ? g : -1;
   }
   __syncthreads();
-  // ---- hits against the slots as they were before this step
-  for (int i = tid; i < TG; i += kWarmThreads) {
+  // ---- hits against the slots as they were before this step: one wave per
+  // entry, its lanes comparing 64 slots at a time
+  for (int i = wid; i < TG; i += kWarmThreads / kWave) {
     const int g = entry[i];
-    int found = -2;
-    if (g < 0) {
-      found = -1;
-    } else {
-      for (int s = 0; s < S; ++s)
-        if (tags[s] == g) {
-          found = s;
-          break;
-        }
+    int found = g < 0 ? -1 : -2;
+    for (int s0 = 0; s0 < S && g >= 0; s0 += kWave) {
+      const uint64_t m = __ballot(s0 + lane < S && tags[s0 + lane] == g);
+      if (m) {
+        found = s0 + __builtin_ctzll(m);
+        break;
+      }
     }
-    slot[i] = found;
+    if (lane == 0) slot[i] = found;
   }
   __syncthreads();
   for (int i = tid; i < TG; i += kWarmThreads)
