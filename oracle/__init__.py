@@ -9,5 +9,5 @@ from .hga_oracle import (  # noqa: F401
     span_summary_literal, span_summary_relative, build_summaries,
     select_top, boundary_gap, chunk_candidates, route_unit, route,
     forced_chunks, visible_tokens, softmax_attend, attend, attend_unit_block,
-    prefill, decode, dense_causal, warm_lru_step,
+    prefill, decode, dense_causal, warm_lru_step, attend_backward,
 )

@@ -395,6 +395,50 @@ def attend_unit_block(Q, q_pos, K, V, group_idx, cfg: HGAConfig, n_kv_heads: int
     return (w @ Vt) / den, (zmax + np.log(den))[..., 0]
 
 
+def attend_backward(Q, q_pos, K, V, group_idx, dO, cfg: HGAConfig, n_kv_heads: int):
+    """Gradients of ``attend``'s O with respect to Q, K and V for an upstream
+    gradient dO, with the selection held fixed.
+
+    [HGA-it, Meccanismo Core, item 4]: O is an exact softmax over the selected
+    tokens.  Reading: routing is a piecewise-constant function of Q and of the
+    summaries, so no gradient flows through it; the gradient is that of the
+    softmax attention over the fixed token set T(t) of every query row.  For one
+    row with scores z_u = q.k_u / sqrt(d), p = softmax(z), o = sum_u p_u v_u:
+        dv_u += p_u do;   dp_u = do.v_u;   dz_u = p_u (dp_u - sum_w p_w dp_w);
+        dq = sum_u dz_u k_u / sqrt(d);   dk_u += dz_u q / sqrt(d).
+    Returns dQ[B, Hq, nq, d], dK and dV[B, Hkv, n_cap, d] (float64).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, Hq, nq, d = Q.shape
+    gq = Hq // n_kv_heads
+    C = cfg.chunk_size
+    Kf = np.asarray(K, dtype=np.float64)
+    Vf = np.asarray(V, dtype=np.float64)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(Kf)
+    dV = np.zeros_like(Vf)
+    sc = 1.0 / math.sqrt(d)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // gq
+            for i in range(nq):
+                t = int(q_pos[b]) + i
+                u = 0 if nq == 1 else (t // C - int(q_pos[b]) // C)
+                toks = visible_tokens(t, group_idx[b, h, u], cfg)
+                Kt, Vt = Kf[b, h, toks], Vf[b, h, toks]
+                q, do = Q[b, hq, i], dO[b, hq, i]
+                z = (Kt @ q) * sc
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                dp = Vt @ do
+                dz = p * (dp - p @ dp)
+                dQ[b, hq, i] = (dz @ Kt) * sc
+                dK[b, h, toks] += np.outer(dz, q) * sc
+                dV[b, h, toks] += np.outer(p, do)
+    return dQ, dK, dV
+
+
 # --------------------------------------------------------------------------- #
 # warm tier: a bounded LRU of recently routed groups
 # --------------------------------------------------------------------------- #

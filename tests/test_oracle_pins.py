@@ -460,3 +460,65 @@ def test_warm_lru_ignores_out_of_range_entries():
     so, mi, tags, stamps, clock = O.warm_lru_step([-1] * 4, [0] * 4, 0, [3, -1, 99, 2], 10)
     assert so[1] == -1 and so[2] == -1
     assert [g for _, g in mi] == [3, 2] and clock == 1
+
+
+# --------------------------------------------------------------------------- #
+# backward through the selected-set attention
+# --------------------------------------------------------------------------- #
+def _bwd_case(seed=21):
+    cf = cfg(head_dim=8, chunk_size=4, group_size=2, n_sink=1, n_local=1, top_k=2, top_g=2)
+    rng = np.random.default_rng(seed)
+    B, Hq, H, n, d = 1, 2, 1, 24, 8
+    Q = rng.standard_normal((B, Hq, n, d))
+    K = rng.standard_normal((B, H, n, d))
+    V = rng.standard_normal((B, H, n, d))
+    q_pos = np.zeros(B, dtype=np.int64)
+    cs, gs = O.build_summaries(K, cf)
+    _, gi, _ = O.route(Q, q_pos, cs, gs, cf, H)
+    dO = rng.standard_normal((B, Hq, n, d))
+    return cf, Q, K, V, q_pos, gi, dO, H
+
+
+def test_attend_backward_matches_central_differences():
+    """Each gradient entry against a central difference of sum(dO * O) with the
+    routed lists held fixed (step 1e-6 in float64)."""
+    cf, Q, K, V, q_pos, gi, dO, H = _bwd_case()
+    dQ, dK, dV = O.attend_backward(Q, q_pos, K, V, gi, dO, cf, H)
+    f = lambda Q_, K_, V_: float((O.attend(Q_, q_pos, K_, V_, gi, cf, H)[0] * dO).sum())
+    rng = np.random.default_rng(1)
+    h = 1e-6
+    for X, G, k in ((Q, dQ, 0), (K, dK, 1), (V, dV, 2)):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(s)) for s in X.shape)
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args_p = [Q, K, V]
+            args_m = [Q, K, V]
+            args_p[k], args_m[k] = Xp, Xm
+            num = (f(*args_p) - f(*args_m)) / (2 * h)
+            assert abs(num - G[idx]) <= 1e-6 * max(1.0, abs(num)), (k, idx, num, G[idx])
+
+
+def test_attend_backward_matches_torch_autograd():
+    """The same gradients from torch autograd (CPU, float64) of a masked softmax
+    attention whose mask is the visible sets."""
+    cf, Q, K, V, q_pos, gi, dO, H = _bwd_case(22)
+    dQ, dK, dV = O.attend_backward(Q, q_pos, K, V, gi, dO, cf, H)
+    B, Hq, n, d = Q.shape
+    gq = Hq // H
+    mask = np.zeros((B, Hq, n, n), dtype=bool)
+    for b in range(B):
+        for hq in range(Hq):
+            for i in range(n):
+                mask[b, hq, i, O.visible_tokens(i, gi[b, hq // gq, i // cf.chunk_size], cf)] = True
+    Qt = torch.tensor(Q, requires_grad=True)
+    Kt = torch.tensor(K, requires_grad=True)
+    Vt = torch.tensor(V, requires_grad=True)
+    Ke = Kt.repeat_interleave(gq, dim=1)
+    Ve = Vt.repeat_interleave(gq, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(Qt, Ke, Ve, attn_mask=torch.tensor(mask))
+    (out * torch.tensor(dO)).sum().backward()
+    assert np.abs(Qt.grad.numpy() - dQ).max() < 1e-10
+    assert np.abs(Kt.grad.numpy() - dK).max() < 1e-10
+    assert np.abs(Vt.grad.numpy() - dV).max() < 1e-10
