@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "routed-attention query tokens/s + % HBM/MFMA roofline, 32K decode & prefill"
 
@@ -356,7 +357,42 @@ def bench_prefill(args, dev):
                       "frac": round(tf_route / MFMA_BF16_PEAK_TFLOPS, 4)},
             "summaries": {"kernel": "summaries_kernel<bf16,128>", "avg_us": round(t_sum, 2),
                           "bytes_per_launch": summ_bytes,
-                          "achieved_gbs": round(summ_bytes / (t_sum * 1e-6) / 1e9, 1)}}
+                          "achieved_gbs": round(summ_bytes / (t_sum * 1e-6) / 1e9, 1)},
+            "backward": bench_backward(s, p, Q, K, V, gi, dev)}
+
+
+def bench_backward(s, p, Q, K, V, gi, dev):
+    """hga_prefill_backward on the 32K prefill with its own routing: dQ, dK, dV
+    for a random dO.  Algorithmic work: 10*d FLOPs per (query row, visible key)
+    (scores recomputed, dP, dQ, dK, dV); fp32 on the vector ALUs."""
+    import torch
+    from hierarchical_sparse_attention_build_amd import hga
+    B, Hq, H, d, n = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens
+    g = torch.Generator(device=dev).manual_seed(s.seed + 5)
+    dO = torch.randn((B, Hq, n, d), device=dev, generator=g)
+    dQ = torch.empty((B, Hq, n, d), device=dev)
+    dK = torch.empty((B, H, n, d), device=dev)
+    dV = torch.empty_like(dK)
+    ws = hga.workspace(p, hga.OP_PREFILL_BACKWARD, n, n, device=dev)
+    run = lambda: hga.prefill_backward(p, Q, K, V, n, gi, dO, dQ, dK, dV, ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(2):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 2 * 1e3
+    fl = prefill_flops(s) // 4 * 10
+    tf = fl / (us * 1e-6) / 1e12
+    log(f"[bench] prefill backward {us / 1e3:.2f} ms: {tf:.1f} TFLOP/s = {tf / FP32_VALU_PEAK_TFLOPS:.3f} of the "
+        f"fp32 vector peak")
+    del dO, dQ, dK, dV
+    return {"workload": "prefill_32k", "ms_per_call": round(us / 1e3, 4),
+            "roofline": {"kernel": "bwd_dq_kernel<bf16,128> + bwd_dkv_kernel<bf16,128>", "bound": "alu",
+                         "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "flops_per_call": fl}}
 
 
 def bench_decode_64k(args, dev):

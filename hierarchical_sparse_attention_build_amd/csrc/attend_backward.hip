@@ -1,0 +1,308 @@
+// Backward of the prefill attention: gradients of O with respect to Q, K and V
+// over each query's selected token set, with the routing held fixed (the
+// selection is a piecewise-constant function of the inputs, so no gradient
+// flows through it).  [HGA technical summary (it), Meccanismo Core, item 4:
+// the output is an exact softmax over the selected tokens.]
+//
+// For one query row with scores z_u = q.k_u / sqrt(d) over its visible set,
+// p = softmax(z) and o = sum_u p_u v_u:
+//   D = sum_u p_u (do.v_u) (= do.o),   dz_u = p_u (do.v_u - D),
+//   dq = sum_u dz_u k_u / sqrt(d),   dk_u += dz_u q / sqrt(d),   dv_u += p_u do.
+//
+// Two gather kernels, all arithmetic in fp32 on the vector ALUs:
+//   * bwd_dq_kernel, one workgroup per (query chunk, b, kv head, query head):
+//     thread (row, quarter) holds a quarter of one query row.  A first pass
+//     over the visible tiles gets the row's softmax statistics (max, sum) and
+//     D; a second pass accumulates dq.  It also stores (log-sum-exp, D) of
+//     every row for the second kernel.
+//   * bwd_dkv_kernel, one workgroup per (key chunk, slice of query chunks,
+//     b, kv head): thread (key row, quarter) holds a quarter of one key and
+//     one value row, walks the query chunks of its slice that see the key
+//     chunk (always-visible windows, or routed groups of the chunk in the
+//     query chunk's list), and accumulates dk and dv over their query rows;
+//     the slices' sums meet in dK and dV through device-scope float atomics.
+// Dot products over a row reduce across the four quarter-threads of a quad
+// with two DPP steps.
+#include "hga_device.hpp"
+#include "hga_kernels.hpp"
+
+namespace hga {
+
+constexpr int kBwdRows = 64;                 // rows per workgroup (one chunk, C = 64)
+constexpr int kBwdThreads = kBwdRows * 4;    // a quad of threads per row
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp::movf<dpp::kQuad1032>(v);
+  v += dpp::movf<dpp::kQuad2301>(v);
+  return v;
+}
+
+template <typename T, int D>
+struct BwdTileSmem {
+  alignas(16) T k[kBwdRows * D];
+  alignas(16) T v[kBwdRows * D];
+  int tok[kBwdRows];   // token of each tile row, -1 if masked
+  int gl[1024];
+};
+
+// Token of row r of tile tt of query chunk j (-1 if masked).  Tile 0 is chunk j
+// itself, then the other always-visible chunks, then the routed groups in list
+// order, 64 / G groups per tile (the forward prefill's schedule).
+__device__ __forceinline__ int64_t bwd_tile_token(const KParams& kp, const Forced& fc, int j, const int* gl,
+                                                  int tt, int r) {
+  const int n_forced_other = fc.n - 1;
+  if (tt == 0) return static_cast<int64_t>(j) * kp.C + r;
+  if (tt <= n_forced_other) return static_cast<int64_t>(forced_chunk_at(fc, tt - 1)) * kp.C + r;
+  const int gpt = kp.C / kp.G;
+  const int rt = tt - 1 - n_forced_other;
+  const int rg = r >> kp.log2G;
+  const int e = rt * gpt + rg;
+  if (e >= kp.top_g) return -1;
+  const int g = gl[e];
+  if (g < 0 || g >= static_cast<int>(kp.n_cap >> kp.log2G)) return -1;
+  return (static_cast<int64_t>(g) << kp.log2G) + (r - (rg << kp.log2G));
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void bwd_stage_tile(const BackwardArgs& a, int64_t bh, const Forced& fc, int j, int tt,
+                                               BwdTileSmem<T, D>& sm) {
+  const KParams& kp = a.kp;
+  constexpr int PER = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte pieces per row
+  const T* Kb = static_cast<const T*>(a.K) + bh * kp.n_cap * D;
+  const T* Vb = static_cast<const T*>(a.V) + bh * kp.n_cap * D;
+  for (int e = threadIdx.x; e < kBwdRows * PER; e += kBwdThreads) {
+    const int r = e / PER, c = e % PER;
+    const int64_t tok = bwd_tile_token(kp, fc, j, sm.gl, tt, r);
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+    if (tok >= 0) {
+      kv = reinterpret_cast<const uint4*>(Kb + tok * D)[c];
+      vv = reinterpret_cast<const uint4*>(Vb + tok * D)[c];
+    }
+    reinterpret_cast<uint4*>(sm.k + r * D)[c] = kv;
+    reinterpret_cast<uint4*>(sm.v + r * D)[c] = vv;
+    if (c == 0) sm.tok[r] = static_cast<int>(tok);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
+  constexpr int QD = D / 4;
+  const KParams& kp = a.kp;
+  const int j = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int hh = blockIdx.z;
+  const int b = static_cast<int>(bh / kp.Hkv), h = static_cast<int>(bh % kp.Hkv);
+  const int r = threadIdx.x >> 2, qq = threadIdx.x & 3;
+  const int pos = j * kp.C + r;
+  const int64_t qrow = (static_cast<int64_t>(b) * kp.Hq + h * kp.gq + hh) * a.n + pos;
+  __shared__ BwdTileSmem<T, D> sm;
+
+  const int32_t* glg = a.group_idx + (bh * a.n_units + j) * kp.top_g;
+  for (int e = threadIdx.x; e < kp.top_g; e += kBwdThreads) sm.gl[e] = glg[e];
+  float q[QD], dout[QD], dq[QD];
+  load_row<T, QD>(static_cast<const T*>(a.Q) + qrow * D + qq * QD, q);
+  load_row<float, QD>(a.dO + qrow * D + qq * QD, dout);
+#pragma unroll
+  for (int i = 0; i < QD; ++i) dq[i] = 0.f;
+  __syncthreads();
+
+  const Forced fc = forced_chunks(j, kp.n_sink, kp.n_local);
+  const int n_tiles = fc.n + (kp.top_g + kp.C / kp.G - 1) / (kp.C / kp.G);
+  const float sc2 = kp.scale_log2;
+  // pass 1: max m and sum l of 2^(z log2 e), and D' = sum 2^(...) (do.v)
+  float m = -__builtin_huge_valf(), l = 0.f, dsum = 0.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    const float lse2 = m + __builtin_log2f(l);
+    const float Dv = dsum / l;
+    for (int tt = 0; tt < n_tiles; ++tt) {
+      bwd_stage_tile<T, D>(a, bh, fc, j, tt, sm);
+      __syncthreads();
+      for (int kr = 0; kr < kBwdRows; ++kr) {
+        const int tok = sm.tok[kr];
+        if (tok < 0 || tok > pos) continue;  // masked, or after the query (causal)
+        float kv[QD], vv[QD];
+        load_row<T, QD>(sm.k + kr * D + qq * QD, kv);
+        load_row<T, QD>(sm.v + kr * D + qq * QD, vv);
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int i = 0; i < QD; ++i) {
+          s = fmaf(q[i], kv[i], s);
+          dp = fmaf(dout[i], vv[i], dp);
+        }
+        s = quad_sum(s) * sc2;
+        dp = quad_sum(dp);
+        if (pass == 0) {
+          if (s > m) {
+            const float al = __builtin_amdgcn_exp2f(m - s);  // 0 while m = -inf
+            l *= al;
+            dsum *= al;
+            m = s;
+          }
+          const float e = __builtin_amdgcn_exp2f(s - m);
+          l += e;
+          dsum = fmaf(e, dp, dsum);
+        } else {
+          const float p = __builtin_amdgcn_exp2f(s - lse2);
+          const float ds = p * (dp - Dv);
+#pragma unroll
+          for (int i = 0; i < QD; ++i) dq[i] = fmaf(ds, kv[i], dq[i]);
+        }
+      }
+      __syncthreads();
+    }
+    if (pass == 1 && qq == 0) {
+      a.stats[2 * qrow] = lse2;
+      a.stats[2 * qrow + 1] = Dv;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < QD; ++i) a.dQ[qrow * D + qq * QD + i] = dq[i] * kp.inv_sqrt_d;
+}
+
+template <typename T, int D>
+struct BwdSrcSmem {
+  alignas(16) T q[kBwdRows * D];
+  alignas(16) float dout[kBwdRows * D];
+  float lse2[kBwdRows];
+  float dv[kBwdRows];
+  int vis;   // bit r/G: group of the key chunk visible to the source chunk; all bits: whole chunk
+  int causal;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
+  constexpr int QD = D / 4;
+  const KParams& kp = a.kp;
+  const int c = blockIdx.x;
+  const int s0 = blockIdx.y * a.unit_slice;
+  const int64_t bh = blockIdx.z;
+  const int b = static_cast<int>(bh / kp.Hkv), h = static_cast<int>(bh % kp.Hkv);
+  const int kr = threadIdx.x >> 2, qq = threadIdx.x & 3;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j_lo = max(s0, c), j_hi = min(s0 + a.unit_slice, a.n_units);
+  if (j_lo >= j_hi) return;  // no query chunk of this slice sees chunk c
+  __shared__ BwdSrcSmem<T, D> sm;
+
+  const int64_t ktok = static_cast<int64_t>(c) * kp.C + kr;
+  float kv[QD], vv[QD], dk[QD], dvv[QD];
+  load_row<T, QD>(static_cast<const T*>(a.K) + (bh * kp.n_cap + ktok) * D + qq * QD, kv);
+  load_row<T, QD>(static_cast<const T*>(a.V) + (bh * kp.n_cap + ktok) * D + qq * QD, vv);
+#pragma unroll
+  for (int i = 0; i < QD; ++i) dk[i] = dvv[i] = 0.f;
+  const int m = kp.C / kp.G;
+  const int all = (1 << m) - 1;
+  const int my_group = kr >> kp.log2G;
+  const float sc2 = kp.scale_log2;
+  bool any = false;
+
+  for (int j = j_lo; j < j_hi; ++j) {
+    // ---- does chunk j's query rows see chunk c, and which of its groups?
+    if (threadIdx.x < kWave) {
+      int vis = 0;
+      const bool forced = c < kp.n_sink || (c >= j - kp.n_local && c <= j);
+      if (forced) {
+        vis = all;
+      } else {
+        const int32_t* gl = a.group_idx + (bh * a.n_units + j) * kp.top_g;
+        for (int e0 = 0; e0 < kp.top_g; e0 += kWave) {
+          const int g = e0 + lane < kp.top_g ? gl[e0 + lane] : -1;
+          const bool mine = g >= 0 && g / m == c;
+          int bit = mine ? 1 << (g % m) : 0;
+          // or-reduce over the wave
+          for (int o = 32; o >= 1; o >>= 1) bit |= __shfl_xor(bit, o);
+          vis |= bit;
+        }
+      }
+      if (threadIdx.x == 0) {
+        sm.vis = vis;
+        sm.causal = c == j;
+      }
+    }
+    __syncthreads();
+    const int vis = sm.vis;
+    const bool causal = sm.causal != 0;
+    if (vis == 0) {
+      __syncthreads();
+      continue;
+    }
+    any = true;
+    const bool key_visible = (vis >> my_group) & 1;
+    for (int hh = 0; hh < kp.gq; ++hh) {
+      // ---- stage chunk j's rows of query head hh: q, do, log-sum-exp, D
+      const int64_t row0 = (static_cast<int64_t>(b) * kp.Hq + h * kp.gq + hh) * a.n + static_cast<int64_t>(j) * kp.C;
+      constexpr int QP = D * static_cast<int>(sizeof(T)) / 16;
+      for (int e = threadIdx.x; e < kBwdRows * QP; e += kBwdThreads)
+        reinterpret_cast<uint4*>(sm.q)[e] = reinterpret_cast<const uint4*>(static_cast<const T*>(a.Q) + row0 * D)[e];
+      for (int e = threadIdx.x; e < kBwdRows * D / 4; e += kBwdThreads)
+        reinterpret_cast<float4*>(sm.dout)[e] = reinterpret_cast<const float4*>(a.dO + row0 * D)[e];
+      if (threadIdx.x < kBwdRows) {
+        sm.lse2[threadIdx.x] = a.stats[2 * (row0 + threadIdx.x)];
+        sm.dv[threadIdx.x] = a.stats[2 * (row0 + threadIdx.x) + 1];
+      }
+      __syncthreads();
+      if (key_visible) {
+        const int r_end = kBwdRows;
+        for (int r = causal ? kr : 0; r < r_end; ++r) {  // causal: queries at or after the key
+          float q[QD], dout[QD];
+          load_row<T, QD>(sm.q + r * D + qq * QD, q);
+          load_row<float, QD>(sm.dout + r * D + qq * QD, dout);
+          float s = 0.f, dp = 0.f;
+#pragma unroll
+          for (int i = 0; i < QD; ++i) {
+            s = fmaf(q[i], kv[i], s);
+            dp = fmaf(dout[i], vv[i], dp);
+          }
+          s = quad_sum(s) * sc2;
+          dp = quad_sum(dp);
+          const float p = __builtin_amdgcn_exp2f(s - sm.lse2[r]);
+          const float ds = p * (dp - sm.dv[r]);
+#pragma unroll
+          for (int i = 0; i < QD; ++i) {
+            dk[i] = fmaf(ds, q[i], dk[i]);
+            dvv[i] = fmaf(p, dout[i], dvv[i]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!any) return;
+  float* dKr = a.dK + (bh * kp.n_cap + ktok) * D + qq * QD;
+  float* dVr = a.dV + (bh * kp.n_cap + ktok) * D + qq * QD;
+#pragma unroll
+  for (int i = 0; i < QD; ++i) {
+    __hip_atomic_fetch_add(dKr + i, dk[i] * kp.inv_sqrt_d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(dVr + i, dvv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ void bwd_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
+bool backward_supported(const KParams& kp) {
+  return kp.C == kBwdRows && (kp.d == 64 || kp.d == 128) && kp.log2G >= 0 && kp.top_g <= 1024;
+}
+
+template <typename T, int D>
+static hipError_t launch_t(const BackwardArgs& a, hipStream_t st) {
+  const KParams& kp = a.kp;
+  const int64_t kv_elems = static_cast<int64_t>(kp.B) * kp.Hkv * kp.n_cap * D;
+  bwd_zero_kernel<<<1024, 256, 0, st>>>(a.dK, kv_elems);
+  bwd_zero_kernel<<<1024, 256, 0, st>>>(a.dV, kv_elems);
+  bwd_dq_kernel<T, D><<<dim3(a.n_units, kp.B * kp.Hkv, kp.gq), kBwdThreads, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int slices = (a.n_units + a.unit_slice - 1) / a.unit_slice;
+  bwd_dkv_kernel<T, D><<<dim3(a.n_units, slices, kp.B * kp.Hkv), kBwdThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BackwardArgs& a, bool bf16_in, hipStream_t st) {
+  if (bf16_in) return a.kp.d == 64 ? launch_t<bf16, 64>(a, st) : launch_t<bf16, 128>(a, st);
+  return a.kp.d == 64 ? launch_t<float, 64>(a, st) : launch_t<float, 128>(a, st);
+}
+
+}  // namespace hga

@@ -385,13 +385,15 @@ const char* hga_version(void) { return "hga-mi355x 0.1 (gfx950)"; }
 size_t hga_workspace_size(const hga_params* p, int32_t op, int64_t nq, int64_t n_cap) {
   KParams kp;
   if (build_kparams(p, n_cap, kp) != HGA_OK) return 0;
-  if (op < HGA_OP_ROUTE || op > HGA_OP_DECODE_OFFLOAD) {
+  if (op < HGA_OP_ROUTE || op > HGA_OP_PREFILL_BACKWARD) {
     fail(HGA_ERR_ARG, "unknown op %d", op);
     return 0;
   }
   if (op == HGA_OP_DECODE || op == HGA_OP_DECODE_OFFLOAD) nq = 1;
   if (check_nq(kp, nq) != HGA_OK) return 0;
   ok();
+  if (op == HGA_OP_PREFILL_BACKWARD)
+    return align256(static_cast<size_t>(kp.B) * kp.Hq * nq * 2 * sizeof(float));
   return plan(kp, op, nq).bytes;
 }
 
@@ -540,6 +542,43 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
     HGA_TRY_HIP(launch_attend_prefill_mfma(aa, st), "attend (mfma)");
   else
     HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+  return ok();
+}
+
+hga_status hga_prefill_backward(const hga_params* p, const void* Q, const void* K, const void* V, int64_t n,
+                                const int32_t* group_idx, const float* dO, float* dQ, float* dK, float* dV,
+                                void* ws, size_t ws_bytes, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n, kp);
+  if (s != HGA_OK) return s;
+  if ((s = check_nq(kp, n)) != HGA_OK) return s;
+  if (n < kp.C) return fail(HGA_ERR_SHAPE, "backward needs n >= C");
+  if (!backward_supported(kp)) return fail(HGA_ERR_UNSUPPORTED, "backward needs C = 64 and d in {64, 128}");
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(K);
+  HGA_CHECK_PTR(V);
+  HGA_CHECK_PTR(dO);
+  HGA_CHECK_PTR(dQ);
+  HGA_CHECK_PTR(dK);
+  HGA_CHECK_PTR(dV);
+  if (kp.top_g > 0 && !group_idx) return fail(HGA_ERR_ARG, "group_idx is null");
+  const size_t need = align256(static_cast<size_t>(kp.B) * kp.Hq * n * 2 * sizeof(float));
+  if ((s = check_ws(ws, ws_bytes, need)) != HGA_OK) return s;
+  BackwardArgs a{};
+  a.kp = kp;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.group_idx = group_idx;
+  a.dO = dO;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.stats = static_cast<float*>(ws);
+  a.n = n;
+  a.n_units = static_cast<int32_t>(n / kp.C);
+  a.unit_slice = 64;
+  HGA_TRY_HIP(launch_backward(a, p->qkv_dtype == HGA_BF16, static_cast<hipStream_t>(stream)), "backward");
   return ok();
 }
 

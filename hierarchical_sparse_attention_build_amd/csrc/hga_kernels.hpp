@@ -113,6 +113,25 @@ struct GatherArgs {
   int32_t elem_bytes;
 };
 
+// Backward of the prefill attention over the selected sets (routing fixed).
+struct BackwardArgs {
+  KParams kp;
+  const void* Q;             // [B, Hq, n, d]
+  const void* K;             // [B, Hkv, n, d]
+  const void* V;
+  const int32_t* group_idx;  // [B*Hkv, n_units, top_g]
+  const float* dO;           // [B, Hq, n, d]
+  float* dQ;                 // [B, Hq, n, d]
+  float* dK;                 // [B, Hkv, n, d]
+  float* dV;
+  float* stats;              // ws [B, Hq, n, 2]: base-2 log-sum-exp and D of every query row
+  int64_t n;
+  int32_t n_units;           // n / C
+  int32_t unit_slice;        // query chunks per dK/dV workgroup
+};
+bool backward_supported(const KParams& kp);
+hipError_t launch_backward(const BackwardArgs& a, bool bf16_in, hipStream_t st);
+
 // Warm tier: per (b, kv head) a bounded LRU of routed groups in device memory.
 struct WarmArgs {
   KParams kp;

@@ -15,12 +15,13 @@ from ctypes import c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhga.so")
 
 HGA_BF16, HGA_F32 = 0, 1
-OP_ROUTE, OP_ATTEND, OP_PREFILL, OP_DECODE, OP_DECODE_OFFLOAD = range(5)
+OP_ROUTE, OP_ATTEND, OP_PREFILL, OP_DECODE, OP_DECODE_OFFLOAD, OP_PREFILL_BACKWARD = range(6)
 STATUS = {0: "HGA_OK", -1: "HGA_ERR_ARG", -2: "HGA_ERR_SHAPE", -3: "HGA_ERR_ALIGN",
           -4: "HGA_ERR_WORKSPACE", -5: "HGA_ERR_UNSUPPORTED", -6: "HGA_ERR_HIP"}
 
 EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_route", "hga_attend", "hga_prefill",
-           "hga_decode", "hga_decode_offload", "hga_decode_offload_warm", "hga_last_error", "hga_version")
+           "hga_prefill_backward", "hga_decode", "hga_decode_offload", "hga_decode_offload_warm",
+           "hga_last_error", "hga_version")
 
 
 class HGAError(RuntimeError):
@@ -62,6 +63,7 @@ def lib():
             "hga_route": (i32, [P, vp, i64, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
             "hga_attend": (i32, [P, vp, i64, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
             "hga_prefill": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "hga_prefill_backward": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
             "hga_decode": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "hga_decode_offload": (i32, [P, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp, sz, vp, vp]),
@@ -152,6 +154,13 @@ def prefill(p, Q, K, V, n, chunk_sum, group_sum, O, ws, chunk_idx=None, group_id
     _check(lib().hga_prefill(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), n, _ptr(chunk_sum),
                              _ptr(group_sum), _ptr(O), _ptr(chunk_idx), _ptr(group_idx),
                              _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def prefill_backward(p, Q, K, V, n, group_idx, dO, dQ, dK, dV, ws, stream=None):
+    """hga_prefill_backward: dQ, dK, dV (float32) of the prefill attention for dO."""
+    _check(lib().hga_prefill_backward(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), n, _ptr(group_idx),
+                                      _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)))
 
 
 def decode(p, Q, K, V, n_cap, seq_len, chunk_sum, group_sum, O, ws, chunk_idx=None,

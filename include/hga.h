@@ -65,7 +65,8 @@ typedef enum {
   HGA_OP_ATTEND = 1,
   HGA_OP_PREFILL = 2,
   HGA_OP_DECODE = 3,
-  HGA_OP_DECODE_OFFLOAD = 4
+  HGA_OP_DECODE_OFFLOAD = 4,
+  HGA_OP_PREFILL_BACKWARD = 5
 } hga_op;
 
 /* Method parameters.  [HGA-it, Meccanismo Core]: item 1 fixes the chunk size C
@@ -180,6 +181,22 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
                               float* group_sum, void* O, int32_t* chunk_idx,
                               int32_t* group_idx, void* staging, size_t staging_bytes,
                               void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
+/* Backward of hga_prefill's attention [HGA-it, Meccanismo Core, item 4: the
+ * output is an exact softmax over the selected tokens].  Gradients of O with
+ * respect to Q, K and V for an upstream gradient dO, with the routing held
+ * fixed: the selection is a piecewise-constant function of the inputs, so no
+ * gradient flows through it (nor into the summaries).  The visible sets are
+ * those of the forward: the sink, local and current chunks (causal) plus the
+ * groups of group_idx, as hga_prefill returned it.  Q, K, V as in
+ * hga_prefill (C = 64); dO: [B, Hq, n, d] float32; dQ: [B, Hq, n, d] float32,
+ * dK, dV: [B, Hkv, n, d] float32, all written.  Workspace:
+ * hga_workspace_size(p, HGA_OP_PREFILL_BACKWARD, n, n).  Float atomics sum
+ * the key-side partials, so dK and dV may differ in the last bits from run to
+ * run. */
+hga_status hga_prefill_backward(const hga_params* p, const void* Q, const void* K, const void* V,
+                                int64_t n, const int32_t* group_idx, const float* dO, float* dQ,
+                                float* dK, float* dV, void* ws, size_t ws_bytes, void* stream);
 
 /* Warm tier of hga_decode_offload_warm [HGA-it, Architettura della Memoria:
  * a bounded LRU cache in device memory holds the recently routed chunks].

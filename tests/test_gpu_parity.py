@@ -352,6 +352,44 @@ def _run_prefill(hga, s, w, units=None):
     return out
 
 
+@pytest.mark.parametrize("name,over", [
+    ("tiny_prefill_fp32", {"n_tokens": 512}),
+    ("prefill_32k", {"n_tokens": 512, "n_q_heads": 8, "n_kv_heads": 2}),
+    ("prefill_32k", {"n_tokens": 384, "n_q_heads": 4, "n_kv_heads": 4, "head_dim": 64, "top_g": 0,
+                     "top_k": 0}),
+])
+def test_prefill_backward(hga, name, over):
+    """dQ, dK, dV of the prefill attention against the oracle's gradients, on
+    index sets the oracle routed (given to both sides)."""
+    s = W.spec(name, **over)
+    say(f"[prefill backward] {name} {over} seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    B, H, n, d = s.batch, s.n_kv_heads, s.n_tokens, s.head_dim
+    q_pos = np.zeros(B, dtype=np.int64)
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    _, or_gi, _ = O.route(Qf, q_pos, ocs, ogs, cfg, H)
+    rng = np.random.default_rng(9)
+    dO = rng.standard_normal((B, s.n_q_heads, n, d)).astype(np.float32)
+    rdQ, rdK, rdV = O.attend_backward(Qf, q_pos, Kf, Vf, or_gi, dO.astype(np.float64), cfg, H)
+    p = params_of(s)
+    gi = torch.from_numpy(np.ascontiguousarray(or_gi if s.top_g else np.zeros((B, H, n // s.chunk_size, 1)),
+                                               dtype=np.int32)).cuda()
+    dQ = torch.empty((B, s.n_q_heads, n, d), device="cuda")
+    dK = torch.full((B, H, n, d), float("nan"), device="cuda")
+    dV = torch.full_like(dK, float("nan"))
+    ws = hga.workspace(p, hga.OP_PREFILL_BACKWARD, n, n)
+    hga.prefill_backward(p, dev(w.Q, s.dtype), dev(w.K, s.dtype), dev(w.V, s.dtype), n, gi,
+                         torch.from_numpy(dO).cuda(), dQ, dK, dV, ws)
+    torch.cuda.synchronize()
+    for nm, got, ref in (("dQ", dQ, rdQ), ("dK", dK, rdK), ("dV", dV, rdV)):
+        e = max_abs(got.cpu().numpy(), ref)
+        scale = max(1.0, float(np.abs(ref).max()))
+        say(f"  {nm} max-abs {e:.3e} (scale {scale:.2f})")
+        assert e <= 1e-4 * scale, nm
+
+
 def test_offload_decode(hga):
     """Cold tier: K/V in pinned host memory, hot windows in HBM, routed groups copied."""
     s = W.spec("offload_decode_128k", batch=2, n_tokens=16384)
