@@ -15,12 +15,14 @@
 //     over the visible tiles gets the row's softmax statistics (max, sum) and
 //     D; a second pass accumulates dq.  It also stores (log-sum-exp, D) of
 //     every row for the second kernel.
-//   * bwd_dkv_kernel, one workgroup per (key chunk, slice of query chunks,
-//     b, kv head): thread (key row, quarter) holds a quarter of one key and
-//     one value row, walks the query chunks of its slice that see the key
-//     chunk (always-visible windows, or routed groups of the chunk in the
-//     query chunk's list), and accumulates dk and dv over their query rows;
-//     the slices' sums meet in dK and dV through device-scope float atomics.
+//   * bwd_dkv_kernel, one workgroup per (block of 16 key rows, slice of query
+//     chunks, b, kv head): lane (key row, quarter) of every wave holds a
+//     quarter of one key and one value row; the workgroup walks the query
+//     chunks of its slice that see rows of the block (always-visible windows,
+//     or routed groups in the query chunk's list), each wave taking a quarter
+//     of their query rows, and accumulates dk and dv.  The waves' partials
+//     meet in LDS and the slices' sums in dK and dV through device-scope float
+//     atomics.
 // Dot products over a row reduce across the four quarter-threads of a quad
 // with two DPP steps.
 #include "hga_device.hpp"
@@ -30,6 +32,21 @@ namespace hga {
 
 constexpr int kBwdRows = 64;                 // rows per workgroup (one chunk, C = 64)
 constexpr int kBwdThreads = kBwdRows * 4;    // a quad of threads per row
+
+// Two dot products of N-element rows with four partial sums each (short
+// dependency chains).
+template <int N>
+__device__ __forceinline__ void dot2(const float (&a)[N], const float (&b)[N], const float (&c)[N],
+                                     const float (&e)[N], float& ab, float& ce) {
+  float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x[i & 3] = fmaf(a[i], b[i], x[i & 3]);
+    y[i & 3] = fmaf(c[i], e[i], y[i & 3]);
+  }
+  ab = (x[0] + x[1]) + (x[2] + x[3]);
+  ce = (y[0] + y[1]) + (y[2] + y[3]);
+}
 
 __device__ __forceinline__ float quad_sum(float v) {
   v += dpp::movf<dpp::kQuad1032>(v);
@@ -123,12 +140,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
         float kv[QD], vv[QD];
         load_row<T, QD>(sm.k + kr * D + qq * QD, kv);
         load_row<T, QD>(sm.v + kr * D + qq * QD, vv);
-        float s = 0.f, dp = 0.f;
-#pragma unroll
-        for (int i = 0; i < QD; ++i) {
-          s = fmaf(q[i], kv[i], s);
-          dp = fmaf(dout[i], vv[i], dp);
-        }
+        float s, dp;
+        dot2(q, kv, dout, vv, s, dp);
         s = quad_sum(s) * sc2;
         dp = quad_sum(dp);
         if (pass == 0) {
@@ -159,61 +172,71 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
   for (int i = 0; i < QD; ++i) a.dQ[qrow * D + qq * QD + i] = dq[i] * kp.inv_sqrt_d;
 }
 
+constexpr int kBwdKeyRows = 16;  // key rows per dK/dV workgroup
+constexpr int kBwdWaves = kBwdThreads / kWave;
+
 template <typename T, int D>
 struct BwdSrcSmem {
+  // a source chunk's query rows of one head; reused at the end for the
+  // waves' partial dK, dV (kBwdWaves - 1 of them)
   alignas(16) T q[kBwdRows * D];
   alignas(16) float dout[kBwdRows * D];
   float lse2[kBwdRows];
   float dv[kBwdRows];
-  int vis;   // bit r/G: group of the key chunk visible to the source chunk; all bits: whole chunk
-  int causal;
+  int vis;     // bit r: key row r of the block visible to the source chunk
+  int causal;  // the source chunk is the key block's own chunk
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
   constexpr int QD = D / 4;
+  static_assert((kBwdWaves - 1) * kBwdKeyRows * D * 2 * sizeof(float) <=
+                    kBwdRows * D * (sizeof(T) + sizeof(float)), "partials fit the staging area");
   const KParams& kp = a.kp;
-  const int c = blockIdx.x;
+  const int kb = blockIdx.x;                    // key block: rows [16 kb, 16 kb + 16)
+  const int c = kb * kBwdKeyRows / kp.C;        // its chunk
   const int s0 = blockIdx.y * a.unit_slice;
   const int64_t bh = blockIdx.z;
   const int b = static_cast<int>(bh / kp.Hkv), h = static_cast<int>(bh % kp.Hkv);
-  const int kr = threadIdx.x >> 2, qq = threadIdx.x & 3;
   const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  const int kr = lane >> 2, qq = lane & 3;
   const int j_lo = max(s0, c), j_hi = min(s0 + a.unit_slice, a.n_units);
-  if (j_lo >= j_hi) return;  // no query chunk of this slice sees chunk c
+  if (j_lo >= j_hi) return;  // no query chunk of this slice sees the block
   __shared__ BwdSrcSmem<T, D> sm;
 
-  const int64_t ktok = static_cast<int64_t>(c) * kp.C + kr;
+  const int64_t ktok0 = static_cast<int64_t>(kb) * kBwdKeyRows;
+  const int64_t ktok = ktok0 + kr;
   float kv[QD], vv[QD], dk[QD], dvv[QD];
   load_row<T, QD>(static_cast<const T*>(a.K) + (bh * kp.n_cap + ktok) * D + qq * QD, kv);
   load_row<T, QD>(static_cast<const T*>(a.V) + (bh * kp.n_cap + ktok) * D + qq * QD, vv);
 #pragma unroll
   for (int i = 0; i < QD; ++i) dk[i] = dvv[i] = 0.f;
-  const int m = kp.C / kp.G;
-  const int all = (1 << m) - 1;
-  const int my_group = kr >> kp.log2G;
   const float sc2 = kp.scale_log2;
   bool any = false;
 
   for (int j = j_lo; j < j_hi; ++j) {
-    // ---- does chunk j's query rows see chunk c, and which of its groups?
-    if (threadIdx.x < kWave) {
+    // ---- which rows of the block do chunk j's queries see?
+    if (wid == 0) {
       int vis = 0;
       const bool forced = c < kp.n_sink || (c >= j - kp.n_local && c <= j);
       if (forced) {
-        vis = all;
+        vis = (1 << kBwdKeyRows) - 1;
       } else {
         const int32_t* gl = a.group_idx + (bh * a.n_units + j) * kp.top_g;
         for (int e0 = 0; e0 < kp.top_g; e0 += kWave) {
           const int g = e0 + lane < kp.top_g ? gl[e0 + lane] : -1;
-          const bool mine = g >= 0 && g / m == c;
-          int bit = mine ? 1 << (g % m) : 0;
-          // or-reduce over the wave
-          for (int o = 32; o >= 1; o >>= 1) bit |= __shfl_xor(bit, o);
-          vis |= bit;
+          int bits = 0;
+          if (g >= 0) {
+            const int64_t lo = max(static_cast<int64_t>(g) << kp.log2G, ktok0);
+            const int64_t hi = min((static_cast<int64_t>(g) + 1) << kp.log2G, ktok0 + kBwdKeyRows);
+            if (lo < hi) bits = ((1 << (hi - lo)) - 1) << (lo - ktok0);
+          }
+          for (int o = 32; o >= 1; o >>= 1) bits |= __shfl_xor(bits, o);
+          vis |= bits;
         }
       }
-      if (threadIdx.x == 0) {
+      if (lane == 0) {
         sm.vis = vis;
         sm.causal = c == j;
       }
@@ -221,12 +244,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
     __syncthreads();
     const int vis = sm.vis;
     const bool causal = sm.causal != 0;
-    if (vis == 0) {
-      __syncthreads();
-      continue;
-    }
+    __syncthreads();  // every thread has read vis before wave 0 writes the next one
+    if (vis == 0) continue;
     any = true;
-    const bool key_visible = (vis >> my_group) & 1;
+    const bool key_visible = (vis >> kr) & 1;
     for (int hh = 0; hh < kp.gq; ++hh) {
       // ---- stage chunk j's rows of query head hh: q, do, log-sum-exp, D
       const int64_t row0 = (static_cast<int64_t>(b) * kp.Hq + h * kp.gq + hh) * a.n + static_cast<int64_t>(j) * kp.C;
@@ -241,17 +262,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
       }
       __syncthreads();
       if (key_visible) {
-        const int r_end = kBwdRows;
-        for (int r = causal ? kr : 0; r < r_end; ++r) {  // causal: queries at or after the key
+        // wave w takes query rows [16 w, 16 w + 16); causal: queries at or after the key
+        const int r_lo = wid * (kBwdRows / kBwdWaves);
+        const int r_hi = r_lo + kBwdRows / kBwdWaves;
+        const int first = causal ? max(r_lo, static_cast<int>(ktok - static_cast<int64_t>(j) * kp.C)) : r_lo;
+        for (int r = first; r < r_hi; ++r) {
           float q[QD], dout[QD];
           load_row<T, QD>(sm.q + r * D + qq * QD, q);
           load_row<float, QD>(sm.dout + r * D + qq * QD, dout);
-          float s = 0.f, dp = 0.f;
-#pragma unroll
-          for (int i = 0; i < QD; ++i) {
-            s = fmaf(q[i], kv[i], s);
-            dp = fmaf(dout[i], vv[i], dp);
-          }
+          float s, dp;
+          dot2(q, kv, dout, vv, s, dp);
           s = quad_sum(s) * sc2;
           dp = quad_sum(dp);
           const float p = __builtin_amdgcn_exp2f(s - sm.lse2[r]);
@@ -267,12 +287,33 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
     }
   }
   if (!any) return;
-  float* dKr = a.dK + (bh * kp.n_cap + ktok) * D + qq * QD;
-  float* dVr = a.dV + (bh * kp.n_cap + ktok) * D + qq * QD;
+  // ---- sum the waves' partials in LDS, then add the block's rows to dK, dV
+  float* red = reinterpret_cast<float*>(sm.q);  // [wave - 1][row][d][2]
+  if (wid > 0) {
+    float* mine = red + (wid - 1) * kBwdKeyRows * D * 2 + (kr * D + qq * QD) * 2;
 #pragma unroll
-  for (int i = 0; i < QD; ++i) {
-    __hip_atomic_fetch_add(dKr + i, dk[i] * kp.inv_sqrt_d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(dVr + i, dvv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < QD; ++i) {
+      mine[2 * i] = dk[i];
+      mine[2 * i + 1] = dvv[i];
+    }
+  }
+  __syncthreads();
+  if (wid == 0) {
+    for (int w = 1; w < kBwdWaves; ++w) {
+      const float* other = red + (w - 1) * kBwdKeyRows * D * 2 + (kr * D + qq * QD) * 2;
+#pragma unroll
+      for (int i = 0; i < QD; ++i) {
+        dk[i] += other[2 * i];
+        dvv[i] += other[2 * i + 1];
+      }
+    }
+    float* dKr = a.dK + (bh * kp.n_cap + ktok) * D + qq * QD;
+    float* dVr = a.dV + (bh * kp.n_cap + ktok) * D + qq * QD;
+#pragma unroll
+    for (int i = 0; i < QD; ++i) {
+      __hip_atomic_fetch_add(dKr + i, dk[i] * kp.inv_sqrt_d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(dVr + i, dvv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -296,7 +337,8 @@ static hipError_t launch_t(const BackwardArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int slices = (a.n_units + a.unit_slice - 1) / a.unit_slice;
-  bwd_dkv_kernel<T, D><<<dim3(a.n_units, slices, kp.B * kp.Hkv), kBwdThreads, 0, st>>>(a);
+  const int blocks = static_cast<int>(kp.n_cap / kBwdKeyRows);
+  bwd_dkv_kernel<T, D><<<dim3(blocks, slices, kp.B * kp.Hkv), kBwdThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
