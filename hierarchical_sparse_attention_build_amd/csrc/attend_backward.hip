@@ -33,6 +33,33 @@ namespace hga {
 constexpr int kBwdRows = 64;                 // rows per workgroup (one chunk, C = 64)
 constexpr int kBwdThreads = kBwdRows * 4;    // a quad of threads per row
 
+typedef __bf16 bwd_bf16x2 __attribute__((ext_vector_type(2)));
+
+// a.b over N/2 packed bf16 pairs on v_dot2_f32_bf16 (products exact in fp32,
+// fp32 sums), four partial sums
+template <int NW>
+__device__ __forceinline__ float dot_bf16(const uint32_t (&a)[NW], const uint32_t (&b)[NW]) {
+  float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    x[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bwd_bf16x2, a[i]), __builtin_bit_cast(bwd_bf16x2, b[i]),
+                                               x[i & 3], false);
+  return (x[0] + x[1]) + (x[2] + x[3]);
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[NW]) {
+  const uint4* s = static_cast<const uint4*>(p);
+#pragma unroll
+  for (int v = 0; v < NW / 4; ++v) {
+    const uint4 x = s[v];
+    w[4 * v] = x.x;
+    w[4 * v + 1] = x.y;
+    w[4 * v + 2] = x.z;
+    w[4 * v + 3] = x.w;
+  }
+}
+
 // Two dot products of N-element rows with four partial sums each (short
 // dependency chains).
 template <int N>
@@ -102,7 +129,7 @@ __device__ __forceinline__ void bwd_stage_tile(const BackwardArgs& a, int64_t bh
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 3) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int QD = D / 4;
   const KParams& kp = a.kp;
   const int j = blockIdx.x;
@@ -117,7 +144,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
   const int32_t* glg = a.group_idx + (bh * a.n_units + j) * kp.top_g;
   for (int e = threadIdx.x; e < kp.top_g; e += kBwdThreads) sm.gl[e] = glg[e];
   float q[QD], dout[QD], dq[QD];
-  load_row<T, QD>(static_cast<const T*>(a.Q) + qrow * D + qq * QD, q);
+  uint32_t qw[QD / 2];  // packed bf16 pairs of q (bf16 inputs)
+  if constexpr (sizeof(T) == 2) load_words(static_cast<const T*>(a.Q) + qrow * D + qq * QD, qw);
+  else load_row<T, QD>(static_cast<const T*>(a.Q) + qrow * D + qq * QD, q);
   load_row<float, QD>(a.dO + qrow * D + qq * QD, dout);
 #pragma unroll
   for (int i = 0; i < QD; ++i) dq[i] = 0.f;
@@ -138,10 +167,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BackwardArgs a) {
         const int tok = sm.tok[kr];
         if (tok < 0 || tok > pos) continue;  // masked, or after the query (causal)
         float kv[QD], vv[QD];
-        load_row<T, QD>(sm.k + kr * D + qq * QD, kv);
-        load_row<T, QD>(sm.v + kr * D + qq * QD, vv);
         float s, dp;
-        dot2(q, kv, dout, vv, s, dp);
+        if constexpr (sizeof(T) == 2) {
+          // bf16: q.k on the packed pairs; k unpacked only for dq
+          uint32_t kw[QD / 2];
+          load_words(sm.k + kr * D + qq * QD, kw);
+          s = dot_bf16(qw, kw);
+          if (pass == 1) {
+#pragma unroll
+            for (int i = 0; i < QD / 2; ++i) {
+              kv[2 * i] = bf16lo(kw[i]);
+              kv[2 * i + 1] = bf16hi(kw[i]);
+            }
+          }
+          load_row<T, QD>(sm.v + kr * D + qq * QD, vv);
+          float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < QD; ++i) y[i & 3] = fmaf(dout[i], vv[i], y[i & 3]);
+          dp = (y[0] + y[1]) + (y[2] + y[3]);
+        } else {
+          load_row<T, QD>(sm.k + kr * D + qq * QD, kv);
+          load_row<T, QD>(sm.v + kr * D + qq * QD, vv);
+          dot2(q, kv, dout, vv, s, dp);
+        }
         s = quad_sum(s) * sc2;
         dp = quad_sum(dp);
         if (pass == 0) {
