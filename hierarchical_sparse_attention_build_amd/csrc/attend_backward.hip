@@ -236,7 +236,7 @@ struct BwdSrcSmem {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 3) void bwd_dkv_kernel(BackwardArgs a) {
   constexpr int QD = D / 4;
   static_assert((kBwdWaves - 1) * kBwdKeyRows * D * 2 * sizeof(float) <=
                     kBwdRows * D * (sizeof(T) + sizeof(float)), "partials fit the staging area");
@@ -256,7 +256,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
   const int64_t ktok0 = static_cast<int64_t>(kb) * kBwdKeyRows;
   const int64_t ktok = ktok0 + kr;
   float kv[QD], vv[QD], dk[QD], dvv[QD];
-  load_row<T, QD>(static_cast<const T*>(a.K) + (bh * kp.n_cap + ktok) * D + qq * QD, kv);
+  uint32_t kw[QD / 2];  // packed bf16 pairs of k (bf16 inputs)
+  if constexpr (sizeof(T) == 2) load_words(static_cast<const T*>(a.K) + (bh * kp.n_cap + ktok) * D + qq * QD, kw);
+  else load_row<T, QD>(static_cast<const T*>(a.K) + (bh * kp.n_cap + ktok) * D + qq * QD, kv);
   load_row<T, QD>(static_cast<const T*>(a.V) + (bh * kp.n_cap + ktok) * D + qq * QD, vv);
 #pragma unroll
   for (int i = 0; i < QD; ++i) dk[i] = dvv[i] = 0.f;
@@ -316,10 +318,26 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BackwardArgs a) {
         const int first = causal ? max(r_lo, static_cast<int>(ktok - static_cast<int64_t>(j) * kp.C)) : r_lo;
         for (int r = first; r < r_hi; ++r) {
           float q[QD], dout[QD];
-          load_row<T, QD>(sm.q + r * D + qq * QD, q);
-          load_row<float, QD>(sm.dout + r * D + qq * QD, dout);
           float s, dp;
-          dot2(q, kv, dout, vv, s, dp);
+          if constexpr (sizeof(T) == 2) {
+            uint32_t qw[QD / 2];
+            load_words(sm.q + r * D + qq * QD, qw);
+            s = dot_bf16(qw, kw);
+#pragma unroll
+            for (int i = 0; i < QD / 2; ++i) {
+              q[2 * i] = bf16lo(qw[i]);
+              q[2 * i + 1] = bf16hi(qw[i]);
+            }
+            load_row<float, QD>(sm.dout + r * D + qq * QD, dout);
+            float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < QD; ++i) y[i & 3] = fmaf(dout[i], vv[i], y[i & 3]);
+            dp = (y[0] + y[1]) + (y[2] + y[3]);
+          } else {
+            load_row<T, QD>(sm.q + r * D + qq * QD, q);
+            load_row<float, QD>(sm.dout + r * D + qq * QD, dout);
+            dot2(q, kv, dout, vv, s, dp);
+          }
           s = quad_sum(s) * sc2;
           dp = quad_sum(dp);
           const float p = __builtin_amdgcn_exp2f(s - sm.lse2[r]);
