@@ -140,10 +140,11 @@ RoutePlan plan_route(const KParams& kp, int64_t nq, size_t base) {
 
 struct AttendPlan {
   int splits1, splits2, tps, parts_total;  // splits2 > 0 only for the two-part (offload) schedule
-  size_t counters_off, partials_off, bytes;
+  size_t counters_off, partials_off, v16_off, bytes;
+  bool v16;  // the pipelined prefill kernel runs (V16 region present)
 };
 
-AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base) {
+AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, bool bf16_in, size_t base) {
   AttendPlan a{};
   const int64_t rows = static_cast<int64_t>(kp.B) * kp.Hkv * nq;
   const int max_blocks = static_cast<int>(cdiv(attend_max_slots(kp), kAttBlockRows));
@@ -169,6 +170,9 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, size_t base
   a.partials_off = off;
   if (a.parts_total > 1)
     off = align256(off + static_cast<size_t>(rows) * a.parts_total * kp.gq * (kp.d + 2) * sizeof(float));
+  a.v16 = !two_part && prefill_pipe_supported(kp, bf16_in, nq);
+  a.v16_off = off;
+  if (a.v16) off = align256(off + prefill_pipe_v16_bytes(kp));
   a.bytes = off - base;
   return a;
 }
@@ -249,7 +253,7 @@ struct FullPlan {
   size_t bytes;
 };
 
-FullPlan plan(const KParams& kp, int op, int64_t nq) {
+FullPlan plan(const KParams& kp, int op, int64_t nq, bool bf16_in) {
   FullPlan f{};
   size_t off = 0;
   const bool needs_route = op == HGA_OP_ROUTE || op == HGA_OP_PREFILL || op == HGA_OP_DECODE ||
@@ -263,7 +267,7 @@ FullPlan plan(const KParams& kp, int op, int64_t nq) {
     off += f.route.bytes;
   }
   if (needs_attend) {
-    f.attend = plan_attend(kp, nq, op == HGA_OP_DECODE_OFFLOAD, off);
+    f.attend = plan_attend(kp, nq, op == HGA_OP_DECODE_OFFLOAD, bf16_in, off);
     off += f.attend.bytes;
   }
   if (op == HGA_OP_DECODE || (op == HGA_OP_ATTEND && nq == 1)) {
@@ -358,6 +362,7 @@ AttendArgs attend_args(const KParams& kp, const FullPlan& f, void* ws, const voi
   a.parts_total = f.attend.parts_total;
   a.partials = at<float>(ws, f.attend.partials_off);
   a.counters = at<uint32_t>(ws, f.attend.counters_off);
+  a.V16 = f.attend.v16 ? at<void>(ws, f.attend.v16_off) : nullptr;
   return a;
 }
 
@@ -394,7 +399,7 @@ size_t hga_workspace_size(const hga_params* p, int32_t op, int64_t nq, int64_t n
   ok();
   if (op == HGA_OP_PREFILL_BACKWARD)
     return align256(static_cast<size_t>(kp.B) * kp.Hq * nq * 2 * sizeof(float));
-  return plan(kp, op, nq).bytes;
+  return plan(kp, op, nq, p->qkv_dtype == HGA_BF16).bytes;
 }
 
 hga_status hga_build_summaries(const hga_params* p, const void* K, int64_t n_cap, int32_t chunk_begin,
@@ -438,7 +443,7 @@ hga_status hga_route(const hga_params* p, const void* Q, int64_t nq, const int32
   HGA_CHECK_PTR(group_idx);
   if (!q_pos) return fail(HGA_ERR_ARG, "q_pos is null");
   if (scores_out && nq != 1) return fail(HGA_ERR_ARG, "scores_out is for decode (nq == 1) only");
-  FullPlan f = plan(kp, HGA_OP_ROUTE, nq);
+  FullPlan f = plan(kp, HGA_OP_ROUTE, nq, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   RouteArgs a = route_args(kp, f, ws, Q, nq, q_pos, 0, chunk_sum, group_sum, chunk_idx, group_idx, scores_out);
   const bool bf = p->qkv_dtype == HGA_BF16;
@@ -463,7 +468,7 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
   if (kp.top_g > 0 && !group_idx) return fail(HGA_ERR_ARG, "group_idx is null");
   if (!q_pos) return fail(HGA_ERR_ARG, "q_pos is null");
   if (lse_out && !aligned16(lse_out)) return fail(HGA_ERR_ALIGN, "lse_out not 16-byte aligned");
-  FullPlan f = plan(kp, HGA_OP_ATTEND, nq);
+  FullPlan f = plan(kp, HGA_OP_ATTEND, nq, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   const int n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
   const bool bf = p->qkv_dtype == HGA_BF16;
@@ -492,7 +497,9 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
   }
   AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, group_idx, n_units, O, lse_out,
                              p->out_dtype == HGA_BF16);
-  if (prefill_mfma_supported(kp, bf, nq))
+  if (a.V16)
+    HGA_TRY_HIP(launch_attend_prefill_pipe(a, static_cast<hipStream_t>(stream)), "attend (mfma, pipelined)");
+  else if (prefill_mfma_supported(kp, bf, nq))
     HGA_TRY_HIP(launch_attend_prefill_mfma(a, static_cast<hipStream_t>(stream)), "attend (mfma)");
   else
     HGA_TRY_HIP(launch_attend_splitk(a, bf, static_cast<hipStream_t>(stream)), "attend");
@@ -515,7 +522,7 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
   HGA_CHECK_PTR(group_sum);
   if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
   if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
-  FullPlan f = plan(kp, HGA_OP_PREFILL, n);
+  FullPlan f = plan(kp, HGA_OP_PREFILL, n, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = p->qkv_dtype == HGA_BF16;
@@ -538,7 +545,9 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
     HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
   AttendArgs aa = attend_args(kp, f, ws, Q, n, nullptr, 0, K, V, gi, f.route.n_units, O, nullptr,
                               p->out_dtype == HGA_BF16);
-  if (prefill_mfma_supported(kp, bf, n))
+  if (aa.V16)
+    HGA_TRY_HIP(launch_attend_prefill_pipe(aa, st), "attend (mfma, pipelined)");
+  else if (prefill_mfma_supported(kp, bf, n))
     HGA_TRY_HIP(launch_attend_prefill_mfma(aa, st), "attend (mfma)");
   else
     HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
@@ -597,7 +606,7 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
   if (!seq_len) return fail(HGA_ERR_ARG, "seq_len is null");
   if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
   if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
-  FullPlan f = plan(kp, HGA_OP_DECODE, 1);
+  FullPlan f = plan(kp, HGA_OP_DECODE, 1, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = p->qkv_dtype == HGA_BF16;
@@ -689,7 +698,7 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
     Kst = staging;
     Vst = static_cast<char*>(staging) + half;
   }
-  FullPlan f = plan(kp, HGA_OP_DECODE_OFFLOAD, 1);
+  FullPlan f = plan(kp, HGA_OP_DECODE_OFFLOAD, 1, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipStream_t cst = static_cast<hipStream_t>(copy_stream);

@@ -74,6 +74,7 @@ struct AttendArgs {
   uint32_t* counters;     // ws [B*Hkv*nq]
   const int32_t* stage_slot;  // nullable [B*Hkv, top_g]: routed entry -> slot of K_stage/V_stage
   int32_t stage_slots;        // slots per (b, kv head) of K_stage/V_stage when stage_slot is set
+  void* V16;                  // ws, pipelined prefill only: V as fp16 blocks of 16 keys [B*Hkv, n_cap, d]
 };
 
 // A decode step (nq = 1) in one launch: routing and the routed rows' attention,
@@ -169,6 +170,11 @@ hipError_t launch_decode_step(const DecodeArgs& a, bool bf16_in, hipStream_t st)
 // Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
 bool prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_attend_prefill_mfma(const AttendArgs& a, hipStream_t st);
+// pipelined MFMA prefill attention (groups of whole 16-key blocks); needs the
+// V16 region of prefill_pipe_v16_bytes in the workspace
+bool prefill_pipe_supported(const KParams& kp, bool bf16_in, int64_t nq);
+size_t prefill_pipe_v16_bytes(const KParams& kp);
+hipError_t launch_attend_prefill_pipe(const AttendArgs& a, hipStream_t st);
 // Prefill routing on the matrix cores (bf16, C = 64, Hq/Hkv <= 4).
 bool route_prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_route_prefill_mfma(const RouteArgs& a, hipStream_t st);

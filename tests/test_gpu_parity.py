@@ -318,6 +318,59 @@ def test_prefill_bf16(hga, over):
     _run_prefill(hga, s, w)
 
 
+@pytest.mark.parametrize("over", [
+    {},                                                # 4 query heads per KV head, G = 16
+    {"n_q_heads": 16, "head_dim": 64},                 # 2 per KV head, d = 64
+    {"n_q_heads": 8, "group_size": 32, "top_g": 12},   # 1 per KV head, groups of two 16-key blocks
+    {"group_size": 64, "top_g": 5},                    # whole-chunk groups, a partly filled last tile
+    {"group_size": 8, "top_g": 24},                    # groups of 8 keys
+])
+def test_prefill_attend_given_lists(hga, over):
+    """hga_attend for a block of prefill queries appended at a position offset
+    (chunked prefill), with given group lists that have holes (-1 entries),
+    against the oracle's unit blocks: O and the log-sum-exp of every row."""
+    s = W.spec("prefill_32k", batch=2, n_tokens=2048, **over)
+    say(f"[prefill attend, given lists] {over} seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    B, Hq, H, d, n, C = s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.n_tokens, s.chunk_size
+    m = C // s.group_size
+    nq = 512
+    nU = nq // C
+    q_pos = np.array([1024, 1536], dtype=np.int64)
+    Qs = np.stack([w.Q[b, :, q_pos[b]:q_pos[b] + nq] for b in range(B)])
+    rng = np.random.default_rng(11)
+    gi = np.full((B, H, nU, s.top_g), -1, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for u in range(nU):
+                j = int(q_pos[b]) // C + u
+                pool = np.arange(s.n_sink * m, max(s.n_sink, j - s.n_local) * m)
+                pick = np.sort(rng.choice(pool, min(s.top_g, len(pool)), replace=False))
+                pick = np.where(rng.random(len(pick)) < 0.7, pick, -1)
+                gi[b, h, u, :len(pick)] = pick
+    p = params_of(s)
+    out = torch.empty((B, Hq, nq, d), device="cuda")
+    lse = torch.empty((B, Hq, nq), device="cuda")
+    ws = hga.workspace(p, hga.OP_ATTEND, nq, n)
+    hga.attend(p, dev(Qs, s.dtype), nq, torch.from_numpy(q_pos.astype(np.int32)).cuda(), dev(w.K, s.dtype),
+               dev(w.V, s.dtype), n, torch.from_numpy(gi).cuda(), out, ws, lse_out=lse)
+    torch.cuda.synchronize()
+    Qf, Kf, Vf = f64(Qs, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
+    got, got_lse = out.cpu().numpy(), lse.cpu().numpy()
+    gq = Hq // H
+    eo = el = 0.0
+    for b in range(B):
+        for h in range(H):
+            for u in range(nU):
+                o, l = O.attend_unit_block(Qf, q_pos, Kf, Vf, gi, cfg, H, b, h, u)
+                rows = slice(u * C, (u + 1) * C)
+                eo = max(eo, max_abs(got[b, h * gq:(h + 1) * gq, rows], o))
+                el = max(el, max_abs(got_lse[b, h * gq:(h + 1) * gq, rows], l))
+    say(f"  O max-abs {eo:.3e}  lse max-abs {el:.3e}")
+    assert eo <= TOL[s.dtype] and el <= TOL[s.dtype]
+
+
 def _run_prefill(hga, s, w, units=None):
     cfg = cfg_of(s)
     Qf, Kf, Vf = f64(w.Q, s.dtype), f64(w.K, s.dtype), f64(w.V, s.dtype)
