@@ -110,7 +110,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the 64K decode and the 128K cold-tier decode figures")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -323,7 +323,8 @@ def bench_prefill(args, dev):
     qpos = torch.zeros(B, dtype=torch.int32, device=dev)
 
     def timed(fn, reps):
-        fn()
+        for _ in range(3):  # warm-up: clocks and caches settle
+            fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()

@@ -262,17 +262,18 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
   // O^T += V^T P^T for sub-block sb of the V tile vs; pk[t] = P^T of its k-step t
+  // (all eight V fragments are read before the first MFMA)
   auto pv = [&](const unsigned char* vs, int sb, const f16x8_t (&pk)[2]) {
+    f16x8_t vf[2][DBLK];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const unsigned char* blk = vs + (2 * sb + t) * VB;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int d = 32 * db + ql;
-        const f16x8_t va = *reinterpret_cast<const f16x8_t*>(blk + vblock_off(d, hb));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pk[t], o[db], 0, 0, 0);
-      }
-    }
+      for (int db = 0; db < DBLK; ++db)
+        vf[t][db] = *reinterpret_cast<const f16x8_t*>(vs + (2 * sb + t) * VB + vblock_off(32 * db + ql, hb));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[t][db], pk[t], o[db], 0, 0, 0);
   };
   // masked scores (-inf) of sub-block sb of tile tt
   auto mask = [&](f32x16_t& s, int tt, int sb) {
@@ -308,14 +309,14 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   const int nsb = 2 * n_tiles;
   const f16x2_t ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
-  // One 32-key sub-block bsb: S of the next one (K tile kn), P.V of the
-  // previous one (V tile vp), P of this one.  The last sub-block's "next"
+  // One 32-key sub-block bsb: P.V of the previous one (V tile vp), S of the
+  // next one (K tile kn), P of this one.  The last sub-block's "next"
   // scores read whatever the slot holds and are dropped; the first P.V has
   // P = 0 over the zeroed slot.
   auto sub = [&](int bsb, const unsigned char* kn, const unsigned char* vp) __attribute__((always_inline)) {
     const bool has_next = bsb + 1 < nsb;
-    f32x16_t s_nxt = qk(kn, (bsb + 1) & 1);
     pv(vp, (bsb + 1) & 1, pk_prev);
+    f32x16_t s_nxt = qk(kn, (bsb + 1) & 1);
     f16x8_t pk_cur[2];
     float rs = 0.f;
 #pragma unroll
