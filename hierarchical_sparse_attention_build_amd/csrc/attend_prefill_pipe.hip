@@ -16,8 +16,9 @@
 // positions).  Keys come in tiles of 64 (the current chunk (causal), the other
 // forced chunks, then the routed groups), loaded into registers one tile
 // ahead and stored into a ring of three LDS tiles, one barrier per tile.  K
-// rows keep their bf16 layout with the 16-byte pieces of row r XOR-swizzled
-// by r, so the A-fragment reads are free of bank conflicts.
+// rows keep their bf16 layout, padded by 16 bytes (a row starts one bank
+// group after the previous one), so the A-fragment reads are free of bank
+// conflicts and every k-step's offset is an immediate.
 //
 // Per wave the work is pipelined over 32-key sub-blocks b:
 //   S(b+1) = K Q^T     (bf16 MFMA, 32x32x16)      \  on the matrix cores
@@ -114,9 +115,12 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   constexpr int CH = D / 8;       // 16-byte pieces per K row
   constexpr int RB = D * 2;       // bytes per K row
   constexpr int VB = D * 32;      // bytes per V block
-  constexpr int TB = kTile * D * 2;     // bytes of a K tile and of a V tile
-  constexpr int NI = TB / 1024 / NW;    // 1 KB copies per wave, for each of the K and V tiles
-  static_assert(NI * NW * 1024 == TB, "tile copies split evenly over the waves");
+  constexpr int TB = kTile * D * 2;     // bytes of a V tile
+  constexpr int KP = CH + 1;            // 16-byte positions per padded K row
+  constexpr int KRB = KP * 16;          // bytes per padded K row
+  constexpr int KTB = kTile * KRB;      // bytes of a K tile (KP copies of 1 KB)
+  constexpr int NI = TB / 1024 / NW;    // 1 KB copies per wave of the V tile
+  static_assert(NI * NW * 1024 == TB, "V tile copies split evenly over the waves");
   const KParams& kp = a.kp;
 
   // ---- unit: KV head fastest (consecutive workgroups share a head's K/V in L2),
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   const int qrow = u * kTile + pos0 + ql;
   const int64_t orow = (static_cast<int64_t>(b) * kp.Hq + static_cast<int64_t>(h) * kp.gq + hh) * a.nq + qrow;
 
-  __shared__ __align__(16) unsigned char k0[TB], k1[TB], k2[TB];
+  __shared__ __align__(16) unsigned char k0[KTB], k1[KTB], k2[KTB];
   __shared__ __align__(16) unsigned char v0[TB], v1[TB], v2[TB];
   __shared__ int tb[kMaxTiles][4];  // V block index (16 keys) of block t of tile tt, -1 if none
   auto kslot = [&](auto S) -> unsigned char* {
@@ -204,22 +208,21 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
                                                                    static_cast<int64_t>(bh) * kp.n_cap * D);
   const unsigned char* Vb = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.V16) +
                                                                    static_cast<int64_t>(bh) * kp.n_cap * D);
-  // Copy tile tt into slot S (no-op past the last tile).  Copy i of this wave
-  // fills bytes [1024 c, 1024 c + 1024) of the slot's K and V tiles, c = wid NI + i,
-  // lane l writing 16 bytes at 16 l.  K: piece position p = 64 c + l is row
-  // p / CH, swizzled piece p % CH; V: the tile is its 4 blocks back to back.
+  // Copy tile tt into slot S (no-op past the last tile).  Copy c fills bytes
+  // [1024 c, 1024 c + 1024) of the slot's K or V tile, lane l writing 16 bytes
+  // at 16 l.  K: position p = 64 c + l is piece p % KP of row p / KP (the last
+  // position of a row is padding and loads a duplicate); V: the tile is its 4
+  // blocks back to back.
   auto copy_tile = [&](auto S, int tt) __attribute__((always_inline)) {
     if (tt >= n_tiles) return;
     unsigned char* ks = kslot(S);
     unsigned char* vs = vslot(S);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int c = wid * NI + i;
+    for (int c = wid; c < KP; c += NW) {
       const int p = 64 * c + lane;
-      const int r = p / CH, cs = p % CH;
+      const int r = p / KP, cs = p % KP;
       const int kb = tb[tt][r >> 4];
       const int64_t tok = kb >= 0 ? static_cast<int64_t>(kb) * kBlk + (r & (kBlk - 1)) : 0;
-      const unsigned char* src = Kb + tok * RB + ((cs ^ (r % CH)) << 4);
+      const unsigned char* src = Kb + tok * RB + ((cs < CH ? cs : 0) << 4);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                        (__attribute__((address_space(3))) void*)(ks + 1024 * c),
                                        16, 0, 0);
@@ -248,12 +251,10 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   // (ql, hb) gets query ql against keys 32 sb + 8 (v / 4) + 4 hb + v % 4
   auto qk = [&](const unsigned char* ks, int sb) -> f32x16_t {
     f32x16_t acc = f32x16_t{};
-    const int r = 32 * sb + ql;
-    const unsigned char* rowp = ks + r * RB;
+    const unsigned char* rowp = ks + (32 * sb + ql) * KRB + hb * 16;
 #pragma unroll
     for (int d = 0; d < KSTEPS; ++d) {
-      const int c = 2 * d + hb;
-      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(rowp + ((c ^ (r % CH)) << 4));
+      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(rowp + 32 * d);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[d], acc, 0, 0, 0);
     }
     return acc;
