@@ -357,6 +357,7 @@ def bench_prefill(args, dev):
                          "flops_per_launch": fl_att, "avg_us": round(t_att, 2),
                          "includes": ["v16_blocks_kernel<128>", "attend_prefill_pipe_kernel<128,8>"]},
             "route": {"kernel": "route_prefill_mfma_kernel<128,8>", "avg_us": round(t_route, 2),
+                      "includes": ["summary_split_kernel<128> (x2)", "route_prefill_mfma_kernel<128,8>"],
                       "flops_per_launch": fl_route, "achieved_tflops": round(tf_route, 1),
                       "frac": round(tf_route / MFMA_BF16_PEAK_TFLOPS, 4)},
             "summaries": {"kernel": "summaries_kernel<bf16,128>", "avg_us": round(t_sum, 2),

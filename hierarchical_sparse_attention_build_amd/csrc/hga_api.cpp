@@ -115,10 +115,11 @@ size_t elem_bytes(const hga_params* p) { return p->qkv_dtype == HGA_BF16 ? 2 : 4
 // ------------------------------------------------------------------ workspace plans
 struct RoutePlan {
   int n_units, slices, cps;
-  size_t scores_off, cand_off, gscores_off, counters_off, bytes;
+  size_t scores_off, cand_off, gscores_off, counters_off, split_off, bytes;
+  bool split;  // the MFMA prefill routing runs (split summary tables present)
 };
 
-RoutePlan plan_route(const KParams& kp, int64_t nq, size_t base) {
+RoutePlan plan_route(const KParams& kp, int64_t nq, bool bf16_in, size_t base) {
   RoutePlan r{};
   r.n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
   r.cps = route_chunks_per_slice(kp, nq);
@@ -134,6 +135,9 @@ RoutePlan plan_route(const KParams& kp, int64_t nq, size_t base) {
   off = align256(off + units * kp.n_chunks_cap * sizeof(int32_t));
   r.gscores_off = off;
   off = align256(off + units * static_cast<size_t>(kp.top_k) * kp.m * sizeof(float));
+  r.split = route_prefill_mfma_supported(kp, bf16_in, nq);
+  r.split_off = off;
+  if (r.split) off = align256(off + route_prefill_split_bytes(kp));
   r.bytes = off - base;
   return r;
 }
@@ -263,7 +267,7 @@ FullPlan plan(const KParams& kp, int op, int64_t nq, bool bf16_in) {
   const bool needs_idx = op == HGA_OP_PREFILL || op == HGA_OP_DECODE || op == HGA_OP_DECODE_OFFLOAD;
   // counters first, so that zeroing the head of the workspace is enough
   if (needs_route) {
-    f.route = plan_route(kp, nq, off);
+    f.route = plan_route(kp, nq, bf16_in, off);
     off += f.route.bytes;
   }
   if (needs_attend) {
@@ -332,6 +336,7 @@ RouteArgs route_args(const KParams& kp, const FullPlan& f, void* ws, const void*
   a.chunk_idx = ci;
   a.group_idx = gi;
   a.scores_out = scores_out;
+  a.split = f.route.split ? at<uint16_t>(ws, f.route.split_off) : nullptr;
   a.build_summary = 0;
   return a;
 }

@@ -42,6 +42,7 @@ struct RouteArgs {
   int32_t* chunk_idx;     // [B*Hkv*n_units, top_k]
   int32_t* group_idx;     // [B*Hkv*n_units, top_g]
   float* scores_out;      // nullable [B*Hkv, n_chunks_cap] (decode)
+  uint16_t* split;        // ws, MFMA prefill routing only: the summary tables as bf16 hi and lo parts
   // fused summary update (decode only): when the query completes its chunk
   int32_t build_summary;
   RowSource ksrc;
@@ -178,6 +179,8 @@ hipError_t launch_attend_prefill_pipe(const AttendArgs& a, hipStream_t st);
 // Prefill routing on the matrix cores (bf16, C = 64, Hq/Hkv <= 4).
 bool route_prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq);
 hipError_t launch_route_prefill_mfma(const RouteArgs& a, hipStream_t st);
+// bytes of the split summary tables that the MFMA prefill routing needs in its workspace
+size_t route_prefill_split_bytes(const KParams& kp);
 
 // Workgroup counts and tiling chosen by the host for a given shape.
 constexpr int kAttBlockRows = 16;  // K/V rows per attention block

@@ -10,9 +10,10 @@
 // partner half-wave and the other waves through LDS).  Q is exact in bf16;
 // the fp32 summaries are split as s = hi + lo with hi = bf16(s) and
 // lo = bf16(s - hi) and both products accumulate in fp32 (relative error of
-// the split about 2^-17).  Summary tiles are converted once per workgroup
-// into LDS.  Top-k on the chunk scores, then the same contraction over the
-// C/G groups of every routed chunk and a top-g.
+// the split about 2^-17).  The split is done once per call by a pre-pass over
+// both tables (every unit of a KV head reads the same rows); the units copy
+// their tiles of hi and lo rows into LDS.  Top-k on the chunk scores, then
+// the same contraction over the C/G groups of every routed chunk and a top-g.
 #include "hga_device.hpp"
 #include "hga_kernels.hpp"
 
@@ -20,6 +21,7 @@ namespace hga {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRTile = 32;  // summaries per tile
 
@@ -28,7 +30,7 @@ struct RoutePrefillSmem {
   static constexpr int ROW = D * 2 + 16;  // bytes per bf16 row (padded)
   alignas(16) unsigned char hi[2][kRTile * ROW];
   alignas(16) unsigned char lo[2][kRTile * ROW];
-  float wmax[NW][kRTile];
+  float wmax[2][NW][kRTile];  // per tile parity: each wave's column maxima
   float scores[1024 * 4];   // chunk scores of the unit, then group scores
   int sel_chunks[1024];
   int sel_groups[1024];
@@ -40,13 +42,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
+// Split tables: rows [0, R) of an fp32 table into hi and lo bf16 rows, 8
+// values per thread.  Layout of the split area: chunk hi, chunk lo, group hi,
+// group lo, each [B*Hkv*rows, d].
+template <int D>
+__global__ __launch_bounds__(256) void summary_split_kernel(const float* __restrict__ src, int64_t rows,
+                                                            uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e >= rows * D) return;
+  const float4 a = *reinterpret_cast<const float4*>(src + e);
+  const float4 b = *reinterpret_cast<const float4*>(src + e + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float h0 = bf16_to_f32(f32_to_bf16(v[2 * i])), h1 = bf16_to_f32(f32_to_bf16(v[2 * i + 1]));
+    h[i] = pack_bf16x2(h0, h1);
+    l[i] = pack_bf16x2(v[2 * i] - h0, v[2 * i + 1] - h1);
+  }
+  *reinterpret_cast<uint4*>(hi + e) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(lo + e) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+size_t route_prefill_split_bytes(const KParams& kp) {
+  const size_t rows = static_cast<size_t>(kp.B) * kp.Hkv * kp.n_chunks_cap * (1 + kp.m);
+  return rows * kp.d * 2 * sizeof(uint16_t);
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;
-  constexpr int F4 = D / 4;                     // float4 per summary row
-  constexpr int FPT = kRTile * F4 / NT;         // float4 per thread per tile
-  static_assert(FPT >= 1 && kRTile * F4 % NT == 0, "tile split");
+  constexpr int P8 = D / 8;                     // 16-byte pieces per bf16 row
+  constexpr int PPT = 2 * kRTile * P8 / NT;     // pieces per thread per tile (hi and lo)
+  static_assert(PPT >= 1 && 2 * kRTile * P8 % NT == 0, "tile split");
   using Smem = RoutePrefillSmem<D, NW>;
   const KParams& kp = a.kp;
 
@@ -87,74 +116,97 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
     for (int d = 0; d < KSTEPS; ++d) qa[d] = __builtin_bit_cast(bf16x8_t, qp[2 * d + hb]);
   }
 
-  // scores of n rows (row(i) -> float32 summary row) into out[0..n)
-  auto score_tiles = [&](int n, auto row, float* out) {
+  // scores of n rows (row(i): index of the summary row in the split tables
+  // hi, lo) into out[0..n).  Tiles are loaded two ahead (register sets A and B
+  // alternate, the loop is unrolled by two so each set is named statically)
+  // and copied into the LDS buffer of their parity.
+  auto score_tiles = [&](int n, auto row, const uint16_t* hi, const uint16_t* lo, float* out) {
     const int n_tiles = (n + kRTile - 1) / kRTile;
-    float4 reg[FPT];
-    auto fetch = [&](int tt) {
+    u32x4_t regA[PPT], regB[PPT];
+    auto fetch = [&](int tt, u32x4_t (&reg)[PPT]) {
 #pragma unroll
-      for (int i = 0; i < FPT; ++i) {
+      for (int i = 0; i < PPT; ++i) {
         const int f = tid + i * NT;
-        const int r = f / F4, c = f % F4;
+        const int part = f / (kRTile * P8), q = f % (kRTile * P8);
+        const int r = q / P8, c = q % P8;
         const int idx = tt * kRTile + r;
-        reg[i] = idx < n ? reinterpret_cast<const float4*>(row(idx))[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint16_t* tab = part ? lo : hi;
+        reg[i] = idx < n ? *reinterpret_cast<const u32x4_t*>(tab + row(idx) * D + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
       }
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](int buf, const u32x4_t (&reg)[PPT]) {
 #pragma unroll
-      for (int i = 0; i < FPT; ++i) {
+      for (int i = 0; i < PPT; ++i) {
         const int f = tid + i * NT;
-        const int r = f / F4, c = f % F4;
-        const float4 v = reg[i];
-        const float hx = bf16_to_f32(f32_to_bf16(v.x)), hy = bf16_to_f32(f32_to_bf16(v.y));
-        const float hz = bf16_to_f32(f32_to_bf16(v.z)), hw = bf16_to_f32(f32_to_bf16(v.w));
-        *reinterpret_cast<uint2*>(&sm.hi[buf][r * Smem::ROW + c * 8]) =
-            make_uint2(pack_bf16x2(hx, hy), pack_bf16x2(hz, hw));
-        *reinterpret_cast<uint2*>(&sm.lo[buf][r * Smem::ROW + c * 8]) =
-            make_uint2(pack_bf16x2(v.x - hx, v.y - hy), pack_bf16x2(v.z - hz, v.w - hw));
+        const int part = f / (kRTile * P8), q = f % (kRTile * P8);
+        const int r = q / P8, c = q % P8;
+        unsigned char* dst = part ? sm.lo[buf] : sm.hi[buf];
+        *reinterpret_cast<u32x4_t*>(dst + r * Smem::ROW + c * 16) = reg[i];
       }
     };
-    if (n_tiles == 0) return;
-    fetch(0);
-    stage(0);
-    __syncthreads();
-    for (int tt = 0; tt < n_tiles; ++tt) {
-      const int buf = tt & 1;
-      if (tt + 1 < n_tiles) fetch(tt + 1);
-      f32x16_t acc = f32x16_t{};
+    // tile tt from LDS buffer buf: the max over the unit's query rows of every
+    // column; the hi and lo products accumulate in two independent chains
+    auto compute = [&](int buf) {
+      f32x16_t acc_h = f32x16_t{}, acc_l = f32x16_t{};
 #pragma unroll
       for (int d = 0; d < KSTEPS; ++d) {
         const int off = ql * Smem::ROW + (16 * d + 8 * hb) * 2;
         const bf16x8_t bh_ = *reinterpret_cast<const bf16x8_t*>(&sm.hi[buf][off]);
         const bf16x8_t bl_ = *reinterpret_cast<const bf16x8_t*>(&sm.lo[buf][off]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], bh_, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], bl_, acc, 0, 0, 0);
+        acc_h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], bh_, acc_h, 0, 0, 0);
+        acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], bl_, acc_l, 0, 0, 0);
       }
-      float mx = acc[0];
+      float mx = acc_h[0] + acc_l[0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc_h[v] + acc_l[v]);
       {
         float pa, pb;
         dpp::swap32(mx, pa, pb);
         mx = fmaxf(pa, pb);
       }
-      if (hb == 0) sm.wmax[wid][ql] = mx;
-      if (tt + 1 < n_tiles) stage(buf ^ 1);
-      __syncthreads();
+      if (hb == 0) sm.wmax[buf][wid][ql] = mx;
+    };
+    auto reduce = [&](int tt) {
       if (tid < kRTile) {
         const int idx = tt * kRTile + tid;
-        float m = sm.wmax[0][tid];
+        float m = sm.wmax[tt & 1][0][tid];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.wmax[w][tid]);
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, sm.wmax[tt & 1][w][tid]);
         if (idx < n) out[idx] = m * kp.inv_sqrt_d;
       }
+    };
+    if (n_tiles == 0) return;
+    // tile tt: its buffer tt % 2 is staged; tile tt + 1 is in the other
+    // register set, tile tt + 2 goes into this one.  One barrier per tile:
+    // buffer (tt + 1) % 2 was last read before the previous barrier, and the
+    // maxima of tile tt are reduced after this one (those of tile tt + 2, in
+    // the same slots, are written after the next).
+    auto step = [&](int tt, u32x4_t (&mine)[PPT], u32x4_t (&other)[PPT]) {
+      if (tt + 2 < n_tiles) fetch(tt + 2, mine);
+      compute(tt & 1);
+      if (tt + 1 < n_tiles) stage((tt + 1) & 1, other);
       __syncthreads();
+      reduce(tt);
+    };
+    fetch(0, regA);
+    if (n_tiles > 1) fetch(1, regB);
+    stage(0, regA);
+    __syncthreads();
+    for (int tt = 0; tt < n_tiles; tt += 2) {
+      step(tt, regA, regB);
+      if (tt + 1 < n_tiles) step(tt + 1, regB, regA);
     }
+    __syncthreads();  // the last scores are in out
   };
 
   // ---- level 1: chunk scores and top-k
-  const float* ctab = a.chunk_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * D;
-  score_tiles(nM, [&](int i) { return ctab + static_cast<int64_t>(kp.n_sink + i) * D; }, sm.scores);
+  const int64_t crow0 = static_cast<int64_t>(bh) * kp.n_chunks_cap + kp.n_sink;
+  const int64_t n_ctab = static_cast<int64_t>(kp.B) * kp.Hkv * kp.n_chunks_cap * D;
+  const uint16_t* c_hi = a.split;
+  const uint16_t* c_lo = a.split + n_ctab;
+  const uint16_t* g_hi = a.split + 2 * n_ctab;
+  const uint16_t* g_lo = a.split + 2 * n_ctab + n_ctab * kp.m;
+  score_tiles(nM, [&](int i) { return crow0 + i; }, c_hi, c_lo, sm.scores);
   int cnt;
   if (nM <= NT)
     cnt = rank_select<NT>(tid < nM ? sm.scores[tid] : 0.f, nM, kp.top_k, sm.sel_chunks, sm.rank);
@@ -166,13 +218,10 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
   // ---- level 2: group scores of the routed chunks and top-g
   const int m = kp.m;
   const int nG = cnt * m;
-  const float* gtab = a.group_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m * D;
+  const int64_t grow0 = static_cast<int64_t>(bh) * kp.n_chunks_cap * m;
   score_tiles(nG,
-              [&](int i) {
-                const int64_t gid = static_cast<int64_t>(kp.n_sink + sm.sel_chunks[i / m]) * m + i % m;
-                return gtab + gid * D;
-              },
-              sm.scores);
+              [&](int i) { return grow0 + static_cast<int64_t>(kp.n_sink + sm.sel_chunks[i / m]) * m + i % m; },
+              g_hi, g_lo, sm.scores);
   int gcnt;
   if (nG <= NT)
     gcnt = rank_select<NT>(tid < nG ? sm.scores[tid] : 0.f, nG, kp.top_g, sm.sel_groups, sm.rank);
@@ -197,12 +246,22 @@ bool route_prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq) {
 
 template <int D, int NW>
 static hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
-  const unsigned n_wg = static_cast<unsigned>(a.kp.B) * a.kp.Hkv * a.n_units;
+  const KParams& kp = a.kp;
+  const int64_t crows = static_cast<int64_t>(kp.B) * kp.Hkv * kp.n_chunks_cap;
+  const int64_t n_ctab = crows * D;
+  auto split = [&](const float* src, int64_t rows, uint16_t* hi, uint16_t* lo) {
+    const int64_t threads = rows * D / 8;
+    summary_split_kernel<D><<<static_cast<unsigned>((threads + 255) / 256), 256, 0, st>>>(src, rows, hi, lo);
+  };
+  split(a.chunk_sum, crows, a.split, a.split + n_ctab);
+  split(a.group_sum, crows * kp.m, a.split + 2 * n_ctab, a.split + 2 * n_ctab + n_ctab * kp.m);
+  const unsigned n_wg = static_cast<unsigned>(kp.B) * kp.Hkv * a.n_units;
   route_prefill_mfma_kernel<D, NW><<<n_wg, NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_route_prefill_mfma(const RouteArgs& a, hipStream_t st) {
+  if (!a.split) return hipErrorInvalidValue;
   const int nw = 2 * a.kp.gq;
   if (a.kp.d == 128) {
     if (nw == 2) return launch_t<128, 2>(a, st);
