@@ -145,7 +145,10 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
 
   __shared__ __align__(16) unsigned char k0[KTB], k1[KTB], k2[KTB];
   __shared__ __align__(16) unsigned char v0[TB], v1[TB], v2[TB];
-  __shared__ int tb[kMaxTiles][4];  // V block index (16 keys) of block t of tile tt, -1 if none
+  // tile table: byte offsets of block t (16 keys) of tile tt in K and in the
+  // fp16 V blocks (0 for an empty block), and the tile's valid blocks (bit t)
+  __shared__ uint32_t tk[kMaxTiles][4], tv[kMaxTiles][4];
+  __shared__ int tvm[kMaxTiles];
   auto kslot = [&](auto S) -> unsigned char* {
     if constexpr (decltype(S)::value == 0) return k0;
     else if constexpr (decltype(S)::value == 1) return k1;
@@ -190,7 +193,11 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
       const int g = e < kp.top_g ? glg[e] : -1;
       kb = g >= 0 && g < n_groups_cap ? g * bpg + t % bpg : -1;
     }
-    tb[tt][t] = kb;
+    tk[tt][t] = kb >= 0 ? static_cast<uint32_t>(kb) * (kBlk * RB) : 0u;
+    tv[tt][t] = kb >= 0 ? static_cast<uint32_t>(kb) * VB : 0u;
+    // the valid bits of the tile, gathered by its block 0 thread
+    const uint64_t ok = __ballot(kb >= 0);
+    if (t == 0) tvm[tt] = static_cast<int>((ok >> (lane & ~3)) & 0xf);
   }
   // V slot 2 stands for tile -1 in the first P.V (with P = 0): finite zeros
   for (int q = tid; q < TB / 16; q += NT) reinterpret_cast<uint4*>(v2)[q] = make_uint4(0u, 0u, 0u, 0u);
@@ -213,38 +220,48 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   // at 16 l.  K: position p = 64 c + l is piece p % KP of row p / KP (the last
   // position of a row is padding and loads a duplicate); V: the tile is its 4
   // blocks back to back.
+  // This lane's part of the copies, fixed for the whole unit: K copy i of
+  // this wave is copy c = wid + i NW (while c < KP), its lane loads piece
+  // kpc of row kr (kr / 16 = its block); V copy i is c = wid NI + i, its lane
+  // loads byte voff of block vt.
+  constexpr int NKC = (KP + NW - 1) / NW;
+  uint32_t koff[NKC];
+  int kblk[NKC];
+#pragma unroll
+  for (int i = 0; i < NKC; ++i) {
+    const int p = 64 * (wid + i * NW) + lane;
+    const int kr = (p / KP) & (kTile - 1), kpc = p % KP;
+    koff[i] = static_cast<uint32_t>((kr & (kBlk - 1)) * RB + ((kpc < CH ? kpc : 0) << 4));
+    kblk[i] = kr >> 4;
+  }
+  uint32_t voff[NI];
+  int vblk[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int p = 64 * (wid * NI + i) + lane;
+    vblk[i] = p / (2 * D);
+    voff[i] = static_cast<uint32_t>((p % (2 * D)) * 16);
+  }
   auto copy_tile = [&](auto S, int tt) __attribute__((always_inline)) {
     if (tt >= n_tiles) return;
     unsigned char* ks = kslot(S);
     unsigned char* vs = vslot(S);
-    for (int c = wid; c < KP; c += NW) {
-      const int p = 64 * c + lane;
-      const int r = p / KP, cs = p % KP;
-      const int kb = tb[tt][r >> 4];
-      const int64_t tok = kb >= 0 ? static_cast<int64_t>(kb) * kBlk + (r & (kBlk - 1)) : 0;
-      const unsigned char* src = Kb + tok * RB + ((cs < CH ? cs : 0) << 4);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                       (__attribute__((address_space(3))) void*)(ks + 1024 * c),
-                                       16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) {
+      const int c = wid + i * NW;
+      if (c < KP) {
+        const unsigned char* src = Kb + tk[tt][kblk[i]] + koff[i];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                         (__attribute__((address_space(3))) void*)(ks + 1024 * c), 16, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int c = wid * NI + i;
-      const int p = 64 * c + lane;
-      const int t = p / (2 * D), w = p % (2 * D);
-      const int kb = tb[tt][t];
-      const unsigned char* src = Vb + static_cast<int64_t>(kb >= 0 ? kb : 0) * VB + w * 16;
+      const unsigned char* src = Vb + tv[tt][vblk[i]] + voff[i];
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                       (__attribute__((address_space(3))) void*)(vs + 1024 * c),
-                                       16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(vs + 1024 * c), 16, 0, 0);
     }
-  };
-  auto valid_mask = [&](int tt) -> uint64_t {
-    uint64_t m = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (tb[tt][t] >= 0) m |= 0xffffull << (16 * t);
-    return m;
   };
 
   // S^T of sub-block sb (keys 32 sb .. 32 sb + 31 of the K tile ks): lane
@@ -278,12 +295,12 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   };
   // masked scores (-inf) of sub-block sb of tile tt
   auto mask = [&](f32x16_t& s, int tt, int sb) {
-    const uint64_t vmask = valid_mask(tt);
-    if (tt > 0 && vmask == ~0ull) return;  // uniform: no masked key
+    const int vm = __builtin_amdgcn_readfirstlane(tvm[tt]);
+    if (tt > 0 && vm == 0xf) return;  // uniform: no masked key
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int kt = 32 * sb + 8 * (v >> 2) + 4 * hb + (v & 3);
-      bool ok = (vmask >> kt) & 1ull;
+      bool ok = (vm >> (kt >> 4)) & 1;
       if (tt == 0) ok = ok && kt <= pos0 + ql;  // causal inside the current chunk
       s[v] = ok ? s[v] : -__builtin_huge_valf();
     }
@@ -412,7 +429,8 @@ bool prefill_pipe_supported(const KParams& kp, bool bf16_in, int64_t nq) {
     return false;
   const int64_t tiles = 1 + static_cast<int64_t>(kp.n_sink) + kp.n_local +
                         (static_cast<int64_t>(kp.top_g) * kp.G + kTile - 1) / kTile;
-  return tiles <= kMaxTiles;
+  // the tile table holds 32-bit byte offsets into one (b, KV head)'s rows
+  return tiles <= kMaxTiles && kp.n_cap * kp.d * 2 <= 0xffffffffll;
 }
 
 size_t prefill_pipe_v16_bytes(const KParams& kp) {
