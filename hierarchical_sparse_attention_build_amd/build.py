@@ -31,6 +31,13 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
+# Per-file additions.  The pipelined prefill attention never sees a NaN from
+# finite inputs (masked scores are -inf): without NaN semantics its row maxima
+# need no canonicalising instruction per MFMA result.
+FILE_FLAGS = {
+    "attend_prefill_pipe.hip": ["-fno-honor-nans"],
+}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
@@ -40,7 +47,7 @@ def sources():
 def _compile(src, opt):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *lang, *COMMON, opt, "-c", src, "-o", obj]
+    cmd = [HIPCC, *lang, *COMMON, *FILE_FLAGS.get(os.path.basename(src), []), opt, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
