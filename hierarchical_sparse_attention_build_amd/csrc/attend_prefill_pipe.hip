@@ -199,8 +199,6 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
     const uint64_t ok = __ballot(kb >= 0);
     if (t == 0) tvm[tt] = static_cast<int>((ok >> (lane & ~3)) & 0xf);
   }
-  // V slot 2 stands for tile -1 in the first P.V (with P = 0): finite zeros
-  for (int q = tid; q < TB / 16; q += NT) reinterpret_cast<uint4*>(v2)[q] = make_uint4(0u, 0u, 0u, 0u);
 
   // ---- the wave's query rows as the B operand of S^T = K Q^T
   bf16x8_t qv[KSTEPS];
@@ -279,15 +277,22 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   f32x16_t o[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
-  // O^T += V^T P^T for sub-block sb of the V tile vs; pk[t] = P^T of its k-step t
-  // (all eight V fragments are read before the first MFMA)
-  auto pv = [&](const unsigned char* vs, int sb, const f16x8_t (&pk)[2]) {
-    f16x8_t vf[2][DBLK];
+  // V fragments of the sub-block whose P.V comes next, read one sub-block
+  // ahead (zeros before the first: its P is zero too)
+  f16x8_t vf[2][DBLK];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) vf[t][db] = f16x8_t{};
+  auto read_v = [&](const unsigned char* vs, int sb) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
         vf[t][db] = *reinterpret_cast<const f16x8_t*>(vs + (2 * sb + t) * VB + vblock_off(32 * db + ql, hb));
+  };
+  // O^T += V^T P^T with the fragments read ahead; pk[t] = P^T of k-step t
+  auto pv = [&](const f16x8_t (&pk)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -327,13 +332,13 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   const int nsb = 2 * n_tiles;
   const f16x2_t ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
-  // One 32-key sub-block bsb: P.V of the previous one (V tile vp), S of the
-  // next one (K tile kn), P of this one.  The last sub-block's "next"
-  // scores read whatever the slot holds and are dropped; the first P.V has
-  // P = 0 over the zeroed slot.
-  auto sub = [&](int bsb, const unsigned char* kn, const unsigned char* vp) __attribute__((always_inline)) {
+  // One 32-key sub-block bsb: P.V of the previous one, S of the next one
+  // (K tile kn), P of this one, and the V fragments of this one (V tile vs)
+  // for the next P.V.  The last sub-block's "next" scores read whatever the
+  // slot holds and are dropped.
+  auto sub = [&](int bsb, const unsigned char* kn, const unsigned char* vs) __attribute__((always_inline)) {
     const bool has_next = bsb + 1 < nsb;
-    pv(vp, (bsb + 1) & 1, pk_prev);
+    pv(pk_prev);
     f32x16_t s_nxt = qk(kn, (bsb + 1) & 1);
     f16x8_t pk_cur[2];
     float rs = 0.f;
@@ -349,6 +354,7 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
         pk_cur[t][2 * i + 1] = h2[1];
       }
     }
+    read_v(vs, bsb & 1);
     {
       float pa, pb;
       dpp::swap32(rs, pa, pb);
@@ -375,15 +381,16 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
     pk_prev[1] = pk_cur[1];
     s_cur = s_nxt;
   };
-  // Tile T in slot S: sub-block 2T (next scores from this K tile, P.V over
-  // the previous V tile), then, once every wave is past the reads of slot
-  // S + 2 and tile T + 1 has landed, tile T + 2 starts copying into slot
-  // S + 2; then sub-block 2T + 1 (next scores from slot S + 1, P.V over slot S).
+  // Tile T in slot S: sub-block 2T (next scores from this K tile), then,
+  // once every wave is past its reads of slot S + 2 (the last were tile
+  // T - 1's V fragments, in sub-block 2T - 1) and tile T + 1 has landed, tile
+  // T + 2 starts copying into slot S + 2; then sub-block 2T + 1 (next scores
+  // from slot S + 1).  Both read their V fragments from slot S.
   auto tile = [&](auto S, int T) __attribute__((always_inline)) {
     constexpr int s0 = decltype(S)::value, s1 = (s0 + 1) % 3, s2 = (s0 + 2) % 3;
     const std::integral_constant<int, s1> S1{};
     const std::integral_constant<int, s2> S2{};
-    sub(2 * T, kslot(S), vslot(S2));
+    sub(2 * T, kslot(S), vslot(S));
     __syncthreads();
     copy_tile(S2, T + 2);
     sub(2 * T + 1, kslot(S1), vslot(S));
@@ -393,13 +400,7 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
     if (T + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, T + 1);
     if (T + 2 < n_tiles) tile(std::integral_constant<int, 2>{}, T + 2);
   }
-  // P.V of the last sub-block (tile n_tiles - 1, slot (n_tiles - 1) % 3)
-  {
-    const int sl = (n_tiles - 1) % 3;
-    if (sl == 0) pv(v0, 1, pk_prev);
-    else if (sl == 1) pv(v1, 1, pk_prev);
-    else pv(v2, 1, pk_prev);
-  }
+  pv(pk_prev);  // the last sub-block
 
   // ---- O = O^T / l: lane (query, half) holds dims 32db + 8i + 4*half + {0..3}
   const float inv = 1.f / l_run;
