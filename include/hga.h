@@ -91,7 +91,10 @@ typedef struct {
 
 /* Bytes of workspace an operation needs (0 on invalid params; see
  * hga_last_error).  `nq` is the number of query rows per sequence (1 for
- * decode), `n_cap` the token capacity of the K/V cache. */
+ * decode), `n_cap` the token capacity of the K/V cache.  With bf16 inputs and
+ * nq > 1 (prefill), the attention's share includes an fp16 copy of V
+ * (B*Hkv*n_cap*d*2 bytes) and the routing's share the summary tables split
+ * into bf16 high and low parts; both are rebuilt by every call. */
 size_t hga_workspace_size(const hga_params* p, int32_t op, int64_t nq, int64_t n_cap);
 
 /* Step 1: RoPE-aware chunk and group summaries [HGA-it, Meccanismo Core,
