@@ -324,6 +324,9 @@ def test_prefill_bf16(hga, over):
     {"n_q_heads": 8, "group_size": 32, "top_g": 12},   # 1 per KV head, groups of two 16-key blocks
     {"group_size": 64, "top_g": 5},                    # whole-chunk groups, a partly filled last tile
     {"group_size": 8, "top_g": 24},                    # groups of 8 keys
+    {"top_k": 0, "top_g": 0},                          # no routed groups: forced chunks only
+    {"n_sink": 0, "n_local": 0, "top_g": 16},          # the current chunk and the routed groups only
+    {"n_q_heads": 8, "head_dim": 64, "top_g": 20},     # 1 query head per KV head, d = 64
 ])
 def test_prefill_attend_given_lists(hga, over):
     """hga_attend for a block of prefill queries appended at a position offset
@@ -340,7 +343,7 @@ def test_prefill_attend_given_lists(hga, over):
     q_pos = np.array([1024, 1536], dtype=np.int64)
     Qs = np.stack([w.Q[b, :, q_pos[b]:q_pos[b] + nq] for b in range(B)])
     rng = np.random.default_rng(11)
-    gi = np.full((B, H, nU, s.top_g), -1, dtype=np.int32)
+    gi = np.full((B, H, nU, max(1, s.top_g)), -1, dtype=np.int32)[..., :s.top_g]
     for b in range(B):
         for h in range(H):
             for u in range(nU):
