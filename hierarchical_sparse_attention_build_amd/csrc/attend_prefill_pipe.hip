@@ -14,16 +14,17 @@
 //
 // One workgroup per unit; each wave owns 32 query rows (one head, 32
 // positions).  Keys come in tiles of 64 (the current chunk (causal), the other
-// forced chunks, then the routed groups), loaded into registers one tile
-// ahead and stored into a ring of three LDS tiles, one barrier per tile.  K
+// forced chunks, then the routed groups), copied from HBM straight into a
+// ring of three LDS tiles two tiles ahead, one barrier per tile.  K
 // rows keep their bf16 layout, padded by 16 bytes (a row starts one bank
 // group after the previous one), so the A-fragment reads are free of bank
 // conflicts and every k-step's offset is an immediate.
 //
 // Per wave the work is pipelined over 32-key sub-blocks b:
-//   S(b+1) = K Q^T     (bf16 MFMA, 32x32x16)      \  on the matrix cores
-//   O^T   += V^T P^T(b-1) (fp16 MFMA)              /
-//   P(b)   = exp2(S(b) scale - m) (vector ALUs, concurrently)
+//   O^T   += V^T P^T(b-1) (fp16 MFMA, V fragments read during b-1) \  matrix
+//   S(b+1) = K Q^T     (bf16 MFMA, 32x32x16)                        /  cores
+//   P(b)   = exp2(S(b) scale - m) (vector ALUs, concurrently), and the V
+//            fragments of b are read for the next step;
 // then the max of S(b+1) decides whether the reference max m rises (when it
 // exceeds m by more than 2^8, base 2); a rise rescales O, l and the pending
 // P(b).  P is rounded to fp16 toward zero (relative error < 2^-10; the row
@@ -41,7 +42,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // register-staged 16-byte pieces
 
 constexpr int kTile = 64;      // keys per tile (= C)
 constexpr int kBlk = 16;       // keys per V block
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   // T + 2 starts copying into slot S + 2; then sub-block 2T + 1 (next scores
   // from slot S + 1).  Both read their V fragments from slot S.
   auto tile = [&](auto S, int T) __attribute__((always_inline)) {
-    constexpr int s0 = decltype(S)::value, s1 = (s0 + 1) % 3, s2 = (s0 + 2) % 3;
+    constexpr int s0 = decltype(S)::value, s1 = (s0 + 1) % kRing, s2 = (s0 + 2) % kRing;
     const std::integral_constant<int, s1> S1{};
     const std::integral_constant<int, s2> S2{};
     sub(2 * T, kslot(S), vslot(S));
@@ -395,7 +395,8 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
     copy_tile(S2, T + 2);
     sub(2 * T + 1, kslot(S1), vslot(S));
   };
-  for (int T = 0; T < n_tiles; T += 3) {
+  static_assert(kRing == 3, "the tile loop names three slots");
+  for (int T = 0; T < n_tiles; T += kRing) {
     tile(std::integral_constant<int, 0>{}, T);
     if (T + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, T + 1);
     if (T + 2 < n_tiles) tile(std::integral_constant<int, 2>{}, T + 2);
