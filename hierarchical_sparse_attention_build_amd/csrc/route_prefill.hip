@@ -16,6 +16,7 @@
 // the same contraction over the C/G groups of every routed chunk and a top-g.
 #include "hga_device.hpp"
 #include "hga_kernels.hpp"
+#include "hga_select.hpp"
 
 namespace hga {
 
@@ -34,8 +35,10 @@ struct RoutePrefillSmem {
   float scores[1024 * 4];   // chunk scores of the unit, then group scores
   int sel_chunks[1024];
   int sel_groups[1024];
-  RankSmem<NW * 64> rank;
-  TopkSmem<NW * 64> topk;
+  union {  // scratch of the selection in use
+    SelSmem<NW * 64> sel;
+    TopkSmem<NW * 64> topk;
+  } u;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -207,11 +210,14 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
   const uint16_t* g_hi = a.split + 2 * n_ctab;
   const uint16_t* g_lo = a.split + 2 * n_ctab + n_ctab * kp.m;
   score_tiles(nM, [&](int i) { return crow0 + i; }, c_hi, c_lo, sm.scores);
-  int cnt;
-  if (nM <= NT)
-    cnt = rank_select<NT>(tid < nM ? sm.scores[tid] : 0.f, nM, kp.top_k, sm.sel_chunks, sm.rank);
-  else
-    cnt = block_topk<NT>([&](int i) { return sm.scores[i]; }, nM, kp.top_k, sm.sel_chunks, sm.topk);
+  // exact top-k of sm.scores[0, n) into out (ascending positions): ballot
+  // search by whole waves, or the radix path for a k too large for it
+  auto select = [&](int n, int k, int* out) -> int {
+    if (block_select_fits<NT>(n, k))
+      return block_select<NT>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.sel);
+    return block_topk<NT>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.topk);
+  };
+  const int cnt = select(nM, kp.top_k, sm.sel_chunks);
   int32_t* ci = a.chunk_idx + unit * kp.top_k;
   for (int i = tid; i < kp.top_k; i += NT) ci[i] = i < cnt ? kp.n_sink + sm.sel_chunks[i] : -1;
 
@@ -222,11 +228,7 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
   score_tiles(nG,
               [&](int i) { return grow0 + static_cast<int64_t>(kp.n_sink + sm.sel_chunks[i / m]) * m + i % m; },
               g_hi, g_lo, sm.scores);
-  int gcnt;
-  if (nG <= NT)
-    gcnt = rank_select<NT>(tid < nG ? sm.scores[tid] : 0.f, nG, kp.top_g, sm.sel_groups, sm.rank);
-  else
-    gcnt = block_topk<NT>([&](int i) { return sm.scores[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
+  const int gcnt = select(nG, kp.top_g, sm.sel_groups);
   int32_t* gi = a.group_idx + unit * kp.top_g;
   for (int i = tid; i < kp.top_g; i += NT) {
     int32_t v = -1;
