@@ -80,6 +80,7 @@ struct AttnLane {
   uint32_t qbf[GQ][kBF ? EPL / 2 : 1];
   float qf[kBF ? 1 : GQ][kBF ? 1 : EPL];
   float m_run[GQ], l_run[GQ], o[GQ][EPL];
+  __device__ __forceinline__ void finish() {}
 
   // q(hh) points at the row of head hh; cc = lane's sixteenth
   template <typename QFn>
@@ -275,6 +276,9 @@ struct AttnLaneMfma {
   static constexpr int KROWB = (D + 8) * 2;  // bytes per LDS tile row (padded against bank conflicts)
   bf16x8_t qb[KS];
   float m_run[GQ], l_run[GQ];
+  // GQ > 4: the running max and sum of head (lane & 15) live in the four lanes
+  // of that head (m_run / l_run are filled from them by finish())
+  float m_lane, l_lane;
   f32x4_t acc[EPL];
   unsigned char* kt;  // this wave's LDS tile of 16 K rows
 
@@ -297,8 +301,21 @@ struct AttnLaneMfma {
       m_run[hh] = -__builtin_huge_valf();
       l_run[hh] = 0.f;
     }
+    m_lane = -__builtin_huge_valf();
+    l_lane = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // per-head statistics into m_run / l_run (head hh from lane hh)
+  __device__ __forceinline__ void finish() {
+    if constexpr (GQ > 4) {
+#pragma unroll
+      for (int hh = 0; hh < GQ; ++hh) {
+        m_run[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_lane), hh));
+        l_run[hh] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lane), hh));
+      }
+    }
   }
 
   struct Buf {
@@ -399,20 +416,39 @@ struct AttnLaneMfma {
     for (int i = 1; i < 8; ++i) bm_lane = fmaxf(bm_lane, sv[i]);
     bm_lane = max_rows(bm_lane);
     float mh = 0.f;
+    if constexpr (GQ <= 4) {
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh) {
-      const float bm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm_lane), hh));
-      if (bm > m_run[hh]) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - bm);  // 0 when m_run = -inf
-        l_run[hh] *= alpha;
-        // head hh sits in item hh%4 of the lanes with g = hh/4
-        const float al = GQ <= 4 || g == (hh >> 2) ? alpha : 1.f;
+      for (int hh = 0; hh < GQ; ++hh) {
+        const float bm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm_lane), hh));
+        if (bm > m_run[hh]) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - bm);  // 0 when m_run = -inf
+          l_run[hh] *= alpha;
+          // head hh sits in item hh%4 of the lanes with g = hh/4 (g = 0 here)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e][hh & 3] *= al;
-        m_run[hh] = bm;
+          for (int e = 0; e < EPL; ++e) acc[e][hh & 3] *= alpha;
+          m_run[hh] = bm;
+        }
+        const float mref = m_run[hh] == -__builtin_huge_valf() ? 0.f : m_run[hh];
+        mh = h == hh ? mref : mh;
       }
-      const float mref = m_run[hh] == -__builtin_huge_valf() ? 0.f : m_run[hh];
-      mh = h == hh ? mref : mh;
+    } else {
+      // every head at once: its four lanes hold its pair max; a rise anywhere
+      // rescales, the accumulator item i of lane (g, c) (head 4g+i) by the
+      // factor of lane 4g+i
+      const bool rise = h < GQ && bm_lane > m_lane;
+      if (__ballot(rise)) {
+        const float alpha = rise ? __builtin_amdgcn_exp2f(m_lane - bm_lane) : 1.f;  // 0 when m_lane = -inf
+        l_lane *= alpha;
+        m_lane = rise ? bm_lane : m_lane;
+        float a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[e][i] *= a[i];
+      }
+      mh = m_lane == -__builtin_huge_valf() ? 0.f : m_lane;
     }
     float p[8], ps = 0.f;
 #pragma unroll
@@ -421,9 +457,13 @@ struct AttnLaneMfma {
       ps += p[i];
     }
     ps = sum_rows(ps);
+    if constexpr (GQ <= 4) {
 #pragma unroll
-    for (int hh = 0; hh < GQ; ++hh)
-      l_run[hh] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps), hh));
+      for (int hh = 0; hh < GQ; ++hh)
+        l_run[hh] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ps), hh));
+    } else {
+      l_lane += ps;
+    }
     // ---- P as hi + lo bf16 pairs (A operand, k = 8g + 4b + i)
     uint4 phi, plo;
     uint32_t* hw = reinterpret_cast<uint32_t*>(&phi);
@@ -533,6 +573,7 @@ template <typename Lane, int D, int GQ, int NWV>
 __device__ __forceinline__ void attn_waves_to_lds(Lane& st, AttnMergeSmem<GQ, D, NWV>& sm) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
+  st.finish();
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh) {
