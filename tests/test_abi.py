@@ -129,3 +129,22 @@ def test_warm_tier_argument_errors(L):
         assert "slots" in hga.last_error()
     w = hga.HGAWarm(None, fake, fake, fake, fake, None, None, p.top_g)
     assert L.hga_decode_offload_warm(P, *args, ctypes.byref(w), fake, 1 << 30, None, None) == -1
+
+
+def test_prefill_workspace_holds_the_converted_tables(L):
+    """With bf16 inputs a prefill's workspace holds the fp16 copy of V and the
+    summary tables split into bf16 high and low parts; with fp32 inputs it does
+    not (those kernels do not run)."""
+    kw = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, chunk_size=64, group_size=16,
+              n_sink=1, n_local=2, top_k=32, top_g=64, rope_base=5e5)
+    n = 8192
+    pb = hga.params(**kw, qkv_dtype=hga.HGA_BF16)
+    pf = hga.params(**kw, qkv_dtype=hga.HGA_F32)
+    v16 = 1 * 8 * n * 128 * 2
+    split = 1 * 8 * (n // 64) * (1 + 4) * 128 * 2 * 2
+    for op in (hga.OP_ATTEND, hga.OP_PREFILL):
+        assert hga.workspace_size(pb, op, n, n) >= hga.workspace_size(pf, op, n, n) + v16
+    assert hga.workspace_size(pb, hga.OP_PREFILL, n, n) >= hga.workspace_size(pf, hga.OP_PREFILL, n, n) + v16 + split
+    # one query per sequence: neither table
+    assert hga.workspace_size(pb, hga.OP_ATTEND, 1, n) < v16
+
