@@ -439,50 +439,6 @@ __device__ int block_topk(ScoreFn sc_raw, int n, int k, int* sel, TopkSmem<NT>& 
   return k;
 }
 
-// Exact top-k for n <= NT candidates, one per thread: thread i (< n) passes its
-// score v and candidate index i.  Each candidate gets the composite key
-// (ordered score << 32 | ~i), unique and ordered like (score desc, index asc);
-// rank = number of larger keys, counted with one 64-bit compare per pair.  The
-// selected ones (rank < k) are written to sel[] in ascending index order.
-// Returns min(n, k).
-template <int NT>
-struct RankSmem {
-  uint64_t keys[NT];
-  int wave_cnt[NT / kWave];
-};
-
-template <int NT>
-__device__ int rank_select(float v, int n, int k, int* sel, RankSmem<NT>& sm) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
-  const uint64_t mine = composite_key(v, tid);
-  if (tid < n) sm.keys[tid] = mine;
-  __syncthreads();
-  bool take = false;
-  if (tid < n) {
-    int rank = 0;
-    int j = 0;
-    for (; j + 16 <= n; j += 16) {
-      uint64_t w[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) w[r] = sm.keys[j + r];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rank += w[r] > mine;
-    }
-    for (; j < n; ++j) rank += sm.keys[j] > mine;
-    take = rank < k;
-  }
-  const uint64_t ballot = __ballot(take);
-  if (lane == 0) sm.wave_cnt[wid] = __popcll(ballot);
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wid; ++w) before += sm.wave_cnt[w];
-  if (take) sel[before + __popcll(ballot & ((uint64_t(1) << lane) - 1))] = tid;
-  __syncthreads();
-  return n < k ? n : k;
-}
-
 // ---------------------------------------------------------------- cross-workgroup hand-off
 // Data that the last workgroup of a unit reads is written and read with
 // device-scope (agent) atomic stores/loads, which go past the per-XCD L2 to the

@@ -21,6 +21,7 @@
 // In a decode step one extra workgroup per (b, kv head) summarises the chunk
 // that the query completes, so a decode loop keeps the tables current.
 #include "hga_kernels.hpp"
+#include "hga_select.hpp"
 #include "hga_summarize.hpp"
 
 namespace hga {
@@ -35,8 +36,10 @@ constexpr int kSliceRows = kRowsPerRound * kRounds;             // candidate chu
 constexpr int kLdsCand = 2048;                                  // candidates staged in LDS for the selections
 
 struct RouteSmem {
-  TopkSmem<kRouteThreads> topk;
-  RankSmem<kRouteThreads> rank;
+  union {  // scratch of the selection in use
+    TopkSmem<kRouteThreads> topk;
+    SelSmem<kRouteThreads> sel;
+  };
   float loc[kSliceRows];
   int loc_sel[kSliceRows];
   int sel_chunks[1024];
@@ -187,8 +190,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
     const int kk = slice_count(x, nM, a.chunks_per_slice, kp.top_k);
     if (kk > 0) {
       if (kk < n_here) {
-        rank_select<kRouteThreads>(threadIdx.x < n_here ? sm.loc[threadIdx.x] : 0.f, n_here, kk, sm.loc_sel,
-                                   sm.rank);
+        block_select<kRouteThreads>([&](int i) { return sm.loc[i]; }, n_here, kk, sm.loc_sel, sm.sel);
         for (int r = threadIdx.x; r < kk; r += kRouteThreads) {
           const int i = sm.loc_sel[r];
           st_agent(cand_s + off + r, sm.loc[i]);
@@ -218,9 +220,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   __syncthreads();
   // candidates are in ascending chunk order, so position order breaks ties
   int cnt;
-  if (n_c <= kRouteThreads) {
-    cnt = rank_select<kRouteThreads>(threadIdx.x < n_c ? sm.cand_s[threadIdx.x] : 0.f, n_c, kp.top_k,
-                                     sm.sel_chunks, sm.rank);
+  if (in_lds && block_select_fits<kRouteThreads>(n_c, kp.top_k)) {
+    cnt = block_select<kRouteThreads>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.sel);
   } else if (in_lds) {
     cnt = block_topk<kRouteThreads>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
   } else {
@@ -250,9 +251,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   __threadfence_block();
   __syncthreads();
   int gcnt;
-  if (nG <= kRouteThreads)
-    gcnt = rank_select<kRouteThreads>(threadIdx.x < nG ? gsc[threadIdx.x] : 0.f, nG, kp.top_g, sm.sel_groups,
-                                      sm.rank);
+  if (block_select_fits<kRouteThreads>(nG, kp.top_g))
+    gcnt = block_select<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.sel);
   else
     gcnt = block_topk<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
   int32_t* gi = a.group_idx + unit * kp.top_g;
