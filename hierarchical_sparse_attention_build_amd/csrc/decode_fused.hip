@@ -5,14 +5,18 @@
 //
 // Work of one (batch, KV head) unit, all on one XCD so that its summaries and
 // K/V rows are shared through that XCD's L2:
-//   * One routing workgroup scores every candidate chunk summary (all rows in
-//     flight at once), selects the top-k chunks, scores their groups, selects
-//     the top-g groups, writes the index lists, and attends the unit's query
-//     heads over the routed groups' rows, which it already holds in LDS.
+//   * R routing workgroups (R = 1 or 2) each score every candidate chunk
+//     summary, select the top-k chunks, score their groups and select the
+//     top-g groups; they compute the same lists (the same arithmetic on the
+//     same data), routing workgroup 0 writes them, and each attends the unit's
+//     query heads over its share of the routed groups' rows.  A second one
+//     costs no hand-off: it repeats the routing (its summary reads hit the
+//     XCD's L2) to halve the routed attention, which follows the routing on
+//     the critical path.
 //   * F forced workgroups attend shares of the sink, local and current chunks
-//     (known before routing) while the routing workgroup works.  Forced
+//     (known before routing) while the routing workgroups work.  Forced
 //     workgroup 0 then summarises the chunk that the query completes.
-// The F + 1 partial softmax results (max, sum, output) are merged by the last
+// The F + R partial softmax results (max, sum, output) are merged by the last
 // of them to finish; no workgroup waits for another.
 //
 // The score of a chunk or group is the max over the unit's query heads of
@@ -126,17 +130,17 @@ __device__ __forceinline__ void scan_scores(const float* qs, int n, float scale,
 
 // ---------------------------------------------------------------------------
 // Forced-window partials and the final merge.  Part slots of a unit: forced
-// workgroup f in slot f, the routing workgroup in slot F.  Every workgroup of
-// a unit counts its arrival once its slot is written; the last arriver merges
-// the other slots with its own result (still in LDS) into O.  The routing
-// workgroup normally arrives last: it checks the count early, and when every
-// forced workgroup has arrived it arrives at once and prefetches their slots
-// while it still routes and attends.  Nobody waits for anybody.
+// workgroup f in slot f, routing workgroup r in slot F + r.  Every workgroup
+// of a unit counts its arrival once its slot is written; the last arriver
+// merges the other slots with its own result (still in LDS) into O.  A lone
+// routing workgroup normally arrives last: it checks the count early, and
+// when every forced workgroup has arrived it arrives at once and prefetches
+// their slots while it still routes and attends.  Nobody waits for anybody.
 
 // This thread's output element e = threadIdx.x (GQ * D <= kDecThreads) of the
 // part slots in `want` (bit p: slot p), loaded with plain loads.
 struct PartRegs {
-  float m[kDecMaxForced + 1], l[kDecMaxForced + 1], o[kDecMaxForced + 1];
+  float m[kDecMaxParts], l[kDecMaxParts], o[kDecMaxParts];
 };
 
 template <int D, int GQ>
@@ -145,7 +149,7 @@ __device__ __forceinline__ void load_parts(const float* parts, uint32_t want, Pa
   const int e = min(static_cast<int>(threadIdx.x), GQ * D - 1);
   const int hh = e / D;
 #pragma unroll
-  for (int p = 0; p <= kDecMaxForced; ++p) {
+  for (int p = 0; p < kDecMaxParts; ++p) {
     const bool in = (want >> p) & 1u;
     const float* q = parts + (in ? p : 0) * stride;
     r.m[p] = in ? q[GQ * D + hh] : -__builtin_huge_valf();
@@ -175,77 +179,65 @@ __device__ __forceinline__ void unstash_parts(const float* stash, int n, PartReg
     r.l[p] = stash[(3 * p + 1) * kDecThreads + t];
     r.o[p] = stash[(3 * p + 2) * kDecThreads + t];
   }
-  r.m[kDecMaxForced] = -__builtin_huge_valf();
-  r.l[kDecMaxForced] = 0.f;
-  r.o[kDecMaxForced] = 0.f;
+#pragma unroll
+  for (int p = kDecMaxForced; p < kDecMaxParts; ++p) {
+    r.m[p] = -__builtin_huge_valf();
+    r.l[p] = 0.f;
+    r.o[p] = 0.f;
+  }
 }
 static_assert(kDecMaxForced * 3 * kDecThreads <= kDecMaxScores, "stash fits the score array");
 
-// O[e] from this workgroup's merged waves (sm) and the loaded slots.
+// O[e] from the unit's part slots, merged in slot order: slot `own` is this
+// workgroup's merged waves (mg, the values it publishes), the others were
+// loaded into r (an empty slot has m = -inf).  The order does not depend on
+// which workgroup arrives last, so a call's output does not either.
 template <int D, int GQ>
-__device__ __forceinline__ void merge_store(const AttnMergeSmem<GQ, D, kDecWaves>& mg, const PartRegs& r,
+__device__ __forceinline__ void merge_store(const AttnMergeSmem<GQ, D, kDecWaves>& mg, const PartRegs& r, int own,
                                             const AttnOut& out) {
   const int e = threadIdx.x;
   if (e >= GQ * D) return;
   const int hh = e / D;
-  float M = mg.M[hh];
+  float m[kDecMaxParts], l[kDecMaxParts], o[kDecMaxParts];
+  const float om = mg.M[hh], ol = mg.L[hh], oo = attn_wg_value<D, GQ, kDecWaves>(mg, e);
 #pragma unroll
-  for (int p = 0; p <= kDecMaxForced; ++p) M = fmaxf(M, r.m[p]);
-  const float wo = mg.M[hh] == -__builtin_huge_valf() ? 0.f : exp2f(mg.M[hh] - M);
-  float num = attn_wg_value<D, GQ, kDecWaves>(mg, e) * wo;
-  float den = mg.L[hh] * wo;
+  for (int p = 0; p < kDecMaxParts; ++p) {
+    m[p] = p == own ? om : r.m[p];
+    l[p] = p == own ? ol : r.l[p];
+    o[p] = p == own ? oo : r.o[p];
+  }
+  float M = -__builtin_huge_valf();
 #pragma unroll
-  for (int p = 0; p <= kDecMaxForced; ++p) {
-    const float w = r.m[p] == -__builtin_huge_valf() ? 0.f : exp2f(r.m[p] - M);
-    num = fmaf(w, r.o[p], num);
-    den = fmaf(w, r.l[p], den);
+  for (int p = 0; p < kDecMaxParts; ++p) M = fmaxf(M, m[p]);
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int p = 0; p < kDecMaxParts; ++p) {
+    if (m[p] != -__builtin_huge_valf()) {
+      const float w = exp2f(m[p] - M);
+      num = fmaf(w, o[p], num);
+      den = fmaf(w, l[p], den);
+    }
   }
   out.put<D>(hh, e % D, num / den);
 }
 
-// The same straight from the waves' raw results (attn_waves_to_lds), every
-// thread weighting the waves of its head itself: one barrier fewer.
-template <int D, int GQ>
-__device__ __forceinline__ void merge_store_waves(const AttnMergeSmem<GQ, D, kDecWaves>& mg, const PartRegs& r,
-                                                  const AttnOut& out) {
-  const int e = threadIdx.x;
-  if (e >= GQ * D) return;
-  const int hh = e / D;
-  float M = -__builtin_huge_valf();
-#pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mg.wm[w][hh]);
-#pragma unroll
-  for (int p = 0; p <= kDecMaxForced; ++p) M = fmaxf(M, r.m[p]);
-  float num = 0.f, den = 0.f;
-#pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
-    const float wt = mg.wm[w][hh] == -__builtin_huge_valf() ? 0.f : exp2f(mg.wm[w][hh] - M);
-    num = fmaf(wt, mg.ow[w][e], num);
-    den = fmaf(wt, mg.wl[w][hh], den);
-  }
-#pragma unroll
-  for (int p = 0; p <= kDecMaxForced; ++p) {
-    const float w = r.m[p] == -__builtin_huge_valf() ? 0.f : exp2f(r.m[p] - M);
-    num = fmaf(w, r.o[p], num);
-    den = fmaf(w, r.l[p], den);
-  }
-  out.put<D>(hh, e % D, num / den);
-}
+// Part slots per unit.
+__device__ __forceinline__ int unit_parts(const DecodeArgs& a) { return a.forced_wgs + a.routing_wgs; }
 
 // Write this workgroup's merged waves into part slot `slot` (device-coherent
 // stores), count the arrival and return true in every thread of the last
-// arriver of the unit's F + 1 workgroups.
+// arriver of the unit's F + R workgroups.
 template <int D, int GQ>
 __device__ __forceinline__ bool publish_arrive(const DecodeArgs& a, int bh, int slot, AttnMergeSmem<GQ, D, kDecWaves>& mg) {
   constexpr int stride = attn_part_stride<D, GQ>();
   const int tid = threadIdx.x;
-  float* mine = a.partials + (static_cast<int64_t>(bh) * (a.forced_wgs + 1) + slot) * stride;
+  float* mine = a.partials + (static_cast<int64_t>(bh) * unit_parts(a) + slot) * stride;
   for (int e = tid; e < GQ * D; e += kDecThreads) st_agent(mine + e, attn_wg_value<D, GQ, kDecWaves>(mg, e));
   if (tid < GQ) {
     st_agent(mine + GQ * D + tid, mg.M[tid]);
     st_agent(mine + GQ * D + GQ + tid, mg.L[tid]);
   }
-  return arrive_last(a.sync + 4 * static_cast<int64_t>(bh), static_cast<uint32_t>(a.forced_wgs + 1), &mg.is_last);
+  return arrive_last(a.sync + 4 * static_cast<int64_t>(bh), static_cast<uint32_t>(unit_parts(a)), &mg.is_last);
 }
 
 __device__ __forceinline__ AttnOut unit_out(const DecodeArgs& a, int bh, int gq) {
@@ -286,12 +278,12 @@ __device__ __forceinline__ void forced_role(const DecodeArgs& a, int bh, int f, 
   st.template run<kForcedPF>(0, bb + wid, be, kDecWaves, kp.scale_log2, row);
   attn_merge_waves(st, sm.mg);
   if (publish_arrive<D, GQ>(a, bh, f, sm.mg)) {
-    // last arriver (rare): merge the other F slots, the routing one included
+    // last arriver (rare): merge the other slots, the routing ones included
     PartRegs r;
-    const uint32_t all = (2u << a.forced_wgs) - 1u;
-    load_parts<D, GQ>(a.partials + static_cast<int64_t>(bh) * (a.forced_wgs + 1) * attn_part_stride<D, GQ>(),
+    const uint32_t all = (1u << unit_parts(a)) - 1u;
+    load_parts<D, GQ>(a.partials + static_cast<int64_t>(bh) * unit_parts(a) * attn_part_stride<D, GQ>(),
                       all & ~(1u << f), r);
-    merge_store<D, GQ>(sm.mg, r, unit_out(a, bh, GQ));
+    merge_store<D, GQ>(sm.mg, r, f, unit_out(a, bh, GQ));
   }
   // ---- the query completes chunk j: summarise it for the next steps' routing
   if (f == 0 && a.build_summary && (t + 1) % kp.C == 0) {
@@ -303,11 +295,14 @@ __device__ __forceinline__ void forced_role(const DecodeArgs& a, int bh, int f, 
 }
 
 // Routing of the unit (chunk top-k, then group top-g) and attention of its GQ
-// query heads over the routed groups' rows, merged with the forced partials.
+// query heads over share r of the routed groups' rows (routed blocks r, r + R,
+// ... of the 16-row blocks), merged with the other partials.
 template <typename T, int D, int GQ>
-__device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, DecodeSmem<GQ, D>& sm) {
+__device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, int r, DecodeSmem<GQ, D>& sm) {
   const KParams& kp = a.kp;
   const int F = a.forced_wgs;
+  const int R = a.routing_wgs;
+  const bool writer = r == 0;  // the one routing workgroup that writes the lists
   const int b = bh / kp.Hkv, h = bh % kp.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -315,7 +310,8 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
   const T* Qb = static_cast<const T*>(a.Q) + (static_cast<int64_t>(b) * kp.Hq + h * GQ) * D;
   const T* Kb = static_cast<const T*>(a.K) + static_cast<int64_t>(bh) * kp.n_cap * D;
   const T* Vb = static_cast<const T*>(a.V) + static_cast<int64_t>(bh) * kp.n_cap * D;
-  const float* parts = a.partials + static_cast<int64_t>(bh) * (F + 1) * attn_part_stride<D, GQ>();
+  const float* parts = a.partials + static_cast<int64_t>(bh) * (F + R) * attn_part_stride<D, GQ>();
+  const uint32_t others = ((1u << (F + R)) - 1u) & ~(1u << (F + r));
   uint32_t* counter = a.sync + 4 * static_cast<int64_t>(bh);
   const float* ctab = a.chunk_sum + (static_cast<int64_t>(bh) * kp.n_chunks_cap + kp.n_sink) * D;
   auto crow = [&](int i) { return ctab + static_cast<int64_t>(i) * D; };
@@ -331,6 +327,7 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
   const int t = a.seq_len[b] + a.pos_offset;
   if (t < 0 || t >= kp.n_cap) {
     // a position outside the cache: empty index lists and NaN output
+    if (!writer) return;
     if (a.chunk_idx)
       for (int i = tid; i < kp.top_k; i += kDecThreads) a.chunk_idx[static_cast<int64_t>(bh) * kp.top_k + i] = -1;
     if (a.group_idx)
@@ -367,11 +364,12 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
   scan_scores<D, GQ, true>(sm.qs, nM, kp.inv_sqrt_d, crow, sm.sc, first);
   __syncthreads();
   const int cnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nM, kp.top_k, sm.selc, sm.sel);
-  // ---- have all forced workgroups arrived?  Then this one is the last: it
-  // arrives now (resetting the count) and prefetches their slots below.
+  // ---- a lone routing workgroup: have all forced workgroups arrived?  Then
+  // this one is the last: it arrives now (resetting the count) and prefetches
+  // their slots below.
   if (tid == 0) {
     int early = 0;
-    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(F)) {
+    if (R == 1 && __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == static_cast<uint32_t>(F)) {
       __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       early = 1;
@@ -379,7 +377,8 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
     sm.early = early;
   }
   int32_t* ci = a.chunk_idx + static_cast<int64_t>(bh) * kp.top_k;
-  for (int i = tid; i < kp.top_k; i += kDecThreads) ci[i] = i < cnt ? kp.n_sink + sm.selc[i] : -1;
+  if (writer)
+    for (int i = tid; i < kp.top_k; i += kDecThreads) ci[i] = i < cnt ? kp.n_sink + sm.selc[i] : -1;
   // ---- level 2: score the groups of the routed chunks, keep the top-g
   const int m = kp.m;
   const int nG = cnt * m;
@@ -403,7 +402,7 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
       v = (kp.n_sink + sm.selc[sg / m]) * m + sg % m;
       sm.gl[i] = v;
     }
-    a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = v;
+    if (writer) a.group_idx[static_cast<int64_t>(bh) * kp.top_g + i] = v;
   }
   __syncthreads();
   }  // routing
@@ -423,7 +422,7 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
       vr = Vb + tok * D;
       return true;
     };
-    st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
+    st.template run<kRoutedPF>(0, r * kDecWaves + wid, nblk, R * kDecWaves, kp.scale_log2, row);
   } else {
     // slots past the list and rows after the query are masked and point at
     // the query's own row
@@ -435,18 +434,18 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, Decode
       vr = Vb + (ok ? tok : t) * D;
       return ok;
     };
-    st.template run<kRoutedPF>(0, wid, nblk, kDecWaves, kp.scale_log2, row);
+    st.template run<kRoutedPF>(0, r * kDecWaves + wid, nblk, R * kDecWaves, kp.scale_log2, row);
   }
   attn_waves_to_lds(st, sm.mg);
+  attn_merge_waves_rest(sm.mg);
   if (early) {
     unstash_parts<D, GQ>(sm.sc, F, pr);
-    merge_store_waves<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
+    merge_store<D, GQ>(sm.mg, pr, F, unit_out(a, bh, GQ));
     return;
   }
-  attn_merge_waves_rest(sm.mg);
-  if (publish_arrive<D, GQ>(a, bh, F, sm.mg)) {
-    load_parts<D, GQ>(parts, (1u << F) - 1u, pr);
-    merge_store<D, GQ>(sm.mg, pr, unit_out(a, bh, GQ));
+  if (publish_arrive<D, GQ>(a, bh, F + r, sm.mg)) {
+    load_parts<D, GQ>(parts, others, pr);
+    merge_store<D, GQ>(sm.mg, pr, F + r, unit_out(a, bh, GQ));
   }
 }
 
@@ -460,20 +459,21 @@ __device__ __forceinline__ void unit_of(const DecodeArgs& a, int& bh, int& role)
   bh = (slot % a.units_per_xcd) * kXcds + x % kXcds;
 }
 
-// One launch per step.  Roles: 0 routing and routed attention, 1..F forced.
+// One launch per step.  Roles: 0..R-1 routing and routed attention, R..R+F-1
+// forced.
 template <typename T, int D, int GQ>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeArgs a) {
   int bh, role;
   unit_of(a, bh, role);
   const KParams& kp = a.kp;
-  if (bh >= kp.B * kp.Hkv || role > a.forced_wgs) return;
+  if (bh >= kp.B * kp.Hkv || role >= a.routing_wgs + a.forced_wgs) return;
   __shared__ DecodeSmem<GQ, D> sm;
-  if (role == 0) {
-    routing_role<T, D, GQ>(a, bh, sm);
+  if (role < a.routing_wgs) {
+    routing_role<T, D, GQ>(a, bh, role, sm);
   } else {
     const int t = a.seq_len[bh / kp.Hkv] + a.pos_offset;
-    if (t < 0 || t >= kp.n_cap) return;  // NaN output written by the routing role
-    forced_role<T, D, GQ>(a, bh, role - 1, t, sm);
+    if (t < 0 || t >= kp.n_cap) return;  // NaN output written by routing workgroup 0
+    forced_role<T, D, GQ>(a, bh, role - a.routing_wgs, t, sm);
   }
 }
 
@@ -489,7 +489,7 @@ bool decode_fused_supported(const KParams& kp) {
 template <typename T, int D, int GQ>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const unsigned per_role = static_cast<unsigned>(kXcds) * a.units_per_xcd;
-  decode_step_kernel<T, D, GQ><<<per_role * (1 + a.forced_wgs), kDecThreads, 0, st>>>(a);
+  decode_step_kernel<T, D, GQ><<<per_role * (a.routing_wgs + a.forced_wgs), kDecThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -504,7 +504,8 @@ static hipError_t launch_gq(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode_step(const DecodeArgs& a, bool bf16_in, hipStream_t st) {
-  if (a.forced_wgs < 1 || a.forced_wgs > kDecMaxForced) return hipErrorInvalidValue;
+  if (a.forced_wgs < 1 || a.forced_wgs > kDecMaxForced || a.routing_wgs < 1 || a.routing_wgs > kDecMaxRouting)
+    return hipErrorInvalidValue;
   if (bf16_in) return a.kp.d == 64 ? launch_gq<bf16, 64>(a, st) : launch_gq<bf16, 128>(a, st);
   return a.kp.d == 64 ? launch_gq<float, 64>(a, st) : launch_gq<float, 128>(a, st);
 }

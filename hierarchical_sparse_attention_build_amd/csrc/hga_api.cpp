@@ -3,6 +3,8 @@
 // launch goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -184,10 +186,13 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, bool bf16_i
   return a;
 }
 
-// Decode step in one launch: per (b, kv head), one workgroup routes and
-// attends the routed rows, F attend the forced window; the last merges.
+// Decode step in one launch: per (b, kv head), R workgroups route and attend
+// shares of the routed rows, F attend the forced window; the last merges.
 #ifndef HGA_DECODE_FORCED_WGS
 #define HGA_DECODE_FORCED_WGS 2
+#endif
+#ifndef HGA_DECODE_ROUTING_WGS
+#define HGA_DECODE_ROUTING_WGS 2
 #endif
 
 struct FusedPlan {
@@ -209,9 +214,30 @@ FusedPlan plan_fused(const KParams& kp, size_t base) {
   r.sync_off = off;
   off = align256(off + static_cast<size_t>(units) * 4 * sizeof(uint32_t));
   r.partials_off = off;
-  off = align256(off + static_cast<size_t>(units) * (r.forced_wgs + 1) * kp.gq * (kp.d + 2) * sizeof(float));
+  off = align256(off + static_cast<size_t>(units) * (r.forced_wgs + kDecMaxRouting) * kp.gq * (kp.d + 2) *
+                           sizeof(float));
   r.bytes = off - base;
   return r;
+}
+
+// Compute units of the current device (0 if it cannot be queried), cached.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Routing workgroups per unit: a second one (which repeats the routing and
+// takes half of the routed rows) only while every workgroup of the launch
+// still has a compute unit of its own; sharing one would slow both streams.
+int fused_routing_wgs(const KParams& kp, const FusedPlan& fp) {
+  const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
+  const int want = std::max(1, std::min(HGA_DECODE_ROUTING_WGS, kDecMaxRouting));
+  return want > 1 && units * (fp.forced_wgs + want) <= device_cus() ? want : 1;
 }
 
 struct IdxPlan {
@@ -497,6 +523,7 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
     da.forced_wgs = fp.forced_wgs;
     da.forced_bpw = fp.forced_bpw;
+    da.routing_wgs = fused_routing_wgs(kp, fp);
     da.units_per_xcd = fp.units_per_xcd;
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);
@@ -639,6 +666,7 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
     da.forced_wgs = fp.forced_wgs;
     da.forced_bpw = fp.forced_bpw;
+    da.routing_wgs = fused_routing_wgs(kp, fp);
     da.units_per_xcd = fp.units_per_xcd;
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);

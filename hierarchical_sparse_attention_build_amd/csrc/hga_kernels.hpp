@@ -97,8 +97,9 @@ struct DecodeArgs {
   int32_t out_bf16;
   int32_t forced_wgs;        // forced-window workgroups per (b, kv head)
   int32_t forced_bpw;        // 16-row blocks of forced rows per forced workgroup
+  int32_t routing_wgs;       // routing workgroups per (b, kv head); each routes and attends a share of the routed rows
   int32_t units_per_xcd;     // ceil(B*Hkv / kXcds)
-  float* partials;           // ws [B*Hkv, forced_wgs + 1, gq * (d + 2)]: partial results
+  float* partials;           // ws [B*Hkv, forced_wgs + routing_wgs, gq * (d + 2)]: partial results
   uint32_t* sync;            // ws [B*Hkv, 4]: arrival counter of each unit (zero between calls)
   const int32_t* routes_in;  // nullable [B*Hkv, top_g]: given group lists (no routing; chunk_idx,
                              // group_idx, chunk_sum and group_sum unused)
@@ -166,6 +167,8 @@ hipError_t launch_warm_fill(const WarmArgs& a, hipStream_t st);
 constexpr int kXcds = 8;             // accelerator dies; workgroups are dealt to them in turn
 constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per unit
 constexpr int kDecMaxForced = 2;    // forced-window workgroups per (b, kv head)
+constexpr int kDecMaxRouting = 2;   // routing workgroups per (b, kv head)
+constexpr int kDecMaxParts = kDecMaxForced + kDecMaxRouting;
 bool decode_fused_supported(const KParams& kp);
 hipError_t launch_decode_step(const DecodeArgs& a, bool bf16_in, hipStream_t st);
 // Prefill attention on the matrix cores (bf16, C = 64, Hq/Hkv <= 4, G | 64).
