@@ -34,6 +34,10 @@ constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kForcedPF = 2;  // forced blocks in flight per wave
 constexpr int kRoutedPF = 2;  // routed blocks in flight per wave
+// Widest selection compiled in: 4 keys per lane covers 2048 candidate chunks
+// and k <= 32 (wider selections go to the separate routing kernel); the 8-
+// and 16-key variants would push the kernel's scalar registers into spills.
+constexpr int kDecSelE = 4;
 
 template <int GQ, int D>
 struct DecodeSmem {
@@ -363,7 +367,7 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, int r,
   const int nM = kp.top_k > 0 ? max(0, j - kp.n_local - kp.n_sink) : 0;
   scan_scores<D, GQ, true>(sm.qs, nM, kp.inv_sqrt_d, crow, sm.sc, first);
   __syncthreads();
-  const int cnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nM, kp.top_k, sm.selc, sm.sel);
+  const int cnt = block_select<kDecThreads, kDecSelE>([&](int i) { return sm.sc[i]; }, nM, kp.top_k, sm.selc, sm.sel);
   // ---- a lone routing workgroup: have all forced workgroups arrived?  Then
   // this one is the last: it arrives now (resetting the count) and prefetches
   // their slots below.
@@ -392,7 +396,7 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, int r,
   __syncthreads();
   early = sm.early != 0;
   if (early) load_parts<D, GQ>(parts, (1u << F) - 1u, pr);
-  gcnt = block_select<kDecThreads>([&](int i) { return sm.sc[i]; }, nG, kp.top_g, sm.selg, sm.sel);
+  gcnt = block_select<kDecThreads, kDecSelE>([&](int i) { return sm.sc[i]; }, nG, kp.top_g, sm.selg, sm.sel);
   // the prefetched slots wait in LDS (the scores are no longer needed)
   if (early) stash_parts<D, GQ>(pr, sm.sc);
   for (int i = tid; i < kp.top_g; i += kDecThreads) {
@@ -481,9 +485,9 @@ bool decode_fused_supported(const KParams& kp) {
   const int64_t max_cand = std::max<int64_t>(0, kp.n_chunks_cap - 1 - kp.n_local - kp.n_sink);
   return (kp.gq == 1 || kp.gq == 2 || kp.gq == 4) && (kp.d == 64 || kp.d == 128) && kp.log2C >= 0 &&
          kp.log2G >= 0 &&
-         max_cand <= kDecMaxScores && block_select_fits<kDecThreads>(static_cast<int>(max_cand), kp.top_k) &&
+         max_cand <= kDecMaxScores && block_select_fits<kDecThreads, kDecSelE>(static_cast<int>(max_cand), kp.top_k) &&
          static_cast<int64_t>(kp.top_k) * kp.m <= kDecMaxScores &&
-         block_select_fits<kDecThreads>(kp.top_k * kp.m, kp.top_g) && kp.top_g <= kSelMaxK;
+         block_select_fits<kDecThreads, kDecSelE>(kp.top_k * kp.m, kp.top_g) && kp.top_g <= kSelMaxK;
 }
 
 template <typename T, int D, int GQ>

@@ -40,12 +40,9 @@ __device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[E], int k
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
-    uint64_t b[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) b[e] = ballot64(key[e] >= cand);
     int c = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(b[e]);
+    for (int e = 0; e < E; ++e) c += __popcll(ballot64(key[e] >= cand));
     if (c >= k) {
       T = cand;
       if (c == k) break;
@@ -104,15 +101,27 @@ __device__ __forceinline__ void wave_topk(KeyFn key_of, int k, bool all, OutFn o
   }
 }
 
-// wave_topk with the slot count rounded up to 1, 2, 4, 8 or 16 (at most kSelMaxE).
-template <typename KeyFn, typename OutFn>
+// wave_topk with the slot count rounded up to 1, 2, 4, 8 or 16 (at most
+// MaxE, a power of two <= kSelMaxE; slots <= MaxE).  Only the variants up to
+// MaxE are compiled: a kernel that inlines the 8- and 16-slot ones needs more
+// scalar registers at its peak, and the excess spills to vector lanes with
+// reloads all over the kernel.
+template <int MaxE, typename KeyFn, typename OutFn>
 __device__ __forceinline__ void wave_topk_n(int slots, KeyFn key_of, int k, bool all, OutFn out) {
+  static_assert(MaxE >= 2 && MaxE <= kSelMaxE && (MaxE & (MaxE - 1)) == 0, "MaxE: 2, 4, 8 or 16");
   if (slots <= 0) return;
-  if (slots <= 1) wave_topk<1>(key_of, k, all, out);
-  else if (slots <= 2) wave_topk<2>(key_of, k, all, out);
-  else if (slots <= 4) wave_topk<4>(key_of, k, all, out);
-  else if (slots <= 8) wave_topk<8>(key_of, k, all, out);
-  else wave_topk<kSelMaxE>(key_of, k, all, out);
+  if (slots <= 1) {
+    wave_topk<1>(key_of, k, all, out);
+  } else if (MaxE == 2 || slots <= 2) {
+    wave_topk<2>(key_of, k, all, out);
+  } else if constexpr (MaxE >= 4) {
+    if (MaxE == 4 || slots <= 4) {
+      wave_topk<4>(key_of, k, all, out);
+    } else if constexpr (MaxE >= 8) {
+      if (MaxE == 8 || slots <= 8) wave_topk<8>(key_of, k, all, out);
+      else wave_topk<kSelMaxE>(key_of, k, all, out);
+    }
+  }
 }
 
 template <int NT>
@@ -122,17 +131,22 @@ struct SelSmem {
   int pos[NW * kSelMaxK];
 };
 
-// True when block_select handles (n, k) for a workgroup of NT threads.
-template <int NT>
+// True when block_select<NT, MaxE> handles (n, k): at most MaxE keys per lane
+// in either phase.  Monotone in n: it holds for every smaller n as well.
+template <int NT, int MaxE = kSelMaxE>
 __host__ __device__ constexpr bool block_select_fits(int n, int k) {
-  return k <= kSelMaxK && n <= NT * kSelMaxE && (NT / kWave) * k <= kWave * kSelMaxE;
+  constexpr int NW = NT / kWave;
+  if (k > kSelMaxK) return false;
+  if (n <= k || n <= 2 * kWave) return true;  // nothing to select, or one wave with two keys per lane
+  const int q = (n + NW - 1) / NW;
+  return q <= kWave * MaxE && NW * (k < q ? k : q) <= kWave * MaxE;
 }
 
 // Exact selection of the min(n, k) best of sc(0..n) (sc reads LDS or memory);
 // the chosen positions go to sel[] (LDS) in ascending order.  Every thread of
 // the workgroup calls it; returns min(n, k) and ends with a barrier.
-// Requires block_select_fits<NT>(n, k).
-template <int NT, typename ScoreFn>
+// Requires block_select_fits<NT, MaxE>(n, k).
+template <int NT, int MaxE = kSelMaxE, typename ScoreFn>
 __device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
@@ -152,7 +166,7 @@ __device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm)
   if (n <= 2 * kWave) {
     // one wave, at most two keys per lane
     if (wid == 0)
-      wave_topk_n((n + kWave - 1) / kWave, [&](int e) { return key_at(e * kWave + lane, n); }, k, false,
+      wave_topk_n<MaxE>((n + kWave - 1) / kWave, [&](int e) { return key_at(e * kWave + lane, n); }, k, false,
                   [&](int r, int e, uint32_t) { sel[r] = e * kWave + lane; });
     __syncthreads();
     return k;
@@ -168,7 +182,7 @@ __device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm)
   const int kw = min(k, nw);
   // with n > 128 and at most 16 waves, every wave but the last has a full share q
   const int start = min(k, q) * wid;
-  wave_topk_n((nw + kWave - 1) / kWave, [&](int e) { return key_at(lo + e * kWave + lane, hi); }, kw, kw == nw,
+  wave_topk_n<MaxE>((nw + kWave - 1) / kWave, [&](int e) { return key_at(lo + e * kWave + lane, hi); }, kw, kw == nw,
               [&](int r, int e, uint32_t kk) {
                 sm.key[start + r] = kk;
                 sm.pos[start + r] = lo + e * kWave + lane;
@@ -178,7 +192,7 @@ __device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm)
   // phase 2: wave 0 selects k among the winners (ascending positions)
   if (wid == 0) {
     const int n2 = min(k, q) * (NW - 1) + min(k, max(0, n - (NW - 1) * q));
-    wave_topk_n((n2 + kWave - 1) / kWave,
+    wave_topk_n<MaxE>((n2 + kWave - 1) / kWave,
                 [&](int e) {
                   const int jj = e * kWave + lane;
                   const uint32_t kk = sm.key[min(jj, n2 - 1)];

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
     }
     if (misses > 0) {
       // key of slot s: ~stamp, or 0 (never taken) for a slot this step uses
-      wave_topk_n((S + kWave - 1) / kWave,
+      wave_topk_n<kSelMaxE>((S + kWave - 1) / kWave,
                   [&](int e) {
                     const int s = e * kWave + lane;
                     const int st = stamps[min(s, S - 1)];
