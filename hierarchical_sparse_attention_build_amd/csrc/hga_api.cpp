@@ -155,10 +155,10 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, bool bf16_i
   const int64_t rows = static_cast<int64_t>(kp.B) * kp.Hkv * nq;
   const int max_blocks = static_cast<int>(cdiv(attend_max_slots(kp), kAttBlockRows));
   // enough workgroups to give every CU work, each with several 16-row blocks;
-  // with more than 4 query heads per KV head the parts are larger and their
-  // merge costs more than the parallelism gains (8 heads, 128K, given lists:
-  // 61 us at 512 workgroups, 38 us at 128-192)
-  const int64_t target = kp.gq > 4 ? 1024 / kp.gq : 512;
+  // with more than 4 query heads per KV head the parts are larger and the
+  // last workgroup's merge of them costs more, so fewer (8 heads, 128K, given
+  // lists: 23 us at 256 workgroups, 25 us at 512, 30 us at 128)
+  const int64_t target = kp.gq > 4 ? 2048 / kp.gq : 512;
   const int splits = static_cast<int>(
       std::min<int64_t>(std::min(max_blocks, kAttMaxParts / 2), std::max<int64_t>(1, cdiv(target, rows))));
   a.tps = static_cast<int>(cdiv(max_blocks, splits));

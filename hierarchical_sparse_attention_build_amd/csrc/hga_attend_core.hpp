@@ -685,8 +685,11 @@ __device__ __forceinline__ void attn_publish_and_merge(AttnMergeSmem<GQ, D, NWV>
         if (e >= GQ * D) continue;
         const int hh = e / D;
         const float M = sm.M[hh];
-        for (int q = 0; q < np; ++q) {
-          const float mp = sm.pm[q * GQ + hh];
+        // unrolled to the register array's bound, so that ov stays in registers
+        // (a loop to np would index it at run time and place it in scratch)
+#pragma unroll
+        for (int q = 0; q < kPR; ++q) {
+          const float mp = q < np ? sm.pm[q * GQ + hh] : -__builtin_huge_valf();
           if (mp != -__builtin_huge_valf()) num[r] += exp2f(mp - M) * ov[q][r];
         }
       }
