@@ -188,16 +188,13 @@ AttendPlan plan_attend(const KParams& kp, int64_t nq, bool two_part, bool bf16_i
 
 // Decode step in one launch: per (b, kv head), R workgroups route and attend
 // shares of the routed rows, F attend the forced window; the last merges.
-#ifndef HGA_DECODE_FORCED_WGS
-#define HGA_DECODE_FORCED_WGS 2
-#endif
 #ifndef HGA_DECODE_ROUTING_WGS
 #define HGA_DECODE_ROUTING_WGS 2
 #endif
 
 struct FusedPlan {
   bool use;
-  int forced_wgs, forced_bpw, units_per_xcd;
+  int forced_blocks, units_per_xcd;
   size_t sync_off, partials_off, bytes;
 };
 
@@ -205,17 +202,14 @@ FusedPlan plan_fused(const KParams& kp, size_t base) {
   FusedPlan r{};
   r.use = decode_fused_supported(kp);
   if (!r.use) return r;
-  const int fblocks = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kAttBlockRows));
-  r.forced_wgs = std::min(std::min(HGA_DECODE_FORCED_WGS, fblocks), kDecMaxForced);
-  r.forced_bpw = static_cast<int>(cdiv(fblocks, r.forced_wgs));
+  r.forced_blocks = static_cast<int>(cdiv(static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C, kAttBlockRows));
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   r.units_per_xcd = static_cast<int>(cdiv(units, kXcds));
   size_t off = base;
   r.sync_off = off;
   off = align256(off + static_cast<size_t>(units) * 4 * sizeof(uint32_t));
   r.partials_off = off;
-  off = align256(off + static_cast<size_t>(units) * (r.forced_wgs + kDecMaxRouting) * kp.gq * (kp.d + 2) *
-                           sizeof(float));
+  off = align256(off + static_cast<size_t>(units) * kDecMaxParts * kp.gq * (kp.d + 2) * sizeof(float));
   r.bytes = off - base;
   return r;
 }
@@ -231,13 +225,20 @@ int device_cus() {
   return n;
 }
 
-// Routing workgroups per unit: a second one (which repeats the routing and
-// takes half of the routed rows) only while every workgroup of the launch
-// still has a compute unit of its own; sharing one would slow both streams.
-int fused_routing_wgs(const KParams& kp, const FusedPlan& fp) {
+// Workgroups per unit of a decode launch.  Two routing workgroups (each
+// repeats the routing and takes half of the routed rows) and one forced one
+// while every workgroup of the launch has a compute unit of its own; else one
+// routing workgroup, which finishes last by far, and two forced ones (decode_32k,
+// B = 8: 21.2 us with 2 + 1, 21.5 with 2 + 2, 21.6 with 3 + 1; with one routing
+// workgroup 22.6 us with two forced, 23.1 with one).
+void fused_shape(const KParams& kp, const FusedPlan& fp, DecodeArgs& da) {
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   const int want = std::max(1, std::min(HGA_DECODE_ROUTING_WGS, kDecMaxRouting));
-  return want > 1 && units * (fp.forced_wgs + want) <= device_cus() ? want : 1;
+  const bool split = want > 1 && units * (want + 1) <= device_cus();
+  da.routing_wgs = split ? want : 1;
+  da.forced_wgs = std::max(1, std::min(std::min(split ? 1 : 2, fp.forced_blocks), kDecMaxForced));
+  da.forced_bpw = static_cast<int>(cdiv(fp.forced_blocks, da.forced_wgs));
+  da.units_per_xcd = fp.units_per_xcd;
 }
 
 struct IdxPlan {
@@ -521,10 +522,7 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
     da.routes_in = group_idx;
     da.O = O;
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
-    da.forced_wgs = fp.forced_wgs;
-    da.forced_bpw = fp.forced_bpw;
-    da.routing_wgs = fused_routing_wgs(kp, fp);
-    da.units_per_xcd = fp.units_per_xcd;
+    fused_shape(kp, fp, da);
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);
     HGA_TRY_HIP(launch_decode_step(da, bf, static_cast<hipStream_t>(stream)), "attend (decode step)");
@@ -664,10 +662,7 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
     da.group_idx = gi;
     da.O = O;
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
-    da.forced_wgs = fp.forced_wgs;
-    da.forced_bpw = fp.forced_bpw;
-    da.routing_wgs = fused_routing_wgs(kp, fp);
-    da.units_per_xcd = fp.units_per_xcd;
+    fused_shape(kp, fp, da);
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);
     da.pos_offset = -1;
