@@ -34,6 +34,7 @@ constexpr int kRounds = 4;                                      // rounds in fli
 constexpr int kQB = 4;                                          // query vectors per register batch
 constexpr int kSliceRows = kRowsPerRound * kRounds;             // candidate chunks per workgroup
 constexpr int kLdsCand = 2048;                                  // candidates staged in LDS for the selections
+constexpr int kRouteQs = 16 * 128;                              // query elements staged in LDS (one query per sequence)
 
 struct RouteSmem {
   union {  // scratch of the selection in use
@@ -46,6 +47,7 @@ struct RouteSmem {
   int sel_groups[1024];
   float cand_s[kLdsCand];
   int cand_i[kLdsCand];
+  float qs[kRouteQs];  // the unit's query vectors in fp32, when they fit (one query per sequence)
   int is_last;
 };
 
@@ -58,10 +60,12 @@ __device__ __forceinline__ int slice_count(int x, int nM, int cps, int k) {
 
 // put(i, max over the unit's query vectors of q . row(i) / sqrt(d)) for i in
 // [0, n); only lanes with lane % 8 == 0 call put.  row(i) is a float32 row.
+// The query vectors come from qs (LDS, fp32, vector v at qs + v * D) when it
+// is set, else from global memory at qbase.
 template <typename T, int D, typename RowFn, typename PutFn>
 __device__ __forceinline__ void score_rows(const T* __restrict__ qbase, int64_t head_stride,
-                                           int rows_per_head, int nqv, const KParams& kp, int n,
-                                           RowFn row, PutFn put) {
+                                           int rows_per_head, int nqv, const float* qs, const KParams& kp,
+                                           int n, RowFn row, PutFn put) {
   constexpr int NV = D / 32;  // float4 pieces per lane per row
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
@@ -85,12 +89,17 @@ __device__ __forceinline__ void score_rows(const T* __restrict__ qbase, int64_t 
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
         const int vv = v0 + qb < nqv ? v0 + qb : nqv - 1;
-        const T* qr = qbase + (vv / rows_per_head) * head_stride + static_cast<int64_t>(vv % rows_per_head) * D;
+        if (qs) {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          const int d0 = v * 32 + piece * 4;
-          q[qb][v] = make_float4(elem<T>::get(qr, d0), elem<T>::get(qr, d0 + 1), elem<T>::get(qr, d0 + 2),
-                                 elem<T>::get(qr, d0 + 3));
+          for (int v = 0; v < NV; ++v) q[qb][v] = *reinterpret_cast<const float4*>(qs + vv * D + v * 32 + piece * 4);
+        } else {
+          const T* qr = qbase + (vv / rows_per_head) * head_stride + static_cast<int64_t>(vv % rows_per_head) * D;
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            const int d0 = v * 32 + piece * 4;
+            q[qb][v] = make_float4(elem<T>::get(qr, d0), elem<T>::get(qr, d0 + 1), elem<T>::get(qr, d0 + 2),
+                                   elem<T>::get(qr, d0 + 3));
+          }
         }
       }
 #pragma unroll
@@ -169,13 +178,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
                    ((static_cast<int64_t>(b) * kp.Hq + static_cast<int64_t>(h) * kp.gq) * a.nq +
                     (prefill ? static_cast<int64_t>(u) * kp.C : 0)) * D;
   const int64_t head_stride = a.nq * D;
+  // one query per sequence: its vectors once into LDS (fp32), instead of 2-byte
+  // global loads of each vector for every batch of rows in both scans
+  const float* qs = !prefill && nqv * D <= kRouteQs ? sm.qs : nullptr;
+  if (qs)
+    for (int e = threadIdx.x; e < nqv * D; e += kRouteThreads) sm.qs[e] = elem<T>::get(qbase, e);
+  __syncthreads();
 
   float* cand_s = a.scores + unit * kp.n_chunks_cap;   // published (score, chunk) pairs
   int* cand_i = a.cand_ids + unit * kp.n_chunks_cap;
   const float* ctab = a.chunk_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * D;
   float* sc_out = a.scores_out ? a.scores_out + static_cast<int64_t>(bh) * kp.n_chunks_cap : nullptr;
   if (n_here > 0) {
-    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, kp, n_here,
+    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, qs, kp, n_here,
                      [&](int i) { return ctab + static_cast<int64_t>(c_lo + i) * D; },
                      [&](int i, float v) {
                        sm.loc[i] = v;
@@ -241,7 +256,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   const float* gtab = a.group_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m * D;
   float* gsc = nG <= kLdsCand ? sm.cand_s : a.gscores + unit * static_cast<int64_t>(kp.top_k) * kp.m;
   if (nG > 0) {
-    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, kp, nG,
+    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, qs, kp, nG,
                      [&](int i) {
                        const int64_t gid = static_cast<int64_t>(sm.sel_chunks[i / m]) * m + i % m;
                        return gtab + gid * D;
