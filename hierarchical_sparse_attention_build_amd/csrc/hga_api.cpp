@@ -225,18 +225,24 @@ int device_cus() {
   return n;
 }
 
-// Workgroups per unit of a decode launch.  Two routing workgroups (each
-// repeats the routing and takes half of the routed rows) and one forced one
-// while every workgroup of the launch has a compute unit of its own; else one
-// routing workgroup, which finishes last by far, and two forced ones (decode_32k,
-// B = 8: 21.2 us with 2 + 1, 21.5 with 2 + 2, 21.6 with 3 + 1; with one routing
-// workgroup 22.6 us with two forced, 23.1 with one).
-void fused_shape(const KParams& kp, const FusedPlan& fp, DecodeArgs& da) {
+// Workgroups per unit of a decode launch.  Routing: two routing workgroups
+// (each repeats the routing and takes half of the routed rows) and one forced
+// one while every workgroup of the launch has a compute unit of its own; else
+// one routing workgroup, which finishes last by far, and two forced ones
+// (decode_32k, B = 8: 21.2 us with 2 + 1, 21.5 with 2 + 2, 21.6 with 3 + 1;
+// with one routing workgroup 22.6 us with two forced, 23.1 with one).  Given
+// lists (no routing): the forced rows outnumber each routing workgroup's
+// share, so two forced workgroups, with two routing ones while they fit
+// (12.3 us against 14.0 with one forced).  No routed rows at all (top_k or
+// top_g = 0, streaming heads): one routing workgroup and two forced.
+void fused_shape(const KParams& kp, const FusedPlan& fp, bool given, DecodeArgs& da) {
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   const int want = std::max(1, std::min(HGA_DECODE_ROUTING_WGS, kDecMaxRouting));
-  const bool split = want > 1 && units * (want + 1) <= device_cus();
+  const bool routed = kp.top_k > 0 && kp.top_g > 0;
+  const int forced_if_split = given ? 2 : 1;
+  const bool split = routed && want > 1 && units * (want + forced_if_split) <= device_cus();
   da.routing_wgs = split ? want : 1;
-  da.forced_wgs = std::max(1, std::min(std::min(split ? 1 : 2, fp.forced_blocks), kDecMaxForced));
+  da.forced_wgs = std::max(1, std::min(std::min(split ? forced_if_split : 2, fp.forced_blocks), kDecMaxForced));
   da.forced_bpw = static_cast<int>(cdiv(fp.forced_blocks, da.forced_wgs));
   da.units_per_xcd = fp.units_per_xcd;
 }
@@ -522,7 +528,7 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
     da.routes_in = group_idx;
     da.O = O;
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
-    fused_shape(kp, fp, da);
+    fused_shape(kp, fp, true, da);
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);
     HGA_TRY_HIP(launch_decode_step(da, bf, static_cast<hipStream_t>(stream)), "attend (decode step)");
@@ -662,7 +668,7 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
     da.group_idx = gi;
     da.O = O;
     da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
-    fused_shape(kp, fp, da);
+    fused_shape(kp, fp, false, da);
     da.partials = at<float>(ws, fp.partials_off);
     da.sync = at<uint32_t>(ws, fp.sync_off);
     da.pos_offset = -1;
