@@ -234,6 +234,52 @@ def test_decode_full_size_32k(hga):
     _run_decode_e2e(hga, s, w)
 
 
+@pytest.mark.timeout(300)
+def test_decode_full_size_64k_sampled(hga):
+    """The long-context decode workload at full size (B=16, 64K context, 128
+    units: one routing and two forced workgroups per unit, the launch that is
+    benchmarked); the routing and output of six sampled units against the
+    oracle, computed on those units' own slices of Q, K and V."""
+    s = W.spec("decode_64k")
+    say(f"[decode e2e full, sampled units] decode_64k seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    p = params_of(s)
+    B, H, n = s.batch, s.n_kv_heads, s.n_tokens
+    gq = s.n_q_heads // H
+    K, V, Q = dev(w.K, s.dtype), dev(w.V, s.dtype), dev(w.Q, s.dtype)
+    cs, gs = _summ_tables(s)
+    seq = torch.from_numpy(w.seq_len.astype(np.int32)).cuda()
+    jq = int((w.seq_len.min() - 1) // s.chunk_size)
+    hga.build_summaries(p, K, n, 0, jq, cs, gs)
+    ci = torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, 1, s.head_dim), device="cuda")
+    hga.decode(p, Q, K, V, n, seq, cs, gs, out, hga.workspace(p, hga.OP_DECODE, 1, n), chunk_idx=ci, group_idx=gi)
+    torch.cuda.synchronize()
+    ci_n, gi_n, got = ci.cpu().numpy(), gi.cpu().numpy(), out.cpu().numpy()
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(s.seed)
+    sample = list(zip(rng.choice(B, 6, replace=False).tolist(), rng.integers(0, H, 6).tolist()))
+    n_unique = 0
+    for b, h in sample:
+        Kf, Vf = f64(w.K[b:b + 1, h:h + 1], s.dtype), f64(w.V[b:b + 1, h:h + 1], s.dtype)
+        Qf = f64(w.Q[b:b + 1, h * gq:(h + 1) * gq], s.dtype)
+        q_pos = (w.seq_len[b:b + 1] - 1).astype(np.int64)
+        ocs, ogs = O.build_summaries(Kf, cfg)
+        or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, 1)
+        _, unique = check_routing(ci_n[b:b + 1, h:h + 1], gi_n[b:b + 1, h:h + 1], or_ci, or_gi, diags,
+                                  s.top_k, s.top_g)
+        if not unique:
+            continue
+        Oo, _ = O.attend(Qf, q_pos, Kf, Vf, or_gi, cfg, 1)
+        e = max_abs(got[b, h * gq:(h + 1) * gq, 0], Oo[0, :, 0])
+        say(f"  unit (b={b}, h={h}): O max-abs {e:.3e}")
+        assert e <= TOL[s.dtype]
+        n_unique += 1
+    assert n_unique >= len(sample) // 2
+
+
 def test_decode_ragged_and_short(hga):
     """Per-sequence lengths from 1 token up to the capacity, partial current chunks,
     sequences with no routing candidates yet."""
