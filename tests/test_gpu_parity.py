@@ -550,6 +550,69 @@ def test_offload_decode(hga):
     assert max_abs(cs.cpu().numpy()[:, :, j], ocs[:, :, j]) < 1e-5
 
 
+@pytest.mark.timeout(300)
+def test_offload_decode_full_size_sampled(hga):
+    """Cold tier on the full 128K offload workload (B=4, 64/8 heads, top_k 64,
+    top_g 128), K/V in pinned host memory: the routing, output and completed
+    chunk's summary of six sampled units against the oracle, computed on
+    those units' own slices of Q, K and V."""
+    s = W.spec("offload_decode_128k")
+    say(f"[offload decode full, sampled units] seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    p = params_of(s)
+    B, H, n, C, d = s.batch, s.n_kv_heads, s.n_tokens, s.chunk_size, s.head_dim
+    gq = s.n_q_heads // H
+    K_host = W.to_torch(w.K, s.dtype, pin=True)
+    V_host = W.to_torch(w.V, s.dtype, pin=True)
+    hot_chunks = s.n_sink + s.n_local + 1
+    K_hot = torch.zeros((B, H, hot_chunks * C, d), dtype=K_host.dtype)
+    V_hot = torch.zeros_like(K_hot)
+    j = (n - 1) // C
+    for c in list(range(s.n_sink)) + list(range(j - s.n_local, j + 1)):
+        sl = hga.hot_slot(c, s.n_sink, s.n_local)
+        K_hot[:, :, sl * C:(sl + 1) * C] = K_host[:, :, c * C:(c + 1) * C]
+        V_hot[:, :, sl * C:(sl + 1) * C] = V_host[:, :, c * C:(c + 1) * C]
+    K_hot, V_hot = K_hot.cuda(), V_hot.cuda()
+    cs, gs = _summ_tables(s)
+    hga.build_summaries(p, K_host.cuda(), n, 0, j, cs, gs)
+    seq = torch.from_numpy(w.seq_len.astype(np.int32)).cuda()
+    out = torch.empty((B, s.n_q_heads, 1, d), device="cuda")
+    ci = torch.empty((B, H, 1, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, 1, s.top_g), dtype=torch.int32, device="cuda")
+    staging = torch.empty(2 * B * H * s.top_g * s.group_size * d * 2, dtype=torch.uint8, device="cuda")
+    ws = hga.workspace(p, hga.OP_DECODE_OFFLOAD, 1, n)
+    copy_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    hga.decode_offload(p, dev(w.Q, s.dtype), K_host, V_host, K_hot, V_hot, n, seq, cs, gs, out,
+                       staging, ws, chunk_idx=ci, group_idx=gi, copy_stream=copy_stream.cuda_stream)
+    torch.cuda.synchronize()
+    ci_n, gi_n, got, cs_n = ci.cpu().numpy(), gi.cpu().numpy(), out.cpu().numpy(), cs.cpu().numpy()
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(s.seed)
+    sample = list(zip(rng.choice(B, 6, replace=True).tolist(), rng.choice(H, 6, replace=False).tolist()))
+    n_unique = 0
+    for b, h in sample:
+        Kf, Vf = f64(w.K[b:b + 1, h:h + 1], s.dtype), f64(w.V[b:b + 1, h:h + 1], s.dtype)
+        Qf = f64(w.Q[b:b + 1, h * gq:(h + 1) * gq], s.dtype)
+        q_pos = (w.seq_len[b:b + 1] - 1).astype(np.int64)
+        ocs, ogs = O.build_summaries(Kf, cfg)
+        if int(w.seq_len[b]) % C == 0:
+            # the step completed chunk j: its summary was built from the hot window
+            assert max_abs(cs_n[b, h, j], ocs[0, 0, j]) < 1e-5
+        or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, 1)
+        _, unique = check_routing(ci_n[b:b + 1, h:h + 1], gi_n[b:b + 1, h:h + 1], or_ci, or_gi, diags,
+                                  s.top_k, s.top_g)
+        if not unique:
+            continue
+        Oo, _ = O.attend(Qf, q_pos, Kf, Vf, or_gi, cfg, 1)
+        e = max_abs(got[b, h * gq:(h + 1) * gq, 0], Oo[0, :, 0])
+        say(f"  unit (b={b}, h={h}): O max-abs {e:.3e}")
+        assert e <= TOL[s.dtype]
+        n_unique += 1
+    assert n_unique >= len(sample) // 2
+
+
 def test_offload_warm_tier_steps(hga):
     """Warm tier over several decode steps with drifting queries: per step the
     output equals the staging path's bit for bit, the LRU state (tags, stamps,
