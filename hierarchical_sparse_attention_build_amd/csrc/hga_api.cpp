@@ -234,7 +234,10 @@ int device_cus() {
 // lists (no routing): the forced rows outnumber each routing workgroup's
 // share, so two forced workgroups, with two routing ones while they fit
 // (12.3 us against 14.0 with one forced).  No routed rows at all (top_k or
-// top_g = 0, streaming heads): one routing workgroup and two forced.
+// top_g = 0, streaming heads): one routing workgroup and two forced.  One
+// routing workgroup with routing, but a grid of three per unit would share
+// CUs: one forced workgroup when that makes it fit (decode_64k, 128 units:
+// 44.7 us against 45.1).
 void fused_shape(const KParams& kp, const FusedPlan& fp, bool given, DecodeArgs& da) {
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   const int want = std::max(1, std::min(HGA_DECODE_ROUTING_WGS, kDecMaxRouting));
@@ -242,7 +245,10 @@ void fused_shape(const KParams& kp, const FusedPlan& fp, bool given, DecodeArgs&
   const int forced_if_split = given ? 2 : 1;
   const bool split = routed && want > 1 && units * (want + forced_if_split) <= device_cus();
   da.routing_wgs = split ? want : 1;
-  da.forced_wgs = std::max(1, std::min(std::min(split ? forced_if_split : 2, fp.forced_blocks), kDecMaxForced));
+  const int cus = device_cus();
+  const bool fit_one_forced = routed && !given && units * 3 > cus && units * 2 <= cus;
+  const int forced = split ? forced_if_split : (fit_one_forced ? 1 : 2);
+  da.forced_wgs = std::max(1, std::min(std::min(forced, fp.forced_blocks), kDecMaxForced));
   da.forced_bpw = static_cast<int>(cdiv(fp.forced_blocks, da.forced_wgs));
   da.units_per_xcd = fp.units_per_xcd;
 }

@@ -212,8 +212,10 @@ def _run_decode_e2e(hga, s, w, check_all_rows=False):
     ("decode_32k", {"batch": 2, "n_tokens": 4096, "n_q_heads": 8, "n_kv_heads": 8}),
     ("decode_32k", {"batch": 1, "n_tokens": 4096, "n_q_heads": 16, "n_kv_heads": 1, "head_dim": 64}),
     # 88 units: too many for two routing workgroups and one forced each on a
-    # 256-CU device (one routing and two forced workgroups per unit instead)
+    # 256-CU device (one routing and one forced workgroup per unit instead)
     ("decode_32k", {"batch": 11, "n_tokens": 2048}),
+    # 136 units: one routing and two forced workgroups per unit
+    ("decode_32k", {"batch": 17, "n_tokens": 2048}),
     # 2042 candidate chunks: four keys per lane in each wave's share of the chunk selection
     ("decode_32k", {"batch": 1, "n_tokens": 131072}),
     # top_k = 32: the second selection phase takes 8 x 32 winners, four keys per lane
