@@ -306,19 +306,22 @@ def forced_chunks(j: int, cfg: HGAConfig) -> np.ndarray:
 def visible_tokens(t: int, group_ids: np.ndarray, cfg: HGAConfig) -> np.ndarray:
     """Exact token set T(t) of a query at position t (ascending).
 
-    Forced chunks contribute their tokens u <= t (causal); routed groups
-    contribute all their tokens (they lie in chunks before t's chunk).
+    The union, as a set, of the forced chunks' tokens and the listed groups'
+    tokens, keeping only tokens u <= t.  Reading: the causal mask applies to
+    every visible token; it only bites in the current chunk for lists that
+    routing produced (their groups lie before the local window), and it drops
+    any later group of a list given by a caller.  Negative ids are holes.
     """
     C, G = cfg.chunk_size, cfg.group_size
     j = t // C
     parts = [np.arange(c * C, c * C + C) for c in forced_chunks(j, cfg)]
     toks = np.concatenate(parts) if parts else np.zeros(0, np.int64)
-    toks = toks[toks <= t]
     g = np.asarray(group_ids)
     g = g[g >= 0]
     if len(g):
         toks = np.concatenate([toks, (g[:, None] * G + np.arange(G)[None, :]).reshape(-1)])
-    return np.unique(toks)
+    toks = np.unique(toks)
+    return toks[toks <= t]
 
 
 # --------------------------------------------------------------------------- #

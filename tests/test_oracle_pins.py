@@ -185,6 +185,78 @@ def test_route_unit_matches_brute_force():
         assert R.tolist() == bR and Gs.tolist() == bG, j
 
 
+def test_boundary_gap_hand_computed():
+    """The relative gap at the k-th boundary on hand-derived cases: ties, negative
+    scores, a zero denominator, NaN ranking last, no boundary."""
+    for c in json.load(open(GOLD))["boundary_gap"]["cases"]:
+        sc = np.array([float(x) for x in c["scores"]])
+        want = math.inf if c["gap"] == "inf" else float(c["gap"])
+        got = O.boundary_gap(sc, c["k"])
+        assert (got == want) if math.isinf(want) else abs(got - want) < 1e-15, (c, got)
+
+
+def _brute_route_heads(Q, q_pos, cs, gs, cf, n_kv_heads, group_of):
+    """Decode routing of every (b, h) by brute force, with query head hq serving
+    KV head group_of(hq)."""
+    B, Hq = Q.shape[:2]
+    out = {}
+    for b in range(B):
+        j = int(q_pos[b]) // cf.chunk_size
+        for h in range(n_kv_heads):
+            Uq = np.stack([Q[b, hq, 0] for hq in range(Hq) if group_of(hq) == h])
+            out[(b, h)] = _brute_route(Uq, cs[b, h], gs[b, h], j, cf)
+    return out
+
+
+def test_route_groups_query_heads_contiguously():
+    """GQA: KV head h serves query heads [h*gq, (h+1)*gq) (the layout of Q, K and V
+    in the pages' GQA models); with two KV heads and a binding top-k, routing
+    equals a brute force over those heads, and differs from an interleaved
+    (hq % Hkv) grouping on this input."""
+    cf = cfg(head_dim=8, chunk_size=4, group_size=2, n_sink=1, n_local=1, top_k=2, top_g=3)
+    rng = np.random.default_rng(5)
+    B, Hq, H, d, nC = 2, 4, 2, 8, 10
+    cs = rng.standard_normal((B, H, nC, d))
+    gs = rng.standard_normal((B, H, nC * 2, d))
+    Q = rng.standard_normal((B, Hq, 1, d)) * 0.1
+    # query head 2 points hard at chunk 3 of KV head 0, query head 1 at chunk 6 of
+    # KV head 1: a grouping error moves those needles to the wrong KV head
+    Q[:, 2, 0] = 8.0 * cs[:, 0, 3]
+    Q[:, 1, 0] = 8.0 * cs[:, 1, 6]
+    q_pos = np.array([39, 38])
+    ci, gi, _ = O.route(Q, q_pos, cs, gs, cf, H)
+    want = _brute_route_heads(Q, q_pos, cs, gs, cf, H, lambda hq: hq // (Hq // H))
+    other = _brute_route_heads(Q, q_pos, cs, gs, cf, H, lambda hq: hq % H)
+    differs = False
+    for (b, h), (R, Gs) in want.items():
+        assert ci[b, h, 0].tolist() == R and gi[b, h, 0].tolist() == Gs, (b, h)
+        differs |= other[(b, h)] != (R, Gs)
+    assert differs
+
+
+def test_visible_set_with_given_lists_is_a_causal_union():
+    """A caller's group list may repeat a group, name groups inside the forced
+    chunks, groups after the query and holes: the visible set is the union of
+    the forced tokens and the listed groups' tokens, each token once, up to the
+    query's position (brute force with Python sets)."""
+    cf = cfg(chunk_size=8, group_size=4, n_sink=1, n_local=1)
+    t = 37  # chunk 4; forced chunks 0, 3, 4
+    lst = np.array([5, -1, 5, 1, 7, 9, 8, 2, 11, -3, 4])
+    want = {u for c in (0, 3, 4) for u in range(8 * c, 8 * c + 8)}
+    want |= {u for g in lst.tolist() if g >= 0 for u in range(4 * g, 4 * g + 4)}
+    want = sorted(u for u in want if u <= t)
+    assert O.visible_tokens(t, lst, cf).tolist() == want
+    # attention over that set counts every token once
+    rng = np.random.default_rng(4)
+    Q = rng.standard_normal((1, 1, 1, 16))
+    K = rng.standard_normal((1, 1, 64, 16))
+    V = rng.standard_normal((1, 1, 64, 16))
+    o, _ = O.attend(Q, np.array([t]), K, V, lst.reshape(1, 1, 1, -1), cf, 1)
+    z = K[0, 0, want] @ Q[0, 0, 0] / 4.0
+    w = np.exp(z - z.max())
+    np.testing.assert_allclose(o[0, 0, 0], w @ V[0, 0, want] / w.sum(), atol=1e-12)
+
+
 def test_route_takes_all_when_fewer_candidates():
     cf = cfg(head_dim=8, chunk_size=4, group_size=2, n_sink=1, n_local=1, top_k=50, top_g=500)
     rng = np.random.default_rng(2)
