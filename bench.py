@@ -4,17 +4,24 @@
 
 A step is one decode step of the 32K-context workload (B=8, 32 query / 8 KV
 heads, d=128, C=64, G=16, sink 1, local 4, top-k 16, top-g 32, bf16): the
-library's hga_decode, which routes (summary scan + chunk top-k + group
-scoring + group top-g, and the summary update of the chunk the query
-completes) and attends over the gathered K/V, in two kernel launches.  Inputs are resident in HBM.
-Consecutive steps rotate over independent copies of the cache (as consecutive
-layers of a model would), so no step finds its working set in the 256 MB
-Infinity Cache; a warm-cache figure is reported separately.
+library's hga_decode, one kernel launch that routes (summary scan + chunk
+top-k + group scoring + group top-g), attends over the union of the routed
+groups and the always-visible chunks, and writes the summaries of the chunk
+the query completes.  Inputs are resident in HBM.
+
+Timing protocol.  Consecutive steps rotate over 12 independent copies of the
+cache (as consecutive layers of a model would), so between two uses of one
+copy more than 512 MB of other copies pass through the 256 MB Infinity Cache.
+The K timed steps are one HIP graph of exactly K launches; the headline value
+is B * K / (host time of one replay, bracketed by device synchronisations).
+The same graph is then replayed 50 times with HIP events on the launch stream
+around each replay: median, p10 and p90 of the per-step time over those
+replays.  A warm-cache figure (every step on one copy) is reported apart.
 
 Printed: one JSON line with the throughput (query tokens/s), the roofline of
-the decode step (its two kernel launches, timed with HIP events on the launch
-stream), the CPU oracle timed on a bounded sample, and the 32K prefill
-figures.
+the decode step (its one launch; achieved = the algorithmic bytes of the step
+/ the median per-step time), the CPU oracle timed on a bounded sample, and the
+32K prefill, 64K decode, route-reuse, streaming-head and cold-tier figures.
 """
 from __future__ import annotations
 
@@ -69,16 +76,18 @@ def measured_traffic(kernel):
     return None
 
 
-def decode_bytes(s, forced_wgs=2):
-    """Algorithmic HBM bytes of one decode step (one launch), by part.
+def decode_bytes(s):
+    """Algorithmic HBM bytes of one decode step, by part: what the method must
+    touch per (b, KV head) unit, times the units.
 
-    routing: the candidate chunk summaries, the group summaries of the routed
-        chunks, Q and the index lists written;
-    attention: the forced (sink + local + current) and routed K and V rows, the
-        forced partial results written and read back once, and O (fp32) written;
-    summary: when the query completes its chunk, its C key rows read and 1 + m
-        summaries written.
-    Returns (bytes by part, total bytes, attended tokens per unit).
+    routing: the candidate chunk summaries and the group summaries of the
+        routed chunks (fp32);
+    attention: the forced (sink + local + current) and routed K and V rows;
+    q_o: Q read and O (fp32) written.
+    Returns (bytes by part, total bytes, attended tokens per unit).  Work that
+    is not the method's own (partial softmax results exchanged between the
+    workgroups of a unit, the index lists, the summary of the chunk a query
+    completes, once every C steps) is left out.
     """
     C, G, d = s.chunk_size, s.group_size, s.head_dim
     L = s.n_tokens
@@ -93,13 +102,45 @@ def decode_bytes(s, forced_wgs=2):
     e = 2 if s.dtype == "bf16" else 4
     forced_tok = n_forced * C
     routed_tok = n_groups * G
-    partials = forced_wgs * gq * (d + 2) * 4
     parts = {
-        "routing": units * ((n_cand + n_routed_chunks * m) * d * 4 + gq * d * e + (s.top_k + s.top_g) * 4),
-        "attention": units * ((forced_tok + routed_tok) * d * e * 2 + 2 * partials + gq * d * 4),
-        "summary": units * (C * d * e + (1 + m) * d * 4) if L % C == 0 else 0,
+        "routing": units * (n_cand + n_routed_chunks * m) * d * 4,
+        "attention": units * (forced_tok + routed_tok) * d * e * 2,
+        "q_o": units * gq * d * (e + 4),
     }
     return parts, sum(parts.values()), forced_tok + routed_tok
+
+
+def graph_of(fn, n):
+    """A HIP graph of n calls fn(0..n-1), captured after one eager pass."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_stats(g, steps_per_replay, n_replays):
+    """Per-step microseconds of each of n_replays replays of g, from HIP events on
+    the launch stream around each replay: (median, p10, p90, mean)."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_replays + 1)]
+    ev[0].record(st)
+    for i in range(n_replays):
+        g.replay()
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / steps_per_replay for i in range(n_replays)])
+    return float(np.median(per)), float(np.percentile(per, 10)), float(np.percentile(per, 90)), float(per.mean())
 
 
 def main():
@@ -107,7 +148,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--replicas", type=int, default=12)
+    ap.add_argument("--stat-replays", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
@@ -173,62 +215,29 @@ def main():
         hga.decode(p, r["Q"], r["K"], r["V"], L, seq, r["cs"], r["gs"], r["O"], r["ws"],
                    chunk_idx=r["ci"], group_idx=r["gi"])
 
-    # The timed work is replayed from HIP graphs: one graph holds one step per
-    # cache replica, so the host issues one launch per R steps.
-    def capture(fn, n, rep0=None):
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(n):
-                fn(i if rep0 is None else rep0)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i if rep0 is None else rep0)
-        torch.cuda.synchronize()
-        return g
-
-    g_cold = capture(step, R)
-    g_warm = capture(step, R, rep0=0)
-    reps_per_replay = R
-    n_replay = max(1, args.steps // reps_per_replay)
-    steps = n_replay * reps_per_replay
-    for _ in range(max(1, args.warmup // R)):
+    # exactly K steps per graph: one replay is the timed region
+    steps = max(1, args.steps)
+    g_cold = graph_of(step, steps)
+    g_warm = graph_of(lambda i: step(0), steps)
+    n_warm_replays = max(1, -(-args.warmup // steps))
+    for _ in range(n_warm_replays):
         g_cold.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(n_replay):
-        g_cold.replay()
+    g_cold.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / steps
     value = B / sec_per_step
-    log(f"[bench] decode step {sec_per_step * 1e6:.2f} us -> {value:.0f} query tokens/s")
+    log(f"[bench] decode step {sec_per_step * 1e6:.2f} us (host clock, {steps} steps) -> {value:.0f} query tokens/s")
 
-    # warm-cache figure: the same step repeated on one replica
-    g_warm.replay()
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(n_replay):
-        g_warm.replay()
-    torch.cuda.synchronize()
-    warm_sec = (time.perf_counter() - t2) / steps
-
-    # the roofline unit is the step's one launch: HIP events on the launch
-    # stream around the same graph replays
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(n_replay):
-        g_cold.replay()
-    e1.record(st)
-    torch.cuda.synchronize()
-    step_us = e0.elapsed_time(e1) * 1e3 / steps
+    # statistics over replays, HIP events on the launch stream
+    med, p10, p90, mean = replay_stats(g_cold, steps, max(1, args.stat_replays))
+    wmed, _, _, _ = replay_stats(g_warm, steps, max(1, args.stat_replays // 5))
     parts, step_bytes, tokens = decode_bytes(s)
-    step_gbs = step_bytes / (step_us * 1e-6) / 1e9
-    log(f"[bench] decode step (HIP events) {step_us:.2f} us: {step_bytes / 1e6:.2f} MB -> {step_gbs:.0f} GB/s")
+    step_gbs = step_bytes / (med * 1e-6) / 1e9
+    log(f"[bench] decode step (HIP events, {args.stat_replays} replays of {steps} steps) median {med:.2f} us "
+        f"(p10 {p10:.2f}, p90 {p90:.2f}): {step_bytes / 1e6:.2f} MB -> {step_gbs:.0f} GB/s; warm cache {wmed:.2f} us")
 
     out = {
         "metric": METRIC,
@@ -236,7 +245,7 @@ def main():
         "unit": "query tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": n_warm_replays * steps,
         "ms_per_step": round(sec_per_step * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -247,13 +256,15 @@ def main():
                    "head_dim": d, "chunk": C, "group": G, "sink": s.n_sink, "local": s.n_local,
                    "top_k": s.top_k, "top_g": s.top_g, "rope_base": s.rope_base,
                    "tokens_attended": tokens, "cache_replicas": R},
+        "step_us": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3), "mean": round(mean, 3),
+                    "replays": args.stat_replays, "steps_per_replay": steps, "clock": "HIP events"},
         "roofline": {"kernel": "decode_step_kernel<bf16,128,4>",
                      "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode_step_kernel<bf16,128,4>"),
-                     "bytes_per_launch": step_bytes, "avg_us": round(step_us, 3),
+                     "bytes_per_launch": step_bytes, "avg_us": round(med, 3), "avg_us_is": "median per step",
                      "bytes_by_part": parts},
-        "warm_cache": {"ms_per_step": round(warm_sec * 1e3, 6), "value": round(B / warm_sec, 1)},
+        "warm_cache": {"us_per_step": round(wmed, 3), "value": round(B / (wmed * 1e-6), 1)},
     }
 
     del reps, g_cold, g_warm
@@ -266,7 +277,7 @@ def main():
         out["offload_decode_128k"] = bench_offload(args, dev)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(s, w)
+        out["cpu_baseline"] = cpu_baseline(s, w, prefill=not args.no_prefill)
 
     print(json.dumps(out), flush=True)
 
@@ -664,9 +675,27 @@ def bench_offload(args, dev):
             "bound": "host link (PCIe Gen5 x16, about 64 GB/s)", "warm_tier": warm_out}
 
 
-def cpu_baseline(s, w):
-    """The oracle timed on this host's cores, one decode step of all sequences
-    (routing over prebuilt oracle summaries + exact attention), repeated."""
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo ("unknown" if absent)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(s, w, prefill=True):
+    """The oracle timed on this host's cores.
+
+    Decode: full decode steps of all sequences (routing over prebuilt oracle
+    summary tables + exact attention), repeated for about 12 s.
+    Prefill (32K): the oracle's summary build over the whole sequence, then
+    routing and attention of a sample of 64 units (8 query chunks spread over
+    the sequence per KV head); the full call's time is estimated as the summary
+    time + the sample's time scaled to all 4096 units."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
@@ -689,12 +718,50 @@ def cpu_baseline(s, w):
             el = time.perf_counter() - t0
             if el > 12.0:
                 break
-    rate = s.batch * reps / el
-    log(f"[bench] cpu oracle: {reps} steps in {el:.1f} s -> {rate:.1f} query tokens/s")
+        del Kf, Vf, Qf, cs, gs
+        rate = s.batch * reps / el
+        log(f"[bench] cpu oracle decode: {reps} steps in {el:.1f} s -> {rate:.1f} query tokens/s")
+        out = {"value": round(rate, 2), "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+               "cpu_model": cpu_model(),
+               "sample": f"{reps} full decode steps of decode_32k (all {s.batch} sequences, 64 units; "
+                         "routing over prebuilt oracle summary tables + exact attention), numpy float64, "
+                         f"BLAS threads = {cores} (the host cores available to the process)"}
+        if prefill:
+            out["prefill"] = cpu_baseline_prefill(cores)
+    return out
+
+
+def cpu_baseline_prefill(cores):
+    import oracle as O
+    from hierarchical_sparse_attention_build_amd import workloads as W
+    sp = W.spec("prefill_32k")
+    log(f"[bench] cpu baseline prefill: generating {sp.name}")
+    wp = W.make(sp)
+    cfg = O.HGAConfig(**W.hga_config_kwargs(sp))
+    H, n, C = sp.n_kv_heads, sp.n_tokens, sp.chunk_size
+    nU = n // C
+    Qf, Kf, Vf = W.to_f64(wp.Q, sp.dtype), W.to_f64(wp.K, sp.dtype), W.to_f64(wp.V, sp.dtype)
+    del wp
+    t0 = time.perf_counter()
+    cs, gs = O.build_summaries(Kf, cfg)
+    t_sum = time.perf_counter() - t0
+    q_pos = np.zeros(1, dtype=np.int64)
+    units = [(0, h, int(u)) for h in range(H) for u in np.linspace(nU // 16, nU - 1, 8).astype(int)]
+    t1 = time.perf_counter()
+    _, gi, _ = O.route(Qf, q_pos, cs, gs, cfg, H, units=units)
+    for (b, h, u) in units:
+        O.attend_unit_block(Qf, q_pos, Kf, Vf, gi, cfg, H, b, h, u)
+    t_units = time.perf_counter() - t1
+    frac = len(units) / (H * nU)
+    est = t_sum + t_units / frac
+    rate = n / est
+    log(f"[bench] cpu oracle prefill: summaries {t_sum:.1f} s, {len(units)} units {t_units:.1f} s -> "
+        f"full call about {est:.0f} s, {rate:.1f} query tokens/s")
     return {"value": round(rate, 2), "unit": "query tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} full decode steps of decode_32k (all {s.batch} sequences, 64 units; "
-                      "routing over prebuilt oracle summary tables + exact attention), numpy float64, "
-                      f"BLAS threads = {cores} (the host cores available to the process)"}
+            "est_s_per_call": round(est, 2),
+            "sample": f"prefill_32k: the oracle's summary build over all 32768 tokens ({t_sum:.1f} s), then "
+                      f"routing + attention of {len(units)} of the {H * nU} units (8 query chunks per KV head, "
+                      f"spread over the sequence; {t_units:.1f} s), scaled to all units"}
 
 
 if __name__ == "__main__":

@@ -344,16 +344,33 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, int r,
   bool early = false;
   PartRegs pr;
   if (given) {
-    // ---- the given list: its entries in [0, n_cap / G), in order, without holes
+    // ---- the given list in canonical form: an entry outside the cache, in a
+    // forced chunk, after the query's chunk, or repeating an earlier entry
+    // adds no token to the visible set and is dropped; the others keep their
+    // order, without holes
+    const int32_t* gin = a.routes_in + static_cast<int64_t>(bh) * kp.top_g;
+    const int64_t n_groups_cap = kp.n_cap / kp.G;
+    int* raw = sm.selc;   // top_g <= kSelMaxK entries
+    int* keep = sm.selg;
+    for (int e = tid; e < kp.top_g; e += kDecThreads) {
+      const int g = gin[e];
+      const int c = g >= 0 ? g / kp.m : -1;
+      raw[e] = g >= 0 && g < n_groups_cap && c >= kp.n_sink && c < j - kp.n_local ? g : -1;
+    }
+    __syncthreads();
+    for (int e = tid; e < kp.top_g; e += kDecThreads) {
+      const int g = raw[e];
+      bool first = g >= 0;
+      for (int f = 0; first && f < e; ++f) first = raw[f] != g;
+      keep[e] = first;
+    }
+    __syncthreads();
     if (wid == 0) {
-      const int n_groups_cap = static_cast<int>(kp.n_cap >> kp.log2G);
-      const int32_t* gin = a.routes_in + static_cast<int64_t>(bh) * kp.top_g;
       int base = 0;
       for (int i0 = 0; i0 < kp.top_g; i0 += kWave) {
-        const int g = i0 + lane < kp.top_g ? gin[i0 + lane] : -1;
-        const bool ok = g >= 0 && g < n_groups_cap;
+        const bool ok = i0 + lane < kp.top_g && keep[i0 + lane];
         const uint64_t mk = __ballot(ok);
-        if (ok) sm.gl[base + bits_below(mk)] = g;
+        if (ok) sm.gl[base + bits_below(mk)] = raw[i0 + lane];
         base += __popcll(mk);
       }
       if (lane == 0) sm.early = base;

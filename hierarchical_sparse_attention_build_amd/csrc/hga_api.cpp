@@ -114,6 +114,11 @@ hga_status build_kparams(const hga_params* p, int64_t n_cap, KParams& kp) {
 
 size_t elem_bytes(const hga_params* p) { return p->qkv_dtype == HGA_BF16 ? 2 : 4; }
 
+template <typename P>
+P* at_ws(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
 // ------------------------------------------------------------------ workspace plans
 struct RoutePlan {
   int n_units, slices, cps;
@@ -296,8 +301,12 @@ struct FullPlan {
   FusedPlan fused;
   WarmPlan warm;
   IdxPlan idx;
+  size_t canon_off;  // canonical copy of a caller-given group list (attend, backward)
   size_t bytes;
 };
+
+// Units of a call: one per (b, kv head) in decode, one per query chunk in prefill.
+int call_units(const KParams& kp, int64_t nq) { return nq == 1 ? 1 : static_cast<int>(nq / kp.C); }
 
 FullPlan plan(const KParams& kp, int op, int64_t nq, bool bf16_in) {
   FullPlan f{};
@@ -307,7 +316,8 @@ FullPlan plan(const KParams& kp, int op, int64_t nq, bool bf16_in) {
   const bool needs_attend = op == HGA_OP_ATTEND || op == HGA_OP_PREFILL || op == HGA_OP_DECODE ||
                             op == HGA_OP_DECODE_OFFLOAD;
   const bool needs_idx = op == HGA_OP_PREFILL || op == HGA_OP_DECODE || op == HGA_OP_DECODE_OFFLOAD;
-  // counters first, so that zeroing the head of the workspace is enough
+  // The caller zero-fills the whole workspace once, before its first use; every
+  // counter in it is back at zero when a call's kernels end.
   if (needs_route) {
     f.route = plan_route(kp, nq, bf16_in, off);
     off += f.route.bytes;
@@ -328,8 +338,37 @@ FullPlan plan(const KParams& kp, int op, int64_t nq, bool bf16_in) {
     f.idx = plan_idx(kp, f.route.n_units, off);
     off += f.idx.bytes;
   }
+  if (op == HGA_OP_PREFILL_BACKWARD) {
+    // per query row: the base-2 log-sum-exp and D of the softmax
+    off = align256(off + static_cast<size_t>(kp.B) * kp.Hq * nq * 2 * sizeof(float));
+  }
+  if (op == HGA_OP_ATTEND || op == HGA_OP_PREFILL_BACKWARD) {
+    f.canon_off = off;
+    off = align256(off + static_cast<size_t>(kp.B) * kp.Hkv * call_units(kp, nq) *
+                             std::max(1, kp.top_g) * sizeof(int32_t));
+  }
   f.bytes = off;
   return f;
+}
+
+// Caller-given group lists in canonical form (repeats and entries that add no
+// visible token replaced by -1), written into the workspace; returns them.
+hga_status canon_lists(const KParams& kp, const FullPlan& f, void* ws, const int32_t* gi, int64_t nq,
+                       const int32_t* q_pos, int32_t bias, hipStream_t st, const int32_t** out) {
+  *out = gi;
+  if (kp.top_g <= 0) return HGA_OK;
+  CanonArgs c{};
+  c.kp = kp;
+  c.in = gi;
+  c.out = at_ws<int32_t>(ws, f.canon_off);
+  c.q_pos = q_pos;
+  c.pos_bias = bias;
+  c.nq = nq;
+  c.n_units = call_units(kp, nq);
+  const hipError_t e = launch_canon_groups(c, st);
+  if (e != hipSuccess) return fail(HGA_ERR_HIP, "canonical group lists: %s", hipGetErrorString(e));
+  *out = c.out;
+  return HGA_OK;
 }
 
 template <typename P>
@@ -444,8 +483,6 @@ size_t hga_workspace_size(const hga_params* p, int32_t op, int64_t nq, int64_t n
   if (op == HGA_OP_DECODE || op == HGA_OP_DECODE_OFFLOAD) nq = 1;
   if (check_nq(kp, nq) != HGA_OK) return 0;
   ok();
-  if (op == HGA_OP_PREFILL_BACKWARD)
-    return align256(static_cast<size_t>(kp.B) * kp.Hq * nq * 2 * sizeof(float));
   return plan(kp, op, nq, p->qkv_dtype == HGA_BF16).bytes;
 }
 
@@ -517,11 +554,12 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
   if (lse_out && !aligned16(lse_out)) return fail(HGA_ERR_ALIGN, "lse_out not 16-byte aligned");
   FullPlan f = plan(kp, HGA_OP_ATTEND, nq, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
-  const int n_units = nq == 1 ? 1 : static_cast<int>(nq / kp.C);
+  const int n_units = call_units(kp, nq);
   const bool bf = p->qkv_dtype == HGA_BF16;
   if (nq == 1 && f.fused.use && !lse_out && kp.top_g > 0) {
     // one query per sequence: the decode step's kernel with the lists given
-    // (route once, attend many: e.g. one layer's routing reused by the next)
+    // (route once, attend many: e.g. one layer's routing reused by the next);
+    // it puts each list in canonical form itself
     const FusedPlan& fp = f.fused;
     DecodeArgs da{};
     da.kp = kp;
@@ -540,7 +578,10 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
     HGA_TRY_HIP(launch_decode_step(da, bf, static_cast<hipStream_t>(stream)), "attend (decode step)");
     return ok();
   }
-  AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, group_idx, n_units, O, lse_out,
+  const int32_t* gi = group_idx;
+  if ((s = canon_lists(kp, f, ws, group_idx, nq, q_pos, 0, static_cast<hipStream_t>(stream), &gi)) != HGA_OK)
+    return s;
+  AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, gi, n_units, O, lse_out,
                              p->out_dtype == HGA_BF16);
   if (a.V16)
     HGA_TRY_HIP(launch_attend_prefill_pipe(a, static_cast<hipStream_t>(stream)), "attend (mfma, pipelined)");
@@ -616,14 +657,17 @@ hga_status hga_prefill_backward(const hga_params* p, const void* Q, const void* 
   HGA_CHECK_PTR(dK);
   HGA_CHECK_PTR(dV);
   if (kp.top_g > 0 && !group_idx) return fail(HGA_ERR_ARG, "group_idx is null");
-  const size_t need = align256(static_cast<size_t>(kp.B) * kp.Hq * n * 2 * sizeof(float));
-  if ((s = check_ws(ws, ws_bytes, need)) != HGA_OK) return s;
+  FullPlan f = plan(kp, HGA_OP_PREFILL_BACKWARD, n, p->qkv_dtype == HGA_BF16);
+  if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  const int32_t* gi = group_idx;
+  if ((s = canon_lists(kp, f, ws, group_idx, n, nullptr, 0, static_cast<hipStream_t>(stream), &gi)) != HGA_OK)
+    return s;
   BackwardArgs a{};
   a.kp = kp;
   a.Q = Q;
   a.K = K;
   a.V = V;
-  a.group_idx = group_idx;
+  a.group_idx = gi;
   a.dO = dO;
   a.dQ = dQ;
   a.dK = dK;
@@ -749,12 +793,16 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
   int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
   int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
 
-  // events ordering the copy stream between routing and the routed attention
-  thread_local hipEvent_t ev_routed = nullptr, ev_copied = nullptr;
-  if (!ev_routed) {
-    HGA_TRY_HIP(hipEventCreateWithFlags(&ev_routed, hipEventDisableTiming), "event create");
-    HGA_TRY_HIP(hipEventCreateWithFlags(&ev_copied, hipEventDisableTiming), "event create");
-  }
+  // events ordering the copy stream between routing and the routed attention:
+  // one pair per thread and device, made on first use and kept
+  constexpr int kMaxDevices = 64;
+  thread_local hipEvent_t ev_pair[kMaxDevices][2] = {};
+  int dev = 0;
+  HGA_TRY_HIP(hipGetDevice(&dev), "get device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HGA_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  for (int i = 0; i < 2; ++i)
+    if (!ev_pair[dev][i]) HGA_TRY_HIP(hipEventCreateWithFlags(&ev_pair[dev][i], hipEventDisableTiming), "event create");
+  hipEvent_t ev_routed = ev_pair[dev][0], ev_copied = ev_pair[dev][1];
 
   const int64_t hot_rows = static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C;
   RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);

@@ -157,6 +157,21 @@ struct WarmArgs {
 constexpr int kWarmMaxSlots = 1024;
 constexpr int kWarmMaxList = 256;   // top_g limit with the warm tier
 
+// Canonical form of a caller-given group list: entries that add no token to
+// the visible set (repeats, groups of forced chunks, after the query chunk or
+// outside the cache) become -1.
+struct CanonArgs {
+  KParams kp;
+  const int32_t* in;      // [B*Hkv*n_units, top_g]
+  int32_t* out;           // [B*Hkv*n_units, top_g]
+  const int32_t* q_pos;   // [B] (nullable: 0); position of query row 0 is q_pos[b] + pos_bias
+  int32_t pos_bias;
+  int64_t nq;             // 1: decode (one unit per (b, kv head)); else query chunks of C rows
+  int32_t n_units;
+};
+constexpr int kCanonMaxList = 1024;
+hipError_t launch_canon_groups(const CanonArgs& a, hipStream_t st);
+
 hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipStream_t st);
 hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);

@@ -131,11 +131,15 @@ hga_status hga_route(const hga_params* p, const void* Q, int64_t nq, const int32
 
 /* Steps 4-5: visibility union and exact attention [HGA-it, Meccanismo Core,
  * item 2 third bullet, item 4].  A query at position t in chunk j attends, with
- * a plain softmax of q.k/sqrt(d), to exactly the tokens u <= t of the sink
- * chunks [0, n_sink), the local chunks [j - n_local, j) and chunk j, plus every
- * token of the groups listed in group_idx for its unit (-1 entries ignored).
- * No summary enters the output.  O: [B, Hq, nq, d] of out_dtype; lse_out
- * (nullable): [B, Hq, nq] float32 natural-log sum of exp of the scaled scores. */
+ * a plain softmax of q.k/sqrt(d), to exactly the tokens u <= t of the set union
+ * of the sink chunks [0, n_sink), the local chunks [j - n_local, j), chunk j and
+ * the groups listed in group_idx for its unit.  The list may be in any order;
+ * -1 holes, ids outside [0, n_cap/G), a group listed twice, a group inside a
+ * forced chunk and a group after chunk j add no token (each token counts
+ * once).  Putting a list in that form costs O(top_g^2) per unit, done on the
+ * device.  No summary enters the output.  O: [B, Hq, nq, d] of out_dtype;
+ * lse_out (nullable): [B, Hq, nq] float32 natural-log sum of exp of the scaled
+ * scores. */
 hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int32_t* q_pos,
                       const void* K, const void* V, int64_t n_cap, const int32_t* group_idx,
                       void* O, float* lse_out, void* ws, size_t ws_bytes, void* stream);
@@ -177,7 +181,11 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
  * ordered after routing and before attention by events; attention reads only
  * device memory (the hot-window part of it overlaps the copy).  Like
  * hga_decode, a step whose query completes its chunk also writes that chunk's
- * summaries, read from the hot window. */
+ * summaries, read from the hot window.
+ * The two events are the one resource the library creates itself: a pair per
+ * calling thread and device, made (hipEventCreateWithFlags, timing disabled)
+ * by that thread's first offload call on the device and kept until the process
+ * ends.  A failure to create them returns HGA_ERR_HIP before any launch. */
 hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_host,
                               const void* V_host, const void* K_hot, const void* V_hot,
                               int64_t n_cap, const int32_t* seq_len, float* chunk_sum,
@@ -190,8 +198,9 @@ hga_status hga_decode_offload(const hga_params* p, const void* Q, const void* K_
  * respect to Q, K and V for an upstream gradient dO, with the routing held
  * fixed: the selection is a piecewise-constant function of the inputs, so no
  * gradient flows through it (nor into the summaries).  The visible sets are
- * those of the forward: the sink, local and current chunks (causal) plus the
- * groups of group_idx, as hga_prefill returned it.  Q, K, V as in
+ * those of the forward: the sink, local and current chunks plus the groups of
+ * group_idx (as hga_prefill returned it, or any list, read as hga_attend
+ * reads it), causal.  Q, K, V as in
  * hga_prefill (C = 64); dO: [B, Hq, n, d] float32; dQ: [B, Hq, n, d] float32,
  * dK, dV: [B, Hkv, n, d] float32, all written.  Workspace:
  * hga_workspace_size(p, HGA_OP_PREFILL_BACKWARD, n, n).  Float atomics sum
