@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "hga.h"
@@ -452,6 +453,34 @@ AttendArgs attend_args(const KParams& kp, const FullPlan& f, void* ws, const voi
   return a;
 }
 
+// One decode step in one launch (the fused kernel), with the unit counters
+// `sync` (zero before the launch, zero again after it) and the partial results.
+hipError_t launch_fused_decode(const hga_params* p, const KParams& kp, const FusedPlan& fp, const void* Q,
+                               const void* K, const void* V, const int32_t* seq_len, float* chunk_sum,
+                               float* group_sum, void* O, int32_t* ci, int32_t* gi, uint32_t* sync, float* partials,
+                               hipStream_t st) {
+  DecodeArgs da{};
+  da.kp = kp;
+  da.Q = Q;
+  da.seq_len = seq_len;
+  da.K = K;
+  da.V = V;
+  da.chunk_sum = chunk_sum;
+  da.group_sum = group_sum;
+  da.chunk_sum_w = chunk_sum;
+  da.group_sum_w = group_sum;
+  da.build_summary = 1;
+  da.chunk_idx = ci;
+  da.group_idx = gi;
+  da.O = O;
+  da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
+  fused_shape(kp, fp, false, da);
+  da.partials = partials;
+  da.sync = sync;
+  da.pos_offset = -1;
+  return launch_decode_step(da, p->qkv_dtype == HGA_BF16, st);
+}
+
 hga_status check_nq(const KParams& kp, int64_t nq) {
   if (nq < 1) return fail(HGA_ERR_SHAPE, "nq must be >= 1");
   if (nq > 1 && nq % kp.C != 0) return fail(HGA_ERR_SHAPE, "prefill nq %lld must be a multiple of C", (long long)nq);
@@ -461,6 +490,50 @@ hga_status check_nq(const KParams& kp, int64_t nq) {
     // grid.y carries the query row in the attention kernel
     return fail(HGA_ERR_UNSUPPORTED, "nq %lld > 65535 rows per call", (long long)nq);
   }
+  return HGA_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ no-allocation decode
+// Scratch of hga_decode_static: one copy per device, kept until the process
+// ends.  Layout: the arrival counters of up to kStaticMaxUnits units at a
+// fixed offset (0), so that calls of different shapes always find them at
+// zero; then the partial results and, when the caller passes no index lists,
+// the lists.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int kStaticMaxUnits = 1024;
+constexpr size_t kStaticSyncBytes = size_t(kStaticMaxUnits) * 4 * sizeof(uint32_t);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+namespace {
+
+constexpr int kStaticMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kStaticMaxDevices] = {};
+
+// The device address of this device's `scratch` (looked up once per device,
+// with the device current); on the first call its counters are cleared on
+// `st` by a fill kernel, ahead of the work the call enqueues.
+hga_status static_scratch(hipStream_t st, unsigned char** out) {
+  int dev = 0;
+  HGA_TRY_HIP(hipGetDevice(&dev), "get device");
+  if (dev < 0 || dev >= kStaticMaxDevices) return fail(HGA_ERR_UNSUPPORTED, "device index %d >= %d", dev, kStaticMaxDevices);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* ptr = nullptr;
+    HGA_TRY_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch address");
+    if (!ptr) return fail(HGA_ERR_HIP, "scratch address is null");
+    constexpr int words = static_cast<int>(kStaticSyncBytes / sizeof(uint32_t));
+    zero_words_kernel<<<(words + 255) / 256, 256, 0, st>>>(static_cast<uint32_t*>(ptr), words);
+    HGA_TRY_HIP(hipGetLastError(), "scratch clear");
+    g_static_ptr[dev] = ptr;
+  }
+  *out = static_cast<unsigned char*>(g_static_ptr[dev]);
   return HGA_OK;
 }
 
@@ -702,27 +775,9 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
   int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
   int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
   if (f.fused.use) {
-    const FusedPlan& fp = f.fused;
-    DecodeArgs da{};
-    da.kp = kp;
-    da.Q = Q;
-    da.seq_len = seq_len;
-    da.K = K;
-    da.V = V;
-    da.chunk_sum = chunk_sum;
-    da.group_sum = group_sum;
-    da.chunk_sum_w = chunk_sum;
-    da.group_sum_w = group_sum;
-    da.build_summary = 1;
-    da.chunk_idx = ci;
-    da.group_idx = gi;
-    da.O = O;
-    da.out_bf16 = p->out_dtype == HGA_BF16 ? 1 : 0;
-    fused_shape(kp, fp, false, da);
-    da.partials = at<float>(ws, fp.partials_off);
-    da.sync = at<uint32_t>(ws, fp.sync_off);
-    da.pos_offset = -1;
-    HGA_TRY_HIP(launch_decode_step(da, bf, st), "decode step");
+    HGA_TRY_HIP(launch_fused_decode(p, kp, f.fused, Q, K, V, seq_len, chunk_sum, group_sum, O, ci, gi,
+                                    at<uint32_t>(ws, f.fused.sync_off), at<float>(ws, f.fused.partials_off), st),
+                "decode step");
     return ok();
   }
   RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);
@@ -735,6 +790,50 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
   HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
   AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K, V, gi, 1, O, nullptr, p->out_dtype == HGA_BF16);
   HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+  return ok();
+}
+
+hga_status hga_decode_static(const hga_params* p, const void* Q, const void* K, const void* V, int64_t n_cap,
+                             const int32_t* seq_len, float* chunk_sum, float* group_sum, void* O,
+                             int32_t* chunk_idx, int32_t* group_idx, void* stream) {
+  KParams kp;
+  hga_status s = build_kparams(p, n_cap, kp);
+  if (s != HGA_OK) return s;
+  HGA_CHECK_PTR(Q);
+  HGA_CHECK_PTR(K);
+  HGA_CHECK_PTR(V);
+  HGA_CHECK_PTR(O);
+  HGA_CHECK_PTR(chunk_sum);
+  HGA_CHECK_PTR(group_sum);
+  if (!seq_len) return fail(HGA_ERR_ARG, "seq_len is null");
+  if (chunk_idx && !aligned16(chunk_idx)) return fail(HGA_ERR_ALIGN, "chunk_idx not 16-byte aligned");
+  if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
+  const FusedPlan fp = plan_fused(kp, 0);
+  if (!fp.use)
+    return fail(HGA_ERR_UNSUPPORTED, "hga_decode_static: shape outside the one-launch decode kernel "
+                                     "(Hq/Hkv in {1, 2, 4}, d in {64, 128}, C and G powers of two, at most "
+                                     "4096 candidate chunks, top_k * C/G <= 4096, top_g <= 256)");
+  const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
+  if (units > kStaticMaxUnits)
+    return fail(HGA_ERR_SHAPE, "hga_decode_static: B*Hkv = %lld > %d", static_cast<long long>(units), kStaticMaxUnits);
+  // layout: [sync counters | partial results | chunk list | group list]
+  const size_t partials_off = kStaticSyncBytes;
+  size_t off = align256(partials_off + static_cast<size_t>(units) * kDecMaxParts * kp.gq * (kp.d + 2) * sizeof(float));
+  const size_t ci_off = off;
+  if (!chunk_idx) off = align256(off + static_cast<size_t>(units) * std::max(1, kp.top_k) * sizeof(int32_t));
+  const size_t gi_off = off;
+  if (!group_idx) off = align256(off + static_cast<size_t>(units) * std::max(1, kp.top_g) * sizeof(int32_t));
+  if (off > kStaticScratchBytes)
+    return fail(HGA_ERR_SHAPE, "hga_decode_static: needs %zu bytes of scratch, limit %zu", off, kStaticScratchBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned char* base = nullptr;
+  if ((s = static_scratch(st, &base)) != HGA_OK) return s;
+  int32_t* ci = chunk_idx ? chunk_idx : reinterpret_cast<int32_t*>(base + ci_off);
+  int32_t* gi = group_idx ? group_idx : reinterpret_cast<int32_t*>(base + gi_off);
+  HGA_TRY_HIP(launch_fused_decode(p, kp, fp, Q, K, V, seq_len, chunk_sum, group_sum, O, ci, gi,
+                                  reinterpret_cast<uint32_t*>(base), reinterpret_cast<float*>(base + partials_off),
+                                  st),
+              "decode step (static scratch)");
   return ok();
 }
 

@@ -20,8 +20,8 @@ STATUS = {0: "HGA_OK", -1: "HGA_ERR_ARG", -2: "HGA_ERR_SHAPE", -3: "HGA_ERR_ALIG
           -4: "HGA_ERR_WORKSPACE", -5: "HGA_ERR_UNSUPPORTED", -6: "HGA_ERR_HIP"}
 
 EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_route", "hga_attend", "hga_prefill",
-           "hga_prefill_backward", "hga_decode", "hga_decode_offload", "hga_decode_offload_warm",
-           "hga_last_error", "hga_version")
+           "hga_prefill_backward", "hga_decode", "hga_decode_static", "hga_decode_offload",
+           "hga_decode_offload_warm", "hga_last_error", "hga_version")
 
 
 class HGAError(RuntimeError):
@@ -65,6 +65,7 @@ def lib():
             "hga_prefill": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
             "hga_prefill_backward": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
             "hga_decode": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "hga_decode_static": (i32, [P, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
             "hga_decode_offload": (i32, [P, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp, sz, vp, vp]),
             "hga_decode_offload_warm": (i32, [P, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
@@ -168,6 +169,15 @@ def decode(p, Q, K, V, n_cap, seq_len, chunk_sum, group_sum, O, ws, chunk_idx=No
     _check(lib().hga_decode(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), n_cap, _ptr(seq_len),
                             _ptr(chunk_sum), _ptr(group_sum), _ptr(O), _ptr(chunk_idx),
                             _ptr(group_idx), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def decode_static(p, Q, K, V, n_cap, seq_len, chunk_sum, group_sum, O, chunk_idx=None,
+                  group_idx=None, stream=None):
+    """``hga_decode_static``: hga_decode with the library's static device scratch
+    (no workspace argument)."""
+    _check(lib().hga_decode_static(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), n_cap, _ptr(seq_len),
+                                   _ptr(chunk_sum), _ptr(group_sum), _ptr(O), _ptr(chunk_idx),
+                                   _ptr(group_idx), _stream(stream)))
 
 
 def decode_offload(p, Q, K_host, V_host, K_hot, V_hot, n_cap, seq_len, chunk_sum, group_sum, O,

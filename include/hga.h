@@ -166,6 +166,26 @@ hga_status hga_decode(const hga_params* p, const void* Q, const void* K, const v
                       void* O, int32_t* chunk_idx, int32_t* group_idx,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* hga_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and launch as hga_decode, minus
+ * ws / ws_bytes: the scratch (per-unit arrival counters, partial softmax
+ * results, and the index lists when chunk_idx / group_idx are null) lives in
+ * a static device array of 16 MiB that the library holds on every device it
+ * runs on until the process ends.  Limits: the shapes of hga_decode's
+ * one-launch kernel (Hq/Hkv in {1, 2, 4}, d in {64, 128}, C and G powers of
+ * two, top_g <= 256), B * Hkv <= 1024 and the scratch size; anything else
+ * returns HGA_ERR_UNSUPPORTED or HGA_ERR_SHAPE before any launch.  The first
+ * call on a device also enqueues, ahead of its step, a small kernel that
+ * clears the array's counters (make it outside graph capture, or replay the
+ * captured graph before other calls); every call leaves them cleared again.
+ * Calls on one device share the array: calls that overlap in time on one
+ * device (different streams, no ordering) race and give wrong results. */
+hga_status hga_decode_static(const hga_params* p, const void* Q, const void* K, const void* V,
+                             int64_t n_cap, const int32_t* seq_len, float* chunk_sum,
+                             float* group_sum, void* O, int32_t* chunk_idx, int32_t* group_idx,
+                             void* stream);
+
 /* Decode with the cold tier in host memory [HGA-it, Architettura della
  * Memoria: hot / warm / cold tiers; Meccanismo Core item 4: routed K/V fetched
  * from host RAM into device memory].  K_host, V_host: [B, Hkv, n_cap, d] in

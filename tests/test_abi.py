@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     out = subprocess.run(["nm", "-D", "--defined-only", hga.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (hga_\w+)", out))
@@ -148,3 +148,18 @@ def test_prefill_workspace_holds_the_converted_tables(L):
     # one query per sequence: neither table
     assert hga.workspace_size(pb, hga.OP_ATTEND, 1, n) < v16
 
+
+
+def test_decode_static_rejects_unsupported_shapes(L):
+    """The no-workspace decode rejects, before any device work, shapes outside
+    its one-launch kernel and more units than its static scratch holds."""
+    fake = 0x10000
+    args = (fake, fake, fake, 4096, fake, fake, fake, fake, None, None, None)
+    p = good(n_q_heads=16, n_kv_heads=2)  # 8 query heads per KV head
+    assert L.hga_decode_static(ctypes.byref(p), *args) == -5
+    assert "hga_decode_static" in hga.last_error()
+    p = good(batch=600, n_q_heads=8, n_kv_heads=2)  # 1200 units
+    assert L.hga_decode_static(ctypes.byref(p), *args) == -2
+    assert "B*Hkv" in hga.last_error()
+    p = good()
+    assert L.hga_decode_static(ctypes.byref(p), None, *args[1:]) == -1
