@@ -42,7 +42,7 @@ constexpr int kDecSelE = 4;
 template <int GQ, int D>
 struct DecodeSmem {
   float qs[GQ * D];             // query rows of the unit (fp32) for the scans
-  float sc[kDecMaxScores];      // chunk scores, then group scores
+  alignas(16) float sc[kDecMaxScores];  // chunk scores, then group scores
   int selc[kSelMaxK];           // selected chunk positions (ascending)
   int selg[kSelMaxK];           // selected group positions (ascending)
   int gl[kSelMaxK];             // routed group ids
@@ -291,10 +291,20 @@ __device__ __forceinline__ void forced_role(const DecodeArgs& a, int bh, int f, 
   }
   // ---- the query completes chunk j: summarise it for the next steps' routing
   if (f == 0 && a.build_summary && (t + 1) % kp.C == 0) {
-    summarize_chunk<T, D>(Kb + static_cast<int64_t>(j) * kp.C * D, j, kp, true, nullptr,
-                          a.chunk_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap + j) * D,
-                          a.group_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m +
-                                           static_cast<int64_t>(j) * kp.m) * D);
+    float* cs = a.chunk_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap + j) * D;
+    float* gs = a.group_sum_w + (static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m + static_cast<int64_t>(j) * kp.m) * D;
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {
+      if (summarize_fast_ok<D>(kp, true, true, kDecMaxScores) && summarize_loads_per_group<D>(kp) == 4) {
+        // the tables and group means in the score array, which this role does
+        // not use (only the 4-load variant is compiled in: the kernel stays
+        // within its registers)
+        summarize_chunk_fast<D, 4>(reinterpret_cast<const bf16*>(Kb) + static_cast<int64_t>(j) * kp.C * D, kp,
+                                   sm.sc, cs, gs);
+        done = true;
+      }
+    }
+    if (!done) summarize_chunk<T, D>(Kb + static_cast<int64_t>(j) * kp.C * D, j, kp, true, nullptr, cs, gs);
   }
 }
 

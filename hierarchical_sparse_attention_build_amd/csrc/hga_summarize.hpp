@@ -115,4 +115,181 @@ __device__ void summarize_chunk(const T* __restrict__ Kc, int c, const KParams& 
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for bf16 post-RoPE keys (C <= 64, G a multiple of the rows that
+// one 64-lane load covers): the same arithmetic as above, with 16-byte row
+// loads, one wave per group, and the rotation angles read from tables:
+//   rot[r * P + i]  = (cos, sin) of theta_i * (gcen - r)         for r < G,
+//   crot[g * P + i] = (cos, sin) of theta_i * (ccen - gcen_g)     for g < m,
+// the identity for high-frequency pairs.  The pair (x_i, x_{i+P}) of a row
+// sits in two lanes of the same row (one holds first halves, the other second
+// halves); each lane rotates its own half with the other's values.
+
+template <int D>
+__host__ __device__ constexpr int summarize_rows_per_load() { return kWave / (D / 8); }
+
+// LDS floats the fast path needs: both tables (float2) and the group means
+__host__ __device__ inline int summarize_lds_floats(const KParams& kp) {
+  return 2 * (kp.G + kp.m) * (kp.d / 2) + kp.m * kp.d;
+}
+
+template <int D>
+__host__ __device__ inline bool summarize_fast_ok(const KParams& kp, bool bf16_in, bool rotated, int lds_floats) {
+  return bf16_in && rotated && kp.d == D && kp.C <= 64 && kp.G % summarize_rows_per_load<D>() == 0 &&
+         summarize_lds_floats(kp) <= lds_floats;
+}
+
+// All threads of the workgroup build the tables (ends with a barrier).
+template <int D>
+__device__ void build_summary_tables(const KParams& kp, float2* rot, float2* crot) {
+  constexpr int P = D / 2;
+  const float gcen = 0.5f * static_cast<float>(kp.G - 1);
+  const float ccen = 0.5f * static_cast<float>(kp.C - 1);
+  for (int x = threadIdx.x; x < kp.G * P; x += blockDim.x) {
+    const int r = x / P, i = x % P;
+    float sn = 0.f, cn = 1.f;
+    if (!((kp.hf_mask >> i) & 1ull)) sincosf(kp.theta_f[i] * (gcen - static_cast<float>(r)), &sn, &cn);
+    rot[x] = make_float2(cn, sn);
+  }
+  for (int x = threadIdx.x; x < kp.m * P; x += blockDim.x) {
+    const int g = x / P, i = x % P;
+    float sn = 0.f, cn = 1.f;
+    if (!((kp.hf_mask >> i) & 1ull))
+      sincosf(kp.theta_f[i] * (ccen - (static_cast<float>(g * kp.G) + gcen)), &sn, &cn);
+    crot[x] = make_float2(cn, sn);
+  }
+  __syncthreads();
+}
+
+// The value that the lane holding the other half of this lane's pairs has.
+template <int D>
+__device__ __forceinline__ float pair_partner(float v) {
+  if constexpr (D == 128) return dpp::movf<dpp::kRowRor8>(v);  // lane c <-> c ^ 8 of a row of 16
+  else return __shfl_xor(v, 4, kWave);                          // lane c <-> c ^ 4 of a group of 8
+}
+
+// Sum over the lanes that hold the same columns (different rows).
+template <int D>
+__device__ __forceinline__ float sum_row_lanes(float v) {
+  if constexpr (D == 64) v += dpp::movf<dpp::kRowRor8>(v);
+  return sum_rows(v);
+}
+
+// The rows of one group that this lane loads (16 bytes each), MAXL loads at
+// most (G <= MAXL rows per load).
+template <int D, int MAXL>
+struct GroupRows {
+  uint4 w[MAXL];
+};
+
+template <int D, int MAXL>
+__device__ __forceinline__ void load_group_rows(const bf16* __restrict__ Kc, const KParams& kp, int g,
+                                                GroupRows<D, MAXL>& rows) {
+  constexpr int LR = D / 8;
+  constexpr int RPI = summarize_rows_per_load<D>();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int cb = lane % LR, ro = lane / LR;
+  const int spg = kp.G / RPI;
+#pragma unroll
+  for (int s = 0; s < MAXL; ++s)
+    if (s < spg)
+      rows.w[s] = *reinterpret_cast<const uint4*>(Kc + static_cast<int64_t>(g * kp.G + s * RPI + ro) * D + cb * 8);
+}
+
+// One wave: group g's mean from its loaded rows, into gs_out (global) and
+// gmean (LDS, [m][D]).
+template <int D, int MAXL>
+__device__ __forceinline__ void group_mean_wave(const GroupRows<D, MAXL>& rows, const KParams& kp, const float2* rot,
+                                                int g, float* __restrict__ gs_out, float* gmean) {
+  constexpr int P = D / 2;
+  constexpr int LR = D / 8;
+  constexpr int RPI = summarize_rows_per_load<D>();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int cb = lane % LR, ro = lane / LR;
+  const int i0 = (cb % (LR / 2)) * 8;                // first pair of this lane's 8 columns
+  const float sgn = cb >= LR / 2 ? 1.f : -1.f;       // second halves: +, first halves: -
+  const int spg = kp.G / RPI;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < MAXL; ++s) {
+    if (s < spg) {
+      const uint32_t ww[4] = {rows.w[s].x, rows.w[s].y, rows.w[s].z, rows.w[s].w};
+      const float4* tr = reinterpret_cast<const float4*>(rot + (s * RPI + ro) * P + i0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x0 = bf16lo(ww[q]), x1 = bf16hi(ww[q]);
+        const float y0 = pair_partner<D>(x0), y1 = pair_partner<D>(x1);
+        const float4 t = tr[q];  // (cos, sin) of pairs i0 + 2q and i0 + 2q + 1
+        acc[2 * q] = fmaf(x0, t.x, fmaf(sgn * y0, t.y, acc[2 * q]));
+        acc[2 * q + 1] = fmaf(x1, t.z, fmaf(sgn * y1, t.w, acc[2 * q + 1]));
+      }
+    }
+  }
+  const float invG = 1.0f / static_cast<float>(kp.G);
+  float gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gm[e] = sum_row_lanes<D>(acc[e]) * invG;
+  if (ro == 0) {
+    const float4 v0 = make_float4(gm[0], gm[1], gm[2], gm[3]), v1 = make_float4(gm[4], gm[5], gm[6], gm[7]);
+    float4* go = reinterpret_cast<float4*>(gs_out + static_cast<int64_t>(g) * D + cb * 8);
+    go[0] = v0;
+    go[1] = v1;
+    float4* gl = reinterpret_cast<float4*>(gmean + g * D + cb * 8);
+    gl[0] = v0;
+    gl[1] = v1;
+  }
+}
+
+// The chunk summary from the group means in LDS (after a barrier): the mean
+// over groups of each group's mean turned to the chunk centre.
+template <int D>
+__device__ void combine_chunk(const KParams& kp, const float2* crot, const float* gmean, float* __restrict__ cs_out) {
+  constexpr int P = D / 2;
+  const float invm = 1.0f / static_cast<float>(kp.m);
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    float sa = 0.f, sb = 0.f;
+    for (int g = 0; g < kp.m; ++g) {
+      const float a = gmean[g * D + i], b = gmean[g * D + i + P];
+      const float2 t = crot[g * P + i];
+      float ra, rb;
+      rot2(a, b, t.x, t.y, ra, rb);
+      sa += ra;
+      sb += rb;
+    }
+    cs_out[i] = sa * invm;
+    cs_out[i + P] = sb * invm;
+  }
+}
+
+// Loads per lane of one group on the fast path: 4 covers G <= 16 (d = 128) and
+// G <= 32 (d = 64); 16 covers every G <= 64.
+template <int D>
+__host__ __device__ inline int summarize_loads_per_group(const KParams& kp) {
+  return kp.G / summarize_rows_per_load<D>() <= 4 ? 4 : 16;
+}
+
+// The whole workgroup: chunk and group summaries of the chunk at Kc, with the
+// LDS area lds (summarize_lds_floats(kp) floats, 16-byte aligned).  Each wave
+// issues the loads of its first group before the tables are built.  Ends with
+// the summaries written (no barrier after the last store).
+template <int D, int MAXL>
+__device__ void summarize_chunk_fast(const bf16* __restrict__ Kc, const KParams& kp, float* lds,
+                                     float* __restrict__ cs_out, float* __restrict__ gs_out) {
+  float2* rot = reinterpret_cast<float2*>(lds);
+  float2* crot = rot + kp.G * (D / 2);
+  float* gmean = reinterpret_cast<float*>(crot + kp.m * (D / 2));
+  const int wid = wave_id(), nw = static_cast<int>(blockDim.x) / kWave;
+  GroupRows<D, MAXL> rows;
+  if (wid < kp.m) load_group_rows<D, MAXL>(Kc, kp, wid, rows);
+  build_summary_tables<D>(kp, rot, crot);
+  for (int g = wid; g < kp.m; g += nw) {
+    if (g != wid) load_group_rows<D, MAXL>(Kc, kp, g, rows);
+    group_mean_wave<D, MAXL>(rows, kp, rot, g, gs_out, gmean);
+  }
+  __syncthreads();
+  combine_chunk<D>(kp, crot, gmean, cs_out);
+}
+
 }  // namespace hga
