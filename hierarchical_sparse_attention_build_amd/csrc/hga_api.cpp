@@ -486,10 +486,15 @@ hga_status check_nq(const KParams& kp, int64_t nq) {
   if (nq > 1 && nq % kp.C != 0) return fail(HGA_ERR_SHAPE, "prefill nq %lld must be a multiple of C", (long long)nq);
   if (nq > kp.n_cap) return fail(HGA_ERR_SHAPE, "nq exceeds n_cap");
   if (nq > 1 && nq / kp.C > 65535) return fail(HGA_ERR_UNSUPPORTED, "too many query chunks");
-  if (nq > 65535 && nq > 1) {
-    // grid.y carries the query row in the attention kernel
-    return fail(HGA_ERR_UNSUPPORTED, "nq %lld > 65535 rows per call", (long long)nq);
-  }
+  return HGA_OK;
+}
+
+// The split-K attention kernel (shapes the MFMA prefill kernels do not take)
+// carries the query row in grid.y.
+hga_status check_splitk_rows(int64_t nq) {
+  if (nq > 65535)
+    return fail(HGA_ERR_UNSUPPORTED, "nq %lld > 65535 rows per call for this shape (split-K attention)",
+                static_cast<long long>(nq));
   return HGA_OK;
 }
 
@@ -651,17 +656,20 @@ hga_status hga_attend(const hga_params* p, const void* Q, int64_t nq, const int3
     HGA_TRY_HIP(launch_decode_step(da, bf, static_cast<hipStream_t>(stream)), "attend (decode step)");
     return ok();
   }
+  const bool splitk = !f.attend.v16 && !prefill_mfma_supported(kp, bf, nq);
+  if (splitk && (s = check_splitk_rows(nq)) != HGA_OK) return s;
   const int32_t* gi = group_idx;
   if ((s = canon_lists(kp, f, ws, group_idx, nq, q_pos, 0, static_cast<hipStream_t>(stream), &gi)) != HGA_OK)
     return s;
   AttendArgs a = attend_args(kp, f, ws, Q, nq, q_pos, 0, K, V, gi, n_units, O, lse_out,
                              p->out_dtype == HGA_BF16);
-  if (a.V16)
+  if (a.V16) {
     HGA_TRY_HIP(launch_attend_prefill_pipe(a, static_cast<hipStream_t>(stream)), "attend (mfma, pipelined)");
-  else if (prefill_mfma_supported(kp, bf, nq))
+  } else if (prefill_mfma_supported(kp, bf, nq)) {
     HGA_TRY_HIP(launch_attend_prefill_mfma(a, static_cast<hipStream_t>(stream)), "attend (mfma)");
-  else
+  } else {
     HGA_TRY_HIP(launch_attend_splitk(a, bf, static_cast<hipStream_t>(stream)), "attend");
+  }
   return ok();
 }
 
@@ -683,6 +691,8 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
   if (group_idx && !aligned16(group_idx)) return fail(HGA_ERR_ALIGN, "group_idx not 16-byte aligned");
   FullPlan f = plan(kp, HGA_OP_PREFILL, n, p->qkv_dtype == HGA_BF16);
   if ((s = check_ws(ws, ws_bytes, f.bytes)) != HGA_OK) return s;
+  if (!f.attend.v16 && !prefill_mfma_supported(kp, p->qkv_dtype == HGA_BF16, n) && (s = check_splitk_rows(n)) != HGA_OK)
+    return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = p->qkv_dtype == HGA_BF16;
   int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
@@ -704,12 +714,13 @@ hga_status hga_prefill(const hga_params* p, const void* Q, const void* K, const 
     HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
   AttendArgs aa = attend_args(kp, f, ws, Q, n, nullptr, 0, K, V, gi, f.route.n_units, O, nullptr,
                               p->out_dtype == HGA_BF16);
-  if (aa.V16)
+  if (aa.V16) {
     HGA_TRY_HIP(launch_attend_prefill_pipe(aa, st), "attend (mfma, pipelined)");
-  else if (prefill_mfma_supported(kp, bf, n))
+  } else if (prefill_mfma_supported(kp, bf, n)) {
     HGA_TRY_HIP(launch_attend_prefill_mfma(aa, st), "attend (mfma)");
-  else
+  } else {
     HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+  }
   return ok();
 }
 

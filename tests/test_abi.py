@@ -163,3 +163,17 @@ def test_decode_static_rejects_unsupported_shapes(L):
     assert "B*Hkv" in hga.last_error()
     p = good()
     assert L.hga_decode_static(ctypes.byref(p), None, *args[1:]) == -1
+
+
+def test_prefill_row_cap_only_for_the_splitk_path(L):
+    """A 64K prefill is accepted by validation; with fp32 inputs (the split-K
+    attention, which carries the row in grid.y) more than 65535 rows are
+    rejected with HGA_ERR_UNSUPPORTED before anything is launched."""
+    fake = 0x10000
+    n = 65536
+    pf = hga.params(1, 32, 8, 128, 64, 16, 1, 2, 32, 64, 5e5, qkv_dtype=hga.HGA_F32)
+    assert hga.workspace_size(pf, hga.OP_PREFILL, n, n) > 0
+    st = L.hga_prefill(ctypes.byref(pf), fake, fake, fake, n, fake, fake, fake, None, None, fake, 1 << 40, None)
+    assert st == -5 and "65535" in hga.last_error()
+    pb = hga.params(1, 32, 8, 128, 64, 16, 1, 2, 32, 64, 5e5, qkv_dtype=hga.HGA_BF16)
+    assert hga.workspace_size(pb, hga.OP_PREFILL, n, n) > 0

@@ -986,3 +986,46 @@ def test_prefill_backward_given_lists_with_repeats(hga):
         scale = max(1.0, float(np.abs(ref).max()))
         say(f"  {nm} max-abs {e:.3e} (scale {scale:.2f})")
         assert e <= 1e-4 * scale, nm
+
+
+@pytest.mark.timeout(300)
+def test_prefill_64k_single_call_sampled(hga):
+    """A 64K-token causal prefill in one hga_prefill call (B=1, 32/8 heads,
+    d=128): the summary tables in full and the routing and output of sampled
+    units against the oracle."""
+    s = W.spec("prefill_32k", n_tokens=65536)
+    say(f"[prefill 64K, one call, sampled units] seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    p = params_of(s)
+    B, H, n, C = s.batch, s.n_kv_heads, s.n_tokens, s.chunk_size
+    nU = n // C
+    cs, gs = _summ_tables(s)
+    ci = torch.empty((B, H, nU, s.top_k), dtype=torch.int32, device="cuda")
+    gi = torch.empty((B, H, nU, s.top_g), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, n, s.head_dim), device="cuda")
+    ws = hga.workspace(p, hga.OP_PREFILL, n, n)
+    hga.prefill(p, dev(w.Q, s.dtype), dev(w.K, s.dtype), dev(w.V, s.dtype), n, cs, gs, out, ws,
+                chunk_idx=ci, group_idx=gi)
+    torch.cuda.synchronize()
+    # float32 views of the bf16 values (exact); the oracle converts the slices it reads to float64
+    Qf = W.bf16_to_f32(w.Q)
+    Kf, Vf = W.bf16_to_f32(w.K), W.bf16_to_f32(w.V)
+    ocs, ogs = O.build_summaries(Kf, cfg)
+    assert max_abs(cs.cpu().numpy(), ocs) < 1e-5
+    assert max_abs(gs.cpu().numpy(), ogs) < 1e-5
+    rng = np.random.default_rng(1)
+    units = [(0, h, u) for h in range(H) for u in sorted(rng.choice(nU, 3, replace=False).tolist())]
+    units += [(0, 0, nU - 1), (0, 7, nU // 2)]
+    q_pos = np.zeros(B, dtype=np.int64)
+    or_ci, or_gi, diags = O.route(Qf, q_pos, ocs, ogs, cfg, H, units=units)
+    gi_n = gi.cpu().numpy()
+    n_units, unique = check_routing(ci.cpu().numpy(), gi_n, or_ci, or_gi, diags, s.top_k, s.top_g)
+    gq = s.n_q_heads // H
+    emax = 0.0
+    for (b, h, u) in sorted(diags):
+        o, _ = O.attend_unit_block(Qf, q_pos, Kf, Vf, gi_n, cfg, H, b, h, u)
+        emax = max(emax, max_abs(out[b, h * gq:(h + 1) * gq, u * C:(u + 1) * C].cpu().numpy(), o))
+    say(f"  sampled units {n_units} unique routing {len(unique)}  O max-abs {emax:.3e}")
+    assert emax <= TOL[s.dtype]
+    assert torch.isfinite(out).all()
