@@ -9,7 +9,9 @@
 //   D = sum_u p_u (do.v_u) (= do.o),   dz_u = p_u (do.v_u - D),
 //   dq = sum_u dz_u k_u / sqrt(d),   dk_u += dz_u q / sqrt(d),   dv_u += p_u do.
 //
-// Two gather kernels, all arithmetic in fp32 on the vector ALUs:
+// This file is the path for fp32 inputs and for shapes the matrix-core
+// backward (attend_backward_mfma.hip, bf16 inputs) does not take.  Two gather
+// kernels, all arithmetic in fp32 on the vector ALUs:
 //   * bwd_dq_kernel, one workgroup per (query chunk, b, kv head, query head):
 //     thread (row, quarter) holds a quarter of one query row.  A first pass
 //     over the visible tiles gets the row's softmax statistics (max, sum) and

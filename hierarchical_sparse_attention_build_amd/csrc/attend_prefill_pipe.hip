@@ -31,6 +31,7 @@
 // sum adds the same rounded values), V to fp16 exactly for |v| < 65504.
 #include "hga_device.hpp"
 #include "hga_kernels.hpp"
+#include "hga_mfma.hpp"
 
 #include <type_traits>
 
@@ -38,27 +39,9 @@ namespace hga {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kTile = 64;      // keys per tile (= C)
-constexpr int kBlk = 16;       // keys per V block
 constexpr int kRing = 3;       // LDS tiles
 constexpr int kMaxTiles = 320;  // tiles of a unit: the forced chunks and the routed groups
-
-// key held at position p (0..15) of a V block: positions 8h..8h+7 serve the
-// lanes of half h of the P.V fragment
-__device__ __forceinline__ int vblock_key(int p) {
-  const int h = p >> 3, j = p & 7;
-  return 8 * (j >> 2) + 4 * h + (j & 3);
-}
-
-// byte offset of (dimension d, half h) inside a V block
-__device__ __forceinline__ int vblock_off(int d, int h) {
-  return d * 32 + ((h ^ ((d >> 3) & 1)) << 4);
-}
 
 }  // namespace
 

@@ -303,6 +303,10 @@ struct FullPlan {
   WarmPlan warm;
   IdxPlan idx;
   size_t canon_off;  // canonical copy of a caller-given group list (attend, backward)
+  // matrix-core backward: dO split in two bf16 parts, the visibility bitmap
+  // and per-key-chunk counts
+  bool bwd_mfma;
+  size_t doh_off, dol_off, vis_off, counts_off;
   size_t bytes;
 };
 
@@ -347,6 +351,19 @@ FullPlan plan(const KParams& kp, int op, int64_t nq, bool bf16_in) {
     f.canon_off = off;
     off = align256(off + static_cast<size_t>(kp.B) * kp.Hkv * call_units(kp, nq) *
                              std::max(1, kp.top_g) * sizeof(int32_t));
+  }
+  if (op == HGA_OP_PREFILL_BACKWARD && backward_mfma_supported(kp, bf16_in)) {
+    f.bwd_mfma = true;
+    const size_t q_elems = static_cast<size_t>(kp.B) * kp.Hq * nq * kp.d;
+    const size_t units = static_cast<size_t>(kp.B) * kp.Hkv * call_units(kp, nq);
+    f.doh_off = off;
+    off = align256(off + q_elems * sizeof(uint16_t));
+    f.dol_off = off;
+    off = align256(off + q_elems * sizeof(uint16_t));
+    f.vis_off = off;
+    off = align256(off + units * backward_vis_words(call_units(kp, nq)) * sizeof(uint32_t));
+    f.counts_off = off;
+    off = align256(off + units * sizeof(int32_t));
   }
   f.bytes = off;
   return f;
@@ -760,6 +777,15 @@ hga_status hga_prefill_backward(const hga_params* p, const void* Q, const void* 
   a.n = n;
   a.n_units = static_cast<int32_t>(n / kp.C);
   a.unit_slice = 64;
+  if (f.bwd_mfma) {
+    a.dOh = at<uint16_t>(ws, f.doh_off);
+    a.dOl = at<uint16_t>(ws, f.dol_off);
+    a.vis = at<uint32_t>(ws, f.vis_off);
+    a.vis_words = backward_vis_words(a.n_units);
+    a.counts = at<int32_t>(ws, f.counts_off);
+    HGA_TRY_HIP(launch_backward_mfma(a, static_cast<hipStream_t>(stream)), "backward (mfma)");
+    return ok();
+  }
   HGA_TRY_HIP(launch_backward(a, p->qkv_dtype == HGA_BF16, static_cast<hipStream_t>(stream)), "backward");
   return ok();
 }

@@ -130,10 +130,20 @@ struct BackwardArgs {
   float* stats;              // ws [B, Hq, n, 2]: base-2 log-sum-exp and D of every query row
   int64_t n;
   int32_t n_units;           // n / C
-  int32_t unit_slice;        // query chunks per dK/dV workgroup
+  int32_t unit_slice;        // query chunks per dK/dV workgroup (vector-ALU path)
+  // matrix-core path (bf16): workspace regions
+  uint16_t* dOh;             // [B, Hq, n, d] bf16: dO rounded
+  uint16_t* dOl;             // [B, Hq, n, d] bf16: dO - dOh rounded
+  uint32_t* vis;             // [B*Hkv, n_units, vis_words]: routed 16-key blocks per (key chunk, query chunk)
+  int32_t vis_words;         // backward_vis_words(n_units)
+  int32_t* counts;           // [B*Hkv, n_units]: query chunks that see each key chunk
 };
 bool backward_supported(const KParams& kp);
 hipError_t launch_backward(const BackwardArgs& a, bool bf16_in, hipStream_t st);
+// Matrix-core backward (bf16, C = 64, Hq/Hkv <= 4, G | 64, 16 | G).
+bool backward_mfma_supported(const KParams& kp, bool bf16_in);
+int backward_vis_words(int n_units);
+hipError_t launch_backward_mfma(const BackwardArgs& a, hipStream_t st);
 
 // Warm tier: per (b, kv head) a bounded LRU of routed groups in device memory.
 struct WarmArgs {
