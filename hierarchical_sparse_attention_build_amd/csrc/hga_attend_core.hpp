@@ -1,10 +1,17 @@
-// Step 5 of HGA on the vector ALUs: exact softmax attention of one query row
-// (all query heads that share a KV head) over a list of token slots, the
-// building block of the decode and generic attention kernels.
+// Step 5 of HGA: exact softmax attention of one query row (all query heads
+// that share a KV head) over a list of token slots, the building block of the
+// decode and generic attention kernels.
 // [HGA technical summary (it), Meccanismo Core, item 4: standard softmax over
 // the bounded set of exact tokens; no summary enters the output].
 //
-// Slots are cut into blocks of 16 rows.  A wave walks its blocks with an
+// Two lane engines share the block walk and the merge below (AttnLaneSel picks
+// one): AttnLane does the arithmetic on the vector ALUs (fp32 inputs);
+// AttnLaneMfma (bf16 inputs) puts QK^T and PV of each pair of 16-row blocks on
+// v_mfma_f32_16x16x32_bf16, the query heads padded to 16 columns.  Decode
+// moves a few bytes per FLOP either way, so the matrix cores serve here to cut
+// vector-ALU instructions per byte, not for their FLOP rate.
+//
+// AttnLane: slots are cut into blocks of 16 rows.  A wave walks its blocks with an
 // online softmax in base 2 and no LDS or barrier: lane (g, c) holds rows g,
 // g+4, g+8, g+12 of the block and the c-th sixteenth of each row, so one load
 // instruction fetches four whole rows; QK^T reduces over the 16 lanes of a row
