@@ -54,7 +54,7 @@ constexpr int kTile = 64;       // keys (and query rows) per tile = C
 constexpr int kRing = 3;        // LDS tiles of the dq kernel
 constexpr int kMaxTiles = 320;  // tiles of a unit
 constexpr int kPiece = 32;      // query chunks per dK/dV workgroup
-constexpr int kDkvWaves = 8;
+constexpr int kDkvWaves = 4;
 
 // x = hi + lo with hi, lo bf16 (round to nearest each)
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
@@ -421,23 +421,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_mfma_kernel(BackwardArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV kernel.  LDS: a ring of three step slots (Q, dO_hi, dO_lo rows padded
-// by 16 bytes, then (lse, D) of the 64 rows), the piece's visit list.
+// dK/dV kernel.  LDS: a ring of three step slots (32 rows of Q, dO_hi, dO_lo
+// padded by 16 bytes, then their (lse, D)), the piece's visit list; about
+// 79 KB, so two workgroups share a CU.
+constexpr int kDkvRows = 32;  // query rows per step
+
 template <int D>
 struct DkvSlot {
   static constexpr int KRB = (D / 8 + 1) * 16;
-  unsigned char q[kTile * KRB];
-  unsigned char oh[kTile * KRB];
-  unsigned char ol[kTile * KRB];
-  float st[kTile * 2];
+  unsigned char q[kDkvRows * KRB];
+  unsigned char oh[kDkvRows * KRB];
+  unsigned char ol[kDkvRows * KRB];
+  float st[kDkvRows * 2];
 };
-
-// s_waitcnt vmcnt(N) for the wave-uniform count n in {N_LO, N_LO + 1}
-template <int N_LO>
-__device__ __forceinline__ void wait_vmem_but_of(int n) {
-  if (n > N_LO) wait_vmem_but<N_LO + 1>();
-  else wait_vmem_but<N_LO>();
-}
 
 template <int D>
 __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardArgs a) {
@@ -447,9 +443,10 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
   constexpr int RB = D * 2;
   constexpr int KP = CH + 1;
   constexpr int KRB = KP * 16;
-  constexpr int NC = 3 * KP + 1;                 // 1 KB copies per step (the last: 512 B of statistics)
-  constexpr int NCW_LO = NC / kDkvWaves;         // copies per wave per step: NCW_LO, or one more
-  constexpr int NCW_HI = (NC + kDkvWaves - 1) / kDkvWaves;
+  constexpr int CPM = (kDkvRows * KP + 63) / 64;  // 1 KB copies per matrix (the last one partly)
+  constexpr int NC = 3 * CPM + 1;                 // and one of 256 bytes of statistics
+  constexpr int NCW = NC / kDkvWaves;             // copies per wave per step
+  static_assert(NC % kDkvWaves == 0, "every wave issues the same number of step copies");
   const KParams& kp = a.kp;
 
   // ---- key chunk.  Workgroups are dealt to the dies in turn, so die x % 8
@@ -466,13 +463,8 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int blk = tid >> 6;  // wave w owns 16-key block w of the chunk
   const int l16 = lane & 15, g = lane >> 4;
-  // Wave w owns 16-key block blk of the chunk and query rows 32 qh.. of every
-  // step.  Waves w and w + 4 share a SIMD; giving them blocks two apart keeps
-  // more SIMDs busy when a query chunk sees only some blocks.
-  const int qh = wid >> 2;
-  const int blk = (wid + 2 * qh) & 3;
 
   __shared__ __align__(16) DkvSlot<D> s0, s1, s2;
   __shared__ int vis_j[kPiece], vis_m[kPiece];
@@ -484,7 +476,7 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
   };
 
   // ---- the piece's query chunks
-  if (wid == 0) {
+  if (blk == 0) {
     const uint32_t* vrow = kp.top_g > 0 ? a.vis + (bh * n_units + c) * a.vis_words : nullptr;
     const int first = piece * kPiece;
     int seen = 0;
@@ -519,47 +511,59 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
 #pragma unroll
   for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x4_t{};
 
-  // ---- this lane's part of the step copies: copy cc = wid + 8 i is 1 KB
-  // cc % KP of matrix cc / KP (0 Q, 1 dO_hi, 2 dO_lo), lane position p =
-  // 64 (cc % KP) + lane = piece p % KP of row p / KP; copy 3 KP: statistics
-  const int ncw = (NC - wid + kDkvWaves - 1) / kDkvWaves;  // this wave's copies per step
-  uint32_t coff[NCW_HI];
+  // ---- this lane's part of the step copies: copy cc = wave + 4 i is 1 KB
+  // cm = cc % CPM of matrix cc / CPM (0 Q, 1 dO_hi, 2 dO_lo): lane position
+  // p = 64 cm + lane (< 32 KP) = piece p % KP of row p / KP; copy 3 CPM: the
+  // statistics, 16 bytes per lane (< 16)
+  uint32_t coff[NCW];
+  bool con[NCW];
 #pragma unroll
-  for (int i = 0; i < NCW_HI; ++i) {
-    const int cc = wid + kDkvWaves * i;
-    const int p = 64 * (cc % KP) + lane;
+  for (int i = 0; i < NCW; ++i) {
+    const int cc = blk + kDkvWaves * i;
+    const int p = 64 * (cc % CPM) + lane;
     const int r = p / KP, pc = p % KP;
-    coff[i] = cc < 3 * KP ? static_cast<uint32_t>(r * RB + ((pc < CH ? pc : 0) << 4)) : static_cast<uint32_t>(16 * lane);
+    const bool row_copy = cc < 3 * CPM;
+    coff[i] = row_copy ? static_cast<uint32_t>(r * RB + ((pc < CH ? pc : 0) << 4)) : static_cast<uint32_t>(16 * lane);
+    con[i] = row_copy ? p < kDkvRows * KP : lane < kDkvRows * 8 / 16;
   }
   __syncthreads();
-  const int n_steps = n_vis_sh * kp.gq;
+  const int steps_per_visit = kp.gq * (kTile / kDkvRows);
+  const int n_steps = n_vis_sh * steps_per_visit;
 
+  // step st: visit st / steps_per_visit, head (st / 2) % gq, rows 32 (st % 2)..
   auto copy_step = [&](auto S, int st) __attribute__((always_inline)) {
     if (st >= n_steps) return;
     DkvSlot<D>& sl = slot(S);
-    const int vi = st / kp.gq, hh = st - vi * kp.gq;
+    const int vi = st / steps_per_visit;
+    const int rem = st - vi * steps_per_visit;
+    const int hh = rem >> 1, half = rem & 1;
     const int64_t row0 = (static_cast<int64_t>(b) * kp.Hq + static_cast<int64_t>(h) * kp.gq + hh) * a.n +
-                         static_cast<int64_t>(vis_j[vi]) * kTile;
+                         static_cast<int64_t>(vis_j[vi]) * kTile + kDkvRows * half;
     const unsigned char* srcq = reinterpret_cast<const unsigned char*>(static_cast<const bf16*>(a.Q) + row0 * D);
     const unsigned char* srch = reinterpret_cast<const unsigned char*>(a.dOh + row0 * D);
     const unsigned char* srcl = reinterpret_cast<const unsigned char*>(a.dOl + row0 * D);
     const unsigned char* srcs = reinterpret_cast<const unsigned char*>(a.stats + row0 * 2);
 #pragma unroll
-    for (int i = 0; i < NCW_HI; ++i) {
-      const int cc = wid + kDkvWaves * i;
-      if (cc < KP) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcq + coff[i]),
-                                         (__attribute__((address_space(3))) void*)(sl.q + 1024 * cc), 16, 0, 0);
-      } else if (cc < 2 * KP) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srch + coff[i]),
-                                         (__attribute__((address_space(3))) void*)(sl.oh + 1024 * (cc - KP)), 16, 0, 0);
-      } else if (cc < 3 * KP) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcl + coff[i]),
-                                         (__attribute__((address_space(3))) void*)(sl.ol + 1024 * (cc - 2 * KP)), 16, 0, 0);
-      } else if (cc == 3 * KP && lane < 32) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcs + coff[i]),
-                                         (__attribute__((address_space(3))) void*)(sl.st), 16, 0, 0);
+    for (int i = 0; i < NCW; ++i) {
+      const int cc = blk + kDkvWaves * i;
+      const unsigned char* src;
+      unsigned char* dst;
+      if (cc < CPM) {
+        src = srcq;
+        dst = sl.q + 1024 * cc;
+      } else if (cc < 2 * CPM) {
+        src = srch;
+        dst = sl.oh + 1024 * (cc - CPM);
+      } else if (cc < 3 * CPM) {
+        src = srcl;
+        dst = sl.ol + 1024 * (cc - 2 * CPM);
+      } else {
+        src = srcs;
+        dst = reinterpret_cast<unsigned char*>(sl.st);
       }
+      if (con[i])
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + coff[i]),
+                                         (__attribute__((address_space(3))) void*)(dst), 16, 0, 0);
     }
   };
 
@@ -567,17 +571,18 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
   const int kl = 16 * blk + l16;  // this lane's key within the chunk
   auto compute_step = [&](auto S, int st) __attribute__((always_inline)) {
     const DkvSlot<D>& sl = slot(S);
-    const int vi = st / kp.gq;
+    const int vi = st / steps_per_visit;
+    const int q0 = kDkvRows * (st & 1);  // first query row of the step within the chunk
     const bool diag = vis_j[vi] == c;
-    // the block unseen, or (current chunk) entirely after the half's queries
-    if (!((vis_m[vi] >> blk) & 1) || (diag && 16 * blk > 32 * qh + 31)) return;
+    // the block unseen, or (current chunk) entirely after the step's queries
+    if (!((vis_m[vi] >> blk) & 1) || (diag && 16 * blk > q0 + kDkvRows - 1)) return;
     // S = Q K^T, dP = dO V^T on two 16-query tiles: lane (key l16, group g)
-    // gets query rows 32 qh + 16 qt + 4 g + i
+    // gets the step's query rows 16 qt + 4 g + i
     f32x4_t sc[2], pa[2], pb[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       sc[qt] = pa[qt] = pb[qt] = f32x4_t{};
-      const int rb = (32 * qh + 16 * qt + l16) * KRB + 16 * g;
+      const int rb = (16 * qt + l16) * KRB + 16 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         sc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(sl.q + rb + 64 * ks), kf[ks],
@@ -588,18 +593,18 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
                                                          pb[qt], 0, 0, 0);
       }
     }
-    // P and dS as A operands over the half's 32 query rows (slot 4 qt + i)
+    // P and dS as A operands over the step's 32 query rows (slot 4 qt + i)
     bf16x8_t ph, pl, dsh, dsl;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const int r0 = 32 * qh + 16 * qt + 4 * g;
+      const int r0 = 16 * qt + 4 * g;
       const float4 st01 = *reinterpret_cast<const float4*>(sl.st + 2 * r0);
       const float4 st23 = *reinterpret_cast<const float4*>(sl.st + 2 * r0 + 4);
       const float lse[4] = {st01.x, st01.z, st23.x, st23.z};
       const float dr[4] = {st01.y, st01.w, st23.y, st23.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = !diag || kl <= r0 + i;
+        const bool ok = !diag || kl <= q0 + r0 + i;
         const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[qt][i], scale, -lse[i])) : 0.f;
         __bf16 hi, lo;
         split_bf16(p, hi, lo);
@@ -610,13 +615,13 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
         dsl[4 * qt + i] = lo;
       }
     }
-    // per 16-dimension tile: Q, dO_hi, dO_lo with the half's query rows along
-    // k (transposing LDS reads); dV += P^T dO, dK += dS^T Q
+    // per 16-dimension tile: Q, dO_hi, dO_lo with the query rows along k
+    // (transposing LDS reads); dV += P^T dO, dK += dS^T Q
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      const bf16x8_t bq = lds_frag_tr16(sl.q, KRB, 32 * qh, 16 * t, lane);
-      const bf16x8_t bh_ = lds_frag_tr16(sl.oh, KRB, 32 * qh, 16 * t, lane);
-      const bf16x8_t bl = lds_frag_tr16(sl.ol, KRB, 32 * qh, 16 * t, lane);
+      const bf16x8_t bq = lds_frag_tr16(sl.q, KRB, 0, 16 * t, lane);
+      const bf16x8_t bh_ = lds_frag_tr16(sl.oh, KRB, 0, 16 * t, lane);
+      const bf16x8_t bl = lds_frag_tr16(sl.ol, KRB, 0, 16 * t, lane);
       dv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bh_, dv[t], 0, 0, 0);
       dv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bl, dv[t], 0, 0, 0);
       dv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bh_, dv[t], 0, 0, 0);
@@ -627,11 +632,11 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
 
   // ---- steps through a ring of three slots: step s computes while the copies
   // of steps s + 1 and s + 2 are in flight.  The barrier after step s waits
-  // (per wave) for every copy but its newest ncw loads, i.e. for step s + 1's,
+  // (per wave) for every copy but its newest NCW loads, i.e. for step s + 1's,
   // then LDS-only fences order the slot reads and the next copy into the slot
   // just read.
   auto step_barrier = [&](bool newest_in_flight) __attribute__((always_inline)) {
-    if (newest_in_flight) wait_vmem_but_of<NCW_LO>(ncw);
+    if (newest_in_flight) wait_vmem_but<NCW>();
     else wait_vmem_but<0>();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -651,37 +656,25 @@ __global__ __launch_bounds__(kDkvWaves * 64) void bwd_dkv_mfma_kernel(BackwardAr
     if (st + 1 < n_steps) one(std::integral_constant<int, 1>{}, st + 1);
     if (st + 2 < n_steps) one(std::integral_constant<int, 2>{}, st + 2);
   }
-  __syncthreads();
 
-  // ---- the two query halves of each block meet in LDS (slot 0), dK then dV
-  float* red = reinterpret_cast<float*>(&s0);  // [blk][t][i][lane]
-  static_assert(4 * DT * 4 * 64 * sizeof(float) <= sizeof(DkvSlot<D>), "reduction fits a slot");
+  // ---- the block's rows of dK (scaled by 1/sqrt(d)) and dV: lane (l16, g)
+  // holds dimension 16 t + l16 of keys 4 g + i
   const int64_t key0 = bh * kp.n_cap + static_cast<int64_t>(c) * kTile + 16 * blk + 4 * g;
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    f32x4_t* acc = which == 0 ? dk : dv;
-    float* out = which == 0 ? a.dK : a.dV;
-    const float sc = which == 0 ? kp.inv_sqrt_d : 1.f;
-    if (qh == 1) {
+  for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[((blk * DT + t) * 4 + i) * 64 + lane] = acc[t][i];
+    for (int i = 0; i < 4; ++i) {
+      float* pk = a.dK + (key0 + i) * D + 16 * t + l16;
+      float* pv = a.dV + (key0 + i) * D + 16 * t + l16;
+      const float vk = dk[t][i] * kp.inv_sqrt_d, vv = dv[t][i];
+      if (shared_rows) {
+        __hip_atomic_fetch_add(pk, vk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(pv, vv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *pk = vk;
+        *pv = vv;
+      }
     }
-    __syncthreads();
-    if (qh == 0) {
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = (acc[t][i] + red[((blk * DT + t) * 4 + i) * 64 + lane]) * sc;
-          float* dst = out + (key0 + i) * D + 16 * t + l16;
-          if (shared_rows) __hip_atomic_fetch_add(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          else *dst = v;
-        }
-    }
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------

@@ -67,6 +67,7 @@ hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st) {
 //     gets the j-th of them;
 //   * list entries outside [0, n_cap / G) are ignored.
 constexpr int kWarmThreads = 256;
+constexpr int kWarmMapGroups = 8192;  // contexts of up to this many groups per (b, kv head) use the LDS map
 
 __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
   const KParams& kp = a.kp;
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
   __shared__ int slot[kWarmMaxList];    // its slot: >= 0 hit or assigned, -1 ignored, -2 missing
   __shared__ int victim[kWarmMaxList];  // slots taken by the missing groups, ascending
   __shared__ int n_hit, n_miss;
+  __shared__ int gmap[kWarmMapGroups];  // lowest slot caching each group id (kWarmMaxSlots: none)
 
   int32_t* gtags = a.tags + bh * S;
   int32_t* gstamps = a.stamps + bh * S;
@@ -95,20 +97,36 @@ __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
     const int g = a.group_idx[bh * TG + i];
     entry[i] = g >= 0 && g < n_groups_cap ? g : -1;
   }
-  __syncthreads();
-  // ---- hits against the slots as they were before this step: one wave per
-  // entry, its lanes comparing 64 slots at a time
-  for (int i = wid; i < TG; i += kWarmThreads / kWave) {
-    const int g = entry[i];
-    int found = g < 0 ? -1 : -2;
-    for (int s0 = 0; s0 < S && g >= 0; s0 += kWave) {
-      const uint64_t m = __ballot(s0 + lane < S && tags[s0 + lane] == g);
-      if (m) {
-        found = s0 + __builtin_ctzll(m);
-        break;
-      }
+  // ---- hits against the slots as they were before this step
+  if (n_groups_cap <= kWarmMapGroups) {
+    // indexed by group id: a map from group to its lowest caching slot,
+    // built from the tags, then one read per entry
+    for (int g = tid; g < n_groups_cap; g += kWarmThreads) gmap[g] = kWarmMaxSlots;
+    __syncthreads();
+    for (int s = tid; s < S; s += kWarmThreads) {
+      const int t = tags[s];
+      if (t >= 0 && t < n_groups_cap) atomicMin(&gmap[t], s);
     }
-    if (lane == 0) slot[i] = found;
+    __syncthreads();
+    for (int i = tid; i < TG; i += kWarmThreads) {
+      const int g = entry[i];
+      slot[i] = g < 0 ? -1 : (gmap[g] < kWarmMaxSlots ? gmap[g] : -2);
+    }
+  } else {
+    __syncthreads();
+    // one wave per entry, its lanes comparing 64 slots at a time
+    for (int i = wid; i < TG; i += kWarmThreads / kWave) {
+      const int g = entry[i];
+      int found = g < 0 ? -1 : -2;
+      for (int s0 = 0; s0 < S && g >= 0; s0 += kWave) {
+        const uint64_t m = __ballot(s0 + lane < S && tags[s0 + lane] == g);
+        if (m) {
+          found = s0 + __builtin_ctzll(m);
+          break;
+        }
+      }
+      if (lane == 0) slot[i] = found;
+    }
   }
   __syncthreads();
   for (int i = tid; i < TG; i += kWarmThreads)

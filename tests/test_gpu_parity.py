@@ -598,14 +598,18 @@ def test_offload_decode_full_size_sampled(hga):
         assert e <= TOL[s.dtype]
 
 
-def test_offload_warm_tier_steps(hga):
+@pytest.mark.parametrize("batch,n_tokens,steps", [
+    (2, 16384, 6),           # 1024 groups per (b, kv head): the lookup's group-to-slot map
+    (1, 8192 * 16 + 4096, 3),  # 8448 groups: above the map's 8192, the slot scan
+])
+def test_offload_warm_tier_steps(hga, batch, n_tokens, steps):
     """Warm tier over several decode steps with drifting queries: per step the
     output equals the staging path's bit for bit and the oracle's attention over
     the step's routed lists, the LRU state (tags, stamps, clock) and the hit and
     miss counts equal the oracle's LRU fed with the same routed lists, and every
     cached slot holds its group's rows."""
-    s = W.spec("offload_decode_128k", batch=2, n_tokens=16384)
-    say(f"[offload warm tier] seed={s.seed}")
+    s = W.spec("offload_decode_128k", batch=batch, n_tokens=n_tokens)
+    say(f"[offload warm tier] B={batch} n={n_tokens} seed={s.seed}")
     w = W.make(s)
     p = params_of(s)
     cfg = cfg_of(s)
@@ -639,7 +643,7 @@ def test_offload_warm_tier_steps(hga):
     Q0 = W.to_f64(w.Q, s.dtype).astype(np.float32)
     n_groups_cap = n // G
     tot_hits = tot_miss = 0
-    for step in range(6):
+    for step in range(steps):
         q = Q0 + 0.5 * rng.standard_normal(Q0.shape).astype(np.float32)
         Qs = W.to_torch(W.bf16_bits(q), "bf16").cuda()
         seq = torch.full((B,), n - 5 + step, dtype=torch.int32, device="cuda")  # positions inside chunk j
