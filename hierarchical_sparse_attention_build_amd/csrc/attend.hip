@@ -73,11 +73,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
   const Forced fc = forced_chunks(j, kp.n_sink, kp.n_local);
   const int nF = fc.n * kp.C;
   const int n_slots = nF + kp.top_g * kp.G;
+  // part 3: both parts in one grid, workgroups [0, part1_splits) on the forced
+  // slots and the rest on the routed ones, with the block ranges and partial
+  // slots of two launches (part 1, then part 2 at part_offset part1_splits)
+  const int part = a.part == 3 ? (x < a.part1_splits ? 1 : 2) : a.part;
+  const int xs = a.part == 3 && part == 2 ? x - a.part1_splits : x;  // index within the part
   int R0 = 0, R1 = n_slots;
-  if (a.part == 1) R1 = nF;
-  if (a.part == 2) R0 = nF;
+  if (part == 1) R1 = nF;
+  if (part == 2) R0 = nF;
   const int nblocks = (R1 - R0 + kAttnBlock - 1) / kAttnBlock;
-  const int bb = min(nblocks, x * a.tiles_per_split);
+  const int bb = min(nblocks, xs * a.tiles_per_split);
   const int be = min(nblocks, bb + a.tiles_per_split);
   const int n_groups_cap = static_cast<int>(kp.n_cap / kp.G);
 

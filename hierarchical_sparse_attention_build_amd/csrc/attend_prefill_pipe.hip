@@ -21,13 +21,13 @@
 // conflicts and every k-step's offset is an immediate.
 //
 // Per wave the work is pipelined over 32-key sub-blocks b:
+//   the max of S(b) (launched during b - 1) decides whether the reference
+//   max m rises (when it exceeds m by more than 2^8, base 2); a rise rescales
+//   O, l and the pending P(b-1);
 //   O^T   += V^T P^T(b-1) (fp16 MFMA, V fragments read during b-1) \  matrix
 //   S(b+1) = K Q^T     (bf16 MFMA, 32x32x16)                        /  cores
 //   P(b)   = exp2(S(b) scale - m) (vector ALUs, concurrently), and the V
-//            fragments of b are read for the next step;
-// then the max of S(b+1) decides whether the reference max m rises (when it
-// exceeds m by more than 2^8, base 2); a rise rescales O, l and the pending
-// P(b).  P is rounded to fp16 toward zero (relative error < 2^-10; the row
+//            fragments of b are read for the next step.  P is rounded to fp16 toward zero (relative error < 2^-10; the row
 // sum adds the same rounded values), V to fp16 exactly for |v| < 65504.
 #include "hga_device.hpp"
 #include "hga_kernels.hpp"
@@ -315,14 +315,32 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
   const int nsb = 2 * n_tiles;
   const f16x2_t ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
-  // One 32-key sub-block bsb: P.V of the previous one, S of the next one
-  // (K tile kn), P of this one, and the V fragments of this one (V tile vs)
-  // for the next P.V.  The last sub-block's "next" scores read whatever the
-  // slot holds and are dropped.
+  // One 32-key sub-block bsb.  Its scores S(bsb) were launched one sub-block
+  // earlier, so their mask and max come first (a rise of the reference max
+  // rescales O, l and the pending P(bsb - 1)); then P.V of the previous
+  // sub-block and S of the next one (K tile kn) go to the matrix cores while
+  // P(bsb) and its row sum are computed and the V fragments of this
+  // sub-block (V tile vs) are read for the next P.V.  The last sub-block's
+  // "next" scores read whatever the slot holds and are dropped.
   auto sub = [&](int bsb, const unsigned char* kn, const unsigned char* vs) __attribute__((always_inline)) {
-    const bool has_next = bsb + 1 < nsb;
+    if (bsb > 0) {  // sub-block 0's max is the initial reference
+      mask(s_cur, bsb >> 1, bsb & 1);
+      const float tmax = tile_max(s_cur);
+      const bool raise = !(tmax <= m_run + 8.f);
+      if (__ballot(raise)) {
+        const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+        const _Float16 ah = static_cast<_Float16>(alpha);
+        pk_prev[0] *= ah;
+        pk_prev[1] *= ah;
+        m_run = m_new;
+      }
+    }
     pv(pk_prev);
-    f32x16_t s_nxt = qk(kn, (bsb + 1) & 1);
+    const f32x16_t s_nxt = qk(kn, (bsb + 1) & 1);
     f16x8_t pk_cur[2];
     float rs = 0.f;
 #pragma unroll
@@ -342,23 +360,6 @@ __global__ __launch_bounds__(NW * 64) void attend_prefill_pipe_kernel(AttendArgs
       float pa, pb;
       dpp::swap32(rs, pa, pb);
       l_run += pa + pb;
-    }
-    if (has_next) {
-      const int tn = (bsb + 1) >> 1;
-      mask(s_nxt, tn, (bsb + 1) & 1);
-      const float tmax = tile_max(s_nxt);
-      const bool raise = !(tmax <= m_run + 8.f);
-      if (__ballot(raise)) {
-        const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
-        const _Float16 ah = static_cast<_Float16>(alpha);
-        pk_cur[0] *= ah;
-        pk_cur[1] *= ah;
-        m_run = m_new;
-      }
     }
     pk_prev[0] = pk_cur[0];
     pk_prev[1] = pk_cur[1];

@@ -929,17 +929,6 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
   int32_t* ci = chunk_idx ? chunk_idx : at<int32_t>(ws, f.idx.ci_off);
   int32_t* gi = group_idx ? group_idx : at<int32_t>(ws, f.idx.gi_off);
 
-  // events ordering the copy stream between routing and the routed attention:
-  // one pair per thread and device, made on first use and kept
-  constexpr int kMaxDevices = 64;
-  thread_local hipEvent_t ev_pair[kMaxDevices][2] = {};
-  int dev = 0;
-  HGA_TRY_HIP(hipGetDevice(&dev), "get device");
-  if (dev < 0 || dev >= kMaxDevices) return fail(HGA_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
-  for (int i = 0; i < 2; ++i)
-    if (!ev_pair[dev][i]) HGA_TRY_HIP(hipEventCreateWithFlags(&ev_pair[dev][i], hipEventDisableTiming), "event create");
-  hipEvent_t ev_routed = ev_pair[dev][0], ev_copied = ev_pair[dev][1];
-
   const int64_t hot_rows = static_cast<int64_t>(kp.n_sink + kp.n_local + 1) * kp.C;
   RouteArgs ra = route_args(kp, f, ws, Q, 1, seq_len, -1, chunk_sum, group_sum, ci, gi, nullptr);
   ra.build_summary = 1;
@@ -968,12 +957,43 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
     wa.slots = warm->slots;
     wa.elem_bytes = static_cast<int32_t>(elem_bytes(p));
     HGA_TRY_HIP(launch_warm_lookup(wa, st), "warm lookup");
+    HGA_TRY_HIP(launch_warm_fill(wa, st), "warm fill");
   }
+  AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K_hot, V_hot, gi, 1, O, nullptr,
+                              p->out_dtype == HGA_BF16);
+  aa.kv.base = K_hot;
+  aa.kv.bh_rows = hot_rows;
+  aa.kv.ring = 1;
+  aa.K_stage = Kst;
+  aa.V_stage = Vst;
+  if (warm) {
+    // The warm tier's copies are the few groups missing from the cache: they
+    // run on the launch stream (a hand-off between streams would cost more
+    // than the overlap gains), and both parts of the attention go in one grid
+    // with the block ranges and merge order of the two launches below.
+    aa.stage_slot = wa.slot_of;
+    aa.stage_slots = warm->slots;
+    aa.part = 3;
+    aa.part1_splits = f.attend.splits1;
+    aa.splits = f.attend.splits1 + f.attend.splits2;
+    aa.part_offset = 0;
+    HGA_TRY_HIP(launch_attend_splitk(aa, bf, st), "attend");
+    return ok();
+  }
+
+  // events ordering the copy stream between routing and the routed attention:
+  // one pair per thread and device, made on first use and kept
+  constexpr int kMaxDevices = 64;
+  thread_local hipEvent_t ev_pair[kMaxDevices][2] = {};
+  int dev = 0;
+  HGA_TRY_HIP(hipGetDevice(&dev), "get device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HGA_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  for (int i = 0; i < 2; ++i)
+    if (!ev_pair[dev][i]) HGA_TRY_HIP(hipEventCreateWithFlags(&ev_pair[dev][i], hipEventDisableTiming), "event create");
+  hipEvent_t ev_routed = ev_pair[dev][0], ev_copied = ev_pair[dev][1];
   HGA_TRY_HIP(hipEventRecord(ev_routed, st), "event record");
   HGA_TRY_HIP(hipStreamWaitEvent(cst, ev_routed, 0), "stream wait");
-  if (warm) {
-    HGA_TRY_HIP(launch_warm_fill(wa, cst), "warm fill");
-  } else {
+  {
     GatherArgs ga{};
     ga.kp = kp;
     ga.K_host = K_host;
@@ -987,18 +1007,6 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
   HGA_TRY_HIP(hipEventRecord(ev_copied, cst), "event record");
 
   // forced (hot) slots overlap the copy; routed slots read the staging buffer
-  // or the warm slots
-  AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K_hot, V_hot, gi, 1, O, nullptr,
-                              p->out_dtype == HGA_BF16);
-  aa.kv.base = K_hot;
-  aa.kv.bh_rows = hot_rows;
-  aa.kv.ring = 1;
-  aa.K_stage = Kst;
-  aa.V_stage = Vst;
-  if (warm) {
-    aa.stage_slot = wa.slot_of;
-    aa.stage_slots = warm->slots;
-  }
   aa.part = 1;
   aa.splits = f.attend.splits1;
   aa.part_offset = 0;

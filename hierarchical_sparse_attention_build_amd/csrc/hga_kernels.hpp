@@ -68,7 +68,9 @@ struct AttendArgs {
   int32_t out_bf16;
   int32_t splits;         // workgroups per (bh, query row) in this launch
   int32_t tiles_per_split; // 16-row blocks per workgroup
-  int32_t part;           // 0 all slots, 1 forced slots only, 2 routed slots only
+  int32_t part;           // 0 all slots, 1 forced slots only, 2 routed slots only,
+                          // 3 both parts in one grid (part1_splits workgroups on the forced slots)
+  int32_t part1_splits;
   int32_t part_offset;    // partial slot of this launch's split 0
   int32_t parts_total;    // partial slots per (bh, row) over all launches
   float* partials;        // ws

@@ -207,9 +207,8 @@ def warm_state(p, slots: int, device="cuda"):
 
 def decode_offload_warm(p, Q, K_host, V_host, K_hot, V_hot, n_cap, seq_len, chunk_sum, group_sum, O,
                         warm, ws, chunk_idx=None, group_idx=None, stream=None, copy_stream=None):
-    """hga_decode_offload_warm; ``warm`` is a dict from ``warm_state``."""
-    if copy_stream is None:
-        raise HGAError(-1, "decode_offload_warm needs a copy stream")
+    """hga_decode_offload_warm; ``warm`` is a dict from ``warm_state``.  The
+    library does not use ``copy_stream`` for the warm tier (it may be None)."""
     w = HGAWarm(_ptr(warm["K"]), _ptr(warm["V"]), _ptr(warm["tags"]), _ptr(warm["stamps"]),
                 _ptr(warm["clock"]), _ptr(warm.get("hits")), _ptr(warm.get("misses")), warm["slots"])
     _check(lib().hga_decode_offload_warm(ctypes.byref(p), _ptr(Q), _ptr(K_host), _ptr(V_host),
