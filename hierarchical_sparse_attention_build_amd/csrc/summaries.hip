@@ -56,30 +56,20 @@ __global__ __launch_bounds__(kSumThreads) void summaries_fast_kernel(const bf16*
   const int wid = wave_id(), nw = static_cast<int>(blockDim.x) / kWave;
   const bool one_group_per_wave = kp.m <= nw;
   auto rows_of = [&](int c) { return K + (bh * kp.n_cap + static_cast<int64_t>(c) * kp.C) * D; };
-  // two register buffers: chunk c's rows in rows[(c - c0) % 2]; with one group
-  // per wave, the rows of chunk c + 2 are requested once chunk c's are used
-  GroupRows<D, MAXL> rows[2];
-  if (wid < kp.m) {
-    load_group_rows<D, MAXL>(rows_of(c0), kp, wid, rows[0]);
-    if (one_group_per_wave && c0 + 1 < c1) load_group_rows<D, MAXL>(rows_of(c0 + 1), kp, wid, rows[1]);
-  }
+  GroupRows<D, MAXL> rows;
+  if (wid < kp.m) load_group_rows<D, MAXL>(rows_of(c0), kp, wid, rows);
   build_summary_tables<D>(kp, rot, crot);
-  auto chunk = [&](int c, GroupRows<D, MAXL>& r) __attribute__((always_inline)) {
+  for (int c = c0; c < c1; ++c) {
     float* gmean = ((c - c0) & 1) ? gmean1 : gmean0;
     float* gs_out = group_sum + (bh * kp.n_chunks_cap * kp.m + static_cast<int64_t>(c) * kp.m) * D;
     for (int g = wid; g < kp.m; g += nw) {
-      if (g != wid || !one_group_per_wave) {
-        if (g != wid || c != c0) load_group_rows<D, MAXL>(rows_of(c), kp, g, r);
-      }
-      group_mean_wave<D, MAXL>(r, kp, rot, g, gs_out, gmean);
+      if (g != wid) load_group_rows<D, MAXL>(rows_of(c), kp, g, rows);
+      group_mean_wave<D, MAXL>(rows, kp, rot, g, gs_out, gmean);
     }
-    if (one_group_per_wave && wid < kp.m && c + 2 < c1) load_group_rows<D, MAXL>(rows_of(c + 2), kp, wid, r);
+    // the next chunk's rows are on their way during the barrier and the combine
+    if (one_group_per_wave && wid < kp.m && c + 1 < c1) load_group_rows<D, MAXL>(rows_of(c + 1), kp, wid, rows);
     __syncthreads();
     combine_chunk<D>(kp, crot, gmean, chunk_sum + (bh * kp.n_chunks_cap + c) * D);
-  };
-  for (int c = c0; c < c1; c += 2) {
-    chunk(c, rows[0]);
-    if (c + 1 < c1) chunk(c + 1, rows[1]);
   }
 }
 
