@@ -1033,3 +1033,74 @@ def test_prefill_64k_single_call_sampled(hga):
     say(f"  sampled units {n_units} unique routing {len(unique)}  O max-abs {emax:.3e}")
     assert emax <= TOL[s.dtype]
     assert torch.isfinite(out).all()
+
+
+def test_prefill_backward_full_size_sampled(hga):
+    """The benchmarked backward at full size (32K tokens, 32/8 heads, the lists
+    of the GPU's own routing), against the oracle's gradients on samples: dQ of
+    whole query chunks (a row's gradient depends on its own visible set only),
+    and dK, dV of whole key chunks, summed over every query chunk that sees
+    them (routed or forced, any KV head)."""
+    s = W.spec("prefill_32k")
+    say(f"[prefill backward full] prefill_32k seed={s.seed}")
+    w = W.make(s)
+    cfg = cfg_of(s)
+    p = params_of(s)
+    B, H, n, C, d, m = s.batch, s.n_kv_heads, s.n_tokens, s.chunk_size, s.head_dim, s.chunk_size // s.group_size
+    nU = n // C
+    cs, gs = _summ_tables(s)
+    gi = torch.empty((B, H, nU, s.top_g), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, s.n_q_heads, n, d), device="cuda")
+    Qd, Kd, Vd = dev(w.Q, s.dtype), dev(w.K, s.dtype), dev(w.V, s.dtype)
+    hga.prefill(p, Qd, Kd, Vd, n, cs, gs, out, hga.workspace(p, hga.OP_PREFILL, n, n), group_idx=gi)
+    g = torch.Generator(device="cuda").manual_seed(s.seed + 5)
+    dO = torch.randn((B, s.n_q_heads, n, d), device="cuda", generator=g)
+    dQ = torch.empty_like(dO)
+    dK = torch.empty((B, H, n, d), device="cuda")
+    dV = torch.empty_like(dK)
+    hga.prefill_backward(p, Qd, Kd, Vd, n, gi, dO, dQ, dK, dV, hga.workspace(p, hga.OP_PREFILL_BACKWARD, n, n))
+    torch.cuda.synchronize()
+    gi_n = gi.cpu().numpy()
+    dO_n = dO.cpu().numpy().astype(np.float64)
+    Kf, Vf = f64(w.K, s.dtype), f64(w.V, s.dtype)
+    Qb = w.Q  # bf16 bits; rows converted per sampled chunk
+
+    def oracle_block(j):
+        """The oracle's gradients from the 64 query rows of chunk j (all heads)."""
+        rows = slice(j * C, (j + 1) * C)
+        Qj = W.to_f64(Qb[:, :, rows], s.dtype)
+        return O.attend_backward(Qj, np.full(B, j * C, dtype=np.int64), Kf, Vf, gi_n[:, :, j:j + 1],
+                                 dO_n[:, :, rows], cfg, H)
+
+    # dQ of sampled query chunks
+    eq, scq = 0.0, 1.0
+    got_q = dQ.cpu().numpy()
+    for j in (2, 257, nU - 1):
+        rdQ, _, _ = oracle_block(j)
+        eq = max(eq, max_abs(got_q[:, :, j * C:(j + 1) * C], rdQ))
+        scq = max(scq, float(np.abs(rdQ).max()))
+    say(f"  dQ (3 query chunks) max-abs {eq:.3e} (scale {scq:.2f})")
+    assert eq <= 1e-4 * scq
+
+    # dK, dV of sampled key chunks: every query chunk that sees a block of c
+    got_k, got_v = dK.cpu().numpy(), dV.cpu().numpy()
+    for c in (nU - 6, 3 * nU // 4):
+        seers = []
+        for j in range(c, nU):
+            forced = c < s.n_sink or j - c <= s.n_local
+            routed = any((x >= 0 and x // m == c) for x in gi_n[:, :, j].ravel())
+            if forced or routed:
+                seers.append(j)
+        rK = np.zeros((B, H, C, d))
+        rV = np.zeros((B, H, C, d))
+        for j in seers:
+            _, pk, pv = oracle_block(j)
+            rK += pk[:, :, c * C:(c + 1) * C]
+            rV += pv[:, :, c * C:(c + 1) * C]
+        ek = max_abs(got_k[:, :, c * C:(c + 1) * C], rK)
+        ev = max_abs(got_v[:, :, c * C:(c + 1) * C], rV)
+        sk, sv = max(1.0, float(np.abs(rK).max())), max(1.0, float(np.abs(rV).max()))
+        say(f"  key chunk {c} (seen by {len(seers)} query chunks): dK max-abs {ek:.3e} (scale {sk:.2f}), "
+            f"dV max-abs {ev:.3e} (scale {sv:.2f})")
+        assert ek <= 1e-4 * sk and ev <= 1e-4 * sv
+    assert np.isfinite(got_q).all() and np.isfinite(got_k).all() and np.isfinite(got_v).all()
