@@ -125,9 +125,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
     const int64_t tok = static_cast<int64_t>(g) * kp.G + (rs - e * kp.G);
     if (tok > t) return false;
     if (staged_routed && a.stage_slot) {
-      ro = ((static_cast<int64_t>(bh) * a.stage_slots + sm.sl[e]) * kp.G + (rs - e * kp.G)) * D;
-      kr = Ks + ro;
-      vr = Vs + ro;
+      const int sl = sm.sl[e];
+      if (sl >= 0) {  // cached: the slot's rows
+        ro = ((static_cast<int64_t>(bh) * a.stage_slots + sl) * kp.G + (rs - e * kp.G)) * D;
+        kr = Ks + ro;
+        vr = Vs + ro;
+      } else {  // missing (-2 - slot): the rows in host memory (written back to the slot)
+        ro = (static_cast<int64_t>(bh) * kp.n_cap + tok) * D;
+        kr = static_cast<const T*>(a.K_host) + ro;
+        vr = static_cast<const T*>(a.V_host) + ro;
+      }
     } else if (staged_routed) {
       ro = (static_cast<int64_t>(bh) * kp.top_g * kp.G + rs) * D;
       kr = Ks + ro;
@@ -140,7 +147,27 @@ __global__ __launch_bounds__(kAttThreads) void attend_splitk_kernel(AttendArgs a
     return true;
   };
 
-  st.run(R0, bb + wid, be, kAttWaves, kp.scale_log2, row);
+  if (a.stage_slot && a.K_host) {
+    // warm tier: a missing group's rows, read from host memory, also go into
+    // the slot the lookup gave it (-2 - slot in the slot list)
+    T* Kw = static_cast<T*>(const_cast<void*>(a.K_stage));
+    T* Vw = static_cast<T*>(const_cast<void*>(a.V_stage));
+    auto wb = [&](int s, T*& kd, T*& vd) -> bool {
+      if (s < nF || s >= R1) return false;
+      const int rs = s - nF;
+      const int e = kp.log2G >= 0 ? rs >> kp.log2G : rs / kp.G;
+      const int g = sm.gl[e];
+      const int sl = sm.sl[e];
+      if (g < 0 || g >= n_groups_cap || sl > -2) return false;
+      const int64_t wo = ((static_cast<int64_t>(bh) * a.stage_slots + (-2 - sl)) * kp.G + (rs - e * kp.G)) * D;
+      kd = Kw + wo;
+      vd = Vw + wo;
+      return true;
+    };
+    st.run(R0, bb + wid, be, kAttWaves, kp.scale_log2, row, wb);
+  } else {
+    st.run(R0, bb + wid, be, kAttWaves, kp.scale_log2, row);
+  }
   attn_merge_waves(st, sm.mg);
 
   if (a.parts_total == 1) {

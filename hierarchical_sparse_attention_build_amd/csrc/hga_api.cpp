@@ -275,10 +275,9 @@ IdxPlan plan_idx(const KParams& kp, int n_units, size_t base) {
   return r;
 }
 
-// Warm-tier lists of a cold-tier decode step: slot of each routed entry, the
-// (slot, group) pairs to copy in, their count.
+// Warm-tier list of a decode step: the slot of each routed entry.
 struct WarmPlan {
-  size_t slot_off, miss_off, count_off, bytes;
+  size_t slot_off, bytes;
 };
 
 WarmPlan plan_warm(const KParams& kp, size_t base) {
@@ -288,10 +287,6 @@ WarmPlan plan_warm(const KParams& kp, size_t base) {
   size_t off = base;
   r.slot_off = off;
   off = align256(off + units * tg * sizeof(int32_t));
-  r.miss_off = off;
-  off = align256(off + units * tg * 2 * sizeof(int32_t));
-  r.count_off = off;
-  off = align256(off + units * sizeof(int32_t));
   r.bytes = off - base;
   return r;
 }
@@ -952,12 +947,9 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
     wa.hits = warm->hits;
     wa.misses = warm->misses;
     wa.slot_of = at<int32_t>(ws, f.warm.slot_off);
-    wa.miss_list = at<int32_t>(ws, f.warm.miss_off);
-    wa.miss_count = at<int32_t>(ws, f.warm.count_off);
     wa.slots = warm->slots;
     wa.elem_bytes = static_cast<int32_t>(elem_bytes(p));
     HGA_TRY_HIP(launch_warm_lookup(wa, st), "warm lookup");
-    HGA_TRY_HIP(launch_warm_fill(wa, st), "warm fill");
   }
   AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K_hot, V_hot, gi, 1, O, nullptr,
                               p->out_dtype == HGA_BF16);
@@ -967,12 +959,16 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
   aa.K_stage = Kst;
   aa.V_stage = Vst;
   if (warm) {
-    // The warm tier's copies are the few groups missing from the cache: they
-    // run on the launch stream (a hand-off between streams would cost more
-    // than the overlap gains), and both parts of the attention go in one grid
-    // with the block ranges and merge order of the two launches below.
+    // The warm tier's copies are the few groups missing from the cache: the
+    // attention reads their rows from host memory and writes them into the
+    // slots the lookup chose, so the copy overlaps the attention of the
+    // cached groups and needs no second stream.  Both parts of the attention
+    // go in one grid with the block ranges and merge order of the two
+    // launches below.
     aa.stage_slot = wa.slot_of;
     aa.stage_slots = warm->slots;
+    aa.K_host = K_host;
+    aa.V_host = V_host;
     aa.part = 3;
     aa.part1_splits = f.attend.splits1;
     aa.splits = f.attend.splits1 + f.attend.splits2;

@@ -54,6 +54,25 @@ __device__ __forceinline__ RawVec<BYTES> load_raw(const void* p) {
 }
 
 template <int BYTES>
+__device__ __forceinline__ void store_raw(void* p, const RawVec<BYTES>& r) {
+  if constexpr (BYTES == 8) *reinterpret_cast<uint2*>(p) = r.v;
+  else if constexpr (BYTES == 16) *reinterpret_cast<uint4*>(p) = r.v;
+  else {
+    reinterpret_cast<uint4*>(p)[0] = r.v0;
+    reinterpret_cast<uint4*>(p)[1] = r.v1;
+  }
+}
+
+// Row write-back of the lane engines' run(): wb(s, kdst, vdst) returns true
+// and sets where the K and V rows of slot s, as loaded, are also stored (the
+// warm tier's missing groups, read from host memory, go into their cache
+// slots on the way).  The default stores nothing and compiles to nothing.
+struct NoWriteBack {
+  template <typename P>
+  __device__ __forceinline__ bool operator()(int, P*&, P*&) const { return false; }
+};
+
+template <int BYTES>
 __device__ __forceinline__ RawVec<BYTES> zero_raw() {
   RawVec<BYTES> r;
   if constexpr (BYTES == 8) r.v = make_uint2(0u, 0u);
@@ -114,8 +133,9 @@ struct AttnLane {
   // sets the K and V row pointers of slot s and returns false for a masked
   // slot; it must then still point them at a readable row of finite values
   // (its score is replaced by -inf, so that row's values get weight 0).
-  template <int PF = 2, typename RowFn>
-  __device__ __forceinline__ void run(int R0, int first, int end, int step, float scale_log2, RowFn row) {
+  template <int PF = 2, typename RowFn, typename WbFn = NoWriteBack>
+  __device__ __forceinline__ void run(int R0, int first, int end, int step, float scale_log2, RowFn row,
+                                      WbFn wb = WbFn{}) {
     const int lane = threadIdx.x & (kWave - 1);
     const int rg = lane >> 4;
     const int cc = lane & 15;
@@ -132,6 +152,12 @@ struct AttnLane {
         ok[i] = row(s, kp, vp);
         kr[i] = load_raw<RB>(kp + cc * EPL);
         vr[i] = load_raw<RB>(vp + cc * EPL);
+        T* kd;
+        T* vd;
+        if (wb(s, kd, vd)) {
+          store_raw<RB>(kd + cc * EPL, kr[i]);
+          store_raw<RB>(vd + cc * EPL, vr[i]);
+        }
       }
     };
     // fill the ring, then consume block c from slot c % PF and refill it with block c + PF
@@ -331,8 +357,8 @@ struct AttnLaneMfma {
     uint32_t ok;           // bit r: row r of the block is visible
   };
 
-  template <typename RowFn>
-  __device__ __forceinline__ void fetch(int R0, int blkid, Buf& b, RowFn row) {
+  template <typename RowFn, typename WbFn>
+  __device__ __forceinline__ void fetch(int R0, int blkid, Buf& b, RowFn row, WbFn& wb) {
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane >> 4;
     const int cc = lane & 15;
@@ -345,6 +371,12 @@ struct AttnLaneMfma {
       const bool ok = row(s0 + 4 * g + i, kp, vp);
       b.k[i] = load_raw<RB>(kp + cc * EPL);
       b.v[i] = load_raw<RB>(vp + cc * EPL);
+      bf16* kd;
+      bf16* vd;
+      if (wb(s0 + 4 * g + i, kd, vd)) {
+        store_raw<RB>(kd + cc * EPL, b.k[i]);
+        store_raw<RB>(vd + cc * EPL, b.v[i]);
+      }
       // row 4g+i is visible iff lane 16g saw ok
       const uint64_t m = __ballot(ok);
 #pragma unroll
@@ -372,8 +404,9 @@ struct AttnLaneMfma {
 
   // Blocks blk = first, first + step, ... < end, in rounds of PF (even): the
   // loads of a round's blocks are all issued before its first pair is computed.
-  template <int PF = 2, typename RowFn>
-  __device__ __forceinline__ void run(int R0, int first, int end, int step, float scale_log2, RowFn row) {
+  template <int PF = 2, typename RowFn, typename WbFn = NoWriteBack>
+  __device__ __forceinline__ void run(int R0, int first, int end, int step, float scale_log2, RowFn row,
+                                      WbFn wb = WbFn{}) {
     static_assert(PF % 2 == 0, "blocks are computed in pairs");
     // blocks of this wave (wave-uniform, so that the block loop branches on the scalar unit)
     const int n = __builtin_amdgcn_readfirstlane(first < end ? (end - first + step - 1) / step : 0);
@@ -393,7 +426,7 @@ struct AttnLaneMfma {
     auto load = [&](int c0, Buf (&buf)[PF]) {
 #pragma unroll
       for (int p = 0; p < PF; ++p)
-        if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row);
+        if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row, wb);
     };
     for (int c0 = 0; c0 < n; c0 += PF) {
       Buf buf[PF];

@@ -76,7 +76,11 @@ struct AttendArgs {
   float* partials;        // ws
   uint32_t* counters;     // ws [B*Hkv*nq]
   const int32_t* stage_slot;  // nullable [B*Hkv, top_g]: routed entry -> slot of K_stage/V_stage
+                              // (>= 0 cached; -2 - slot: missing, read from K_host/V_host and
+                              // written into that slot; -1 ignored)
   int32_t stage_slots;        // slots per (b, kv head) of K_stage/V_stage when stage_slot is set
+  const void* K_host;         // nullable: pinned host [B, Hkv, n_cap, d] (warm tier misses)
+  const void* V_host;
   void* V16;                  // ws, pipelined prefill only: V as fp16 blocks of 16 keys [B*Hkv, n_cap, d]
 };
 
@@ -160,9 +164,8 @@ struct WarmArgs {
   int32_t* clock;            // [B*Hkv] steps taken
   int32_t* hits;             // nullable [B*Hkv]
   int32_t* misses;           // nullable [B*Hkv]
-  int32_t* slot_of;          // ws [B*Hkv, top_g]: slot of each list entry, -1 ignored
-  int32_t* miss_list;        // ws [B*Hkv, top_g, 2]: (slot, group) to copy in
-  int32_t* miss_count;       // ws [B*Hkv]
+  int32_t* slot_of;          // ws [B*Hkv, top_g]: slot of each list entry (>= 0 cached, -2 - slot
+                             // missing: copied in by the attention), -1 ignored
   int32_t slots;
   int32_t elem_bytes;
 };
@@ -189,7 +192,6 @@ hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipSt
 hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
 hipError_t launch_warm_lookup(const WarmArgs& a, hipStream_t st);
-hipError_t launch_warm_fill(const WarmArgs& a, hipStream_t st);
 // Decode routing launch (Hq/Hkv <= 4, d in {64, 128}, candidate and index limits).
 constexpr int kXcds = 8;             // accelerator dies; workgroups are dealt to them in turn
 constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per unit

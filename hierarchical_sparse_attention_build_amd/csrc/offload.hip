@@ -167,11 +167,9 @@ __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
       if (miss) {
         const int j = base + bits_below(m);
         const int v = victim[j];
-        slot[i] = v;
+        slot[i] = -2 - v;  // missing: the attention reads host memory and fills slot v
         tags[v] = entry[i];
         stamps[v] = now;
-        a.miss_list[(bh * TG + j) * 2] = v;
-        a.miss_list[(bh * TG + j) * 2 + 1] = entry[i];
       }
       base += __popcll(m);
     }
@@ -184,48 +182,8 @@ __global__ __launch_bounds__(kWarmThreads) void warm_lookup_kernel(WarmArgs a) {
   for (int i = tid; i < TG; i += kWarmThreads) a.slot_of[bh * TG + i] = slot[i];
   if (tid == 0) {
     a.clock[bh] = now;
-    a.miss_count[bh] = n_miss;
     if (a.hits) a.hits[bh] = n_hit;
     if (a.misses) a.misses[bh] = n_miss;
-  }
-}
-
-// Copy the missing groups' rows from host memory into their slots.
-// One workgroup per missing group (the j-th of its (b, kv head)): a step
-// usually misses a few groups, each read over the host link in one round of
-// 16-byte loads (every thread's loads issued before its stores).
-__global__ __launch_bounds__(kGatherThreads) void warm_fill_kernel(WarmArgs a) {
-  const KParams& kp = a.kp;
-  const int64_t bh = blockIdx.y;
-  const int j = blockIdx.x;
-  if (j >= a.miss_count[bh]) return;
-  const int v = a.miss_list[(bh * kp.top_g + j) * 2];
-  const int g = a.miss_list[(bh * kp.top_g + j) * 2 + 1];
-  const int64_t vec_per_group = static_cast<int64_t>(kp.G) * kp.d * a.elem_bytes / 16;
-  const int64_t vec_per_row = static_cast<int64_t>(kp.d) * a.elem_bytes / 16;
-  const uint4* Kh = static_cast<const uint4*>(a.K_host) + (bh * kp.n_cap + static_cast<int64_t>(g) * kp.G) * vec_per_row;
-  const uint4* Vh = static_cast<const uint4*>(a.V_host) + (bh * kp.n_cap + static_cast<int64_t>(g) * kp.G) * vec_per_row;
-  uint4* Kw = static_cast<uint4*>(a.K) + (bh * a.slots + v) * vec_per_group;
-  uint4* Vw = static_cast<uint4*>(a.V) + (bh * a.slots + v) * vec_per_group;
-  constexpr int kU = 4;  // vectors per thread in flight at once
-  for (int64_t e0 = threadIdx.x; e0 < vec_per_group; e0 += kU * kGatherThreads) {
-    uint4 kv[kU], vv[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t e = e0 + u * kGatherThreads;
-      if (e < vec_per_group) {
-        kv[u] = Kh[e];
-        vv[u] = Vh[e];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t e = e0 + u * kGatherThreads;
-      if (e < vec_per_group) {
-        Kw[e] = kv[u];
-        Vw[e] = vv[u];
-      }
-    }
   }
 }
 
@@ -233,13 +191,6 @@ hipError_t launch_warm_lookup(const WarmArgs& a, hipStream_t st) {
   if (a.kp.top_g <= 0) return hipSuccess;
   if (a.slots < a.kp.top_g || a.slots > kWarmMaxSlots || a.kp.top_g > kWarmMaxList) return hipErrorInvalidValue;
   warm_lookup_kernel<<<a.kp.B * a.kp.Hkv, kWarmThreads, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_warm_fill(const WarmArgs& a, hipStream_t st) {
-  if (a.kp.top_g <= 0) return hipSuccess;
-  dim3 grid(a.kp.top_g, a.kp.B * a.kp.Hkv);
-  warm_fill_kernel<<<grid, kGatherThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -258,14 +258,14 @@ typedef struct hga_warm {
  * renewed); the missing groups take the least recently used slots that this
  * step does not use (smallest stamp first, the lower slot on equal stamps; the
  * j-th missing group in list order gets the j-th of those slots in slot
- * order).  Only the missing groups are copied from host memory, one
- * workgroup per group, and attention reads the routed rows from their slots.
- * Everything runs on `stream`: a step misses few groups, and a hand-off to a
- * second stream and back costs more than the overlap would gain, so
- * `copy_stream` is not used (it may be null) and no event is created.  The
- * output equals hga_decode_offload's bit for bit (the attention splits its
- * work and merges the parts the same way).  Steps that share one `warm` must
- * be ordered (same stream or events). */
+ * order).  Attention reads the cached groups' rows from their slots and the
+ * missing groups' rows from host memory, and writes the latter into the
+ * slots the lookup chose, so only the missing groups cross the host link and
+ * their copy overlaps the attention of the cached ones.  Everything runs on
+ * `stream`: `copy_stream` is not used (it may be null) and no event is
+ * created.  The output equals hga_decode_offload's bit for bit (the
+ * attention splits its work and merges the parts the same way).  Steps that
+ * share one `warm` must be ordered (same stream or events). */
 hga_status hga_decode_offload_warm(const hga_params* p, const void* Q, const void* K_host,
                                    const void* V_host, const void* K_hot, const void* V_hot,
                                    int64_t n_cap, const int32_t* seq_len, float* chunk_sum,
