@@ -932,25 +932,18 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
   ra.ksrc.ring = 1;
   ra.chunk_sum_w = chunk_sum;
   ra.group_sum_w = group_sum;
-  HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
-  WarmArgs wa{};
+  int32_t* slot_of = warm ? at<int32_t>(ws, f.warm.slot_off) : nullptr;
   if (warm) {
-    wa.kp = kp;
-    wa.group_idx = gi;
-    wa.K_host = K_host;
-    wa.V_host = V_host;
-    wa.K = warm->K;
-    wa.V = warm->V;
-    wa.tags = warm->tags;
-    wa.stamps = warm->stamps;
-    wa.clock = warm->clock;
-    wa.hits = warm->hits;
-    wa.misses = warm->misses;
-    wa.slot_of = at<int32_t>(ws, f.warm.slot_off);
-    wa.slots = warm->slots;
-    wa.elem_bytes = static_cast<int32_t>(elem_bytes(p));
-    HGA_TRY_HIP(launch_warm_lookup(wa, st), "warm lookup");
+    // the routing launch's last workgroup of each unit runs the unit's LRU lookup
+    ra.warm.tags = warm->tags;
+    ra.warm.stamps = warm->stamps;
+    ra.warm.clock = warm->clock;
+    ra.warm.hits = warm->hits;
+    ra.warm.misses = warm->misses;
+    ra.warm.slot_of = slot_of;
+    ra.warm.slots = warm->slots;
   }
+  HGA_TRY_HIP(launch_route_scan(ra, bf, bf, st), "route");
   AttendArgs aa = attend_args(kp, f, ws, Q, 1, seq_len, -1, K_hot, V_hot, gi, 1, O, nullptr,
                               p->out_dtype == HGA_BF16);
   aa.kv.base = K_hot;
@@ -965,7 +958,7 @@ hga_status decode_offload_impl(const hga_params* p, const void* Q, const void* K
     // cached groups and needs no second stream.  Both parts of the attention
     // go in one grid with the block ranges and merge order of the two
     // launches below.
-    aa.stage_slot = wa.slot_of;
+    aa.stage_slot = slot_of;
     aa.stage_slots = warm->slots;
     aa.K_host = K_host;
     aa.V_host = V_host;

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "hga_kparams.hpp"
+#include "hga_warm_state.hpp"
 
 namespace hga {
 
@@ -48,6 +49,8 @@ struct RouteArgs {
   RowSource ksrc;
   float* chunk_sum_w;
   float* group_sum_w;
+  // warm tier (decode, nullable tags): the unit's LRU lookup after its lists
+  WarmState warm;
 };
 
 struct AttendArgs {
@@ -151,27 +154,6 @@ bool backward_mfma_supported(const KParams& kp, bool bf16_in);
 int backward_vis_words(int n_units);
 hipError_t launch_backward_mfma(const BackwardArgs& a, hipStream_t st);
 
-// Warm tier: per (b, kv head) a bounded LRU of routed groups in device memory.
-struct WarmArgs {
-  KParams kp;
-  const int32_t* group_idx;  // [B*Hkv, top_g] this step's routed groups
-  const void* K_host;        // pinned host [B, Hkv, n_cap, d]
-  const void* V_host;
-  void* K;                   // [B*Hkv, slots, G, d] cached rows
-  void* V;
-  int32_t* tags;             // [B*Hkv, slots] group of each slot, -1 empty
-  int32_t* stamps;           // [B*Hkv, slots] last step that used each slot
-  int32_t* clock;            // [B*Hkv] steps taken
-  int32_t* hits;             // nullable [B*Hkv]
-  int32_t* misses;           // nullable [B*Hkv]
-  int32_t* slot_of;          // ws [B*Hkv, top_g]: slot of each list entry (>= 0 cached, -2 - slot
-                             // missing: copied in by the attention), -1 ignored
-  int32_t slots;
-  int32_t elem_bytes;
-};
-constexpr int kWarmMaxSlots = 1024;
-constexpr int kWarmMaxList = 256;   // top_g limit with the warm tier
-
 // Canonical form of a caller-given group list: entries that add no token to
 // the visible set (repeats, groups of forced chunks, after the query chunk or
 // outside the cache) become -1.
@@ -191,7 +173,6 @@ hipError_t launch_summaries(const SummariesArgs& a, bool bf16_in, hipStream_t st
 hipError_t launch_route_scan(const RouteArgs& a, bool bf16_q, bool bf16_k, hipStream_t st);
 hipError_t launch_attend_splitk(const AttendArgs& a, bool bf16_in, hipStream_t st);
 hipError_t launch_gather_groups(const GatherArgs& a, hipStream_t st);
-hipError_t launch_warm_lookup(const WarmArgs& a, hipStream_t st);
 // Decode routing launch (Hq/Hkv <= 4, d in {64, 128}, candidate and index limits).
 constexpr int kXcds = 8;             // accelerator dies; workgroups are dealt to them in turn
 constexpr int kDecMaxScores = 4096;  // chunk (and group) scores held in LDS per unit

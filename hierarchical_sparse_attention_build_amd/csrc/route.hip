@@ -19,10 +19,14 @@
 // bandwidth in decode.
 //
 // In a decode step one extra workgroup per (b, kv head) summarises the chunk
-// that the query completes, so a decode loop keeps the tables current.
+// that the query completes, so a decode loop keeps the tables current.  With
+// the warm tier, the workgroup that finishes a unit's lists also runs the
+// unit's LRU lookup (hga_warm.hpp) on them, in LDS the selections no longer
+// use.
 #include "hga_kernels.hpp"
 #include "hga_select.hpp"
 #include "hga_summarize.hpp"
+#include "hga_warm.hpp"
 
 namespace hga {
 
@@ -138,7 +142,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   const bool prefill = a.nq > 1;
   const int j = t0 / kp.C + (prefill ? u : 0);
 
-  __shared__ RouteSmem sm;
+  __shared__ union {
+    RouteSmem r;
+    WarmSmem w;
+  } smu;
+  RouteSmem& sm = smu.r;
+  __shared__ int wlist[kWarmMaxList];  // the unit's group list for the warm lookup
+  const int n_groups_cap = static_cast<int>(kp.n_cap / kp.G);
 
   // positions outside the cache (or a prefill block not aligned to C): the unit
   // gets empty index lists and nothing else happens
@@ -148,6 +158,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
       const int64_t unit = static_cast<int64_t>(bh) * a.n_units + u;
       for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads) a.chunk_idx[unit * kp.top_k + i] = -1;
       for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) a.group_idx[unit * kp.top_g + i] = -1;
+      if (a.warm.tags) {  // the step still counts
+        for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) wlist[i] = -1;
+        __syncthreads();
+        warm_lookup_unit<kRouteThreads>(a.warm, unit, kp.top_g, n_groups_cap, wlist, smu.w);
+      }
     }
     return;
   }
@@ -278,6 +293,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
       v = sm.sel_chunks[sg / m] * m + sg % m;
     }
     gi[i] = v;
+    if (a.warm.tags) wlist[i] = v;
+  }
+  if (a.warm.tags) {
+    __syncthreads();  // the selections' LDS is free from here on
+    warm_lookup_unit<kRouteThreads>(a.warm, unit, kp.top_g, n_groups_cap, wlist, smu.w);
   }
 }
 
