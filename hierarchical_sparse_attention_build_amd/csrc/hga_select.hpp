@@ -32,13 +32,58 @@ __device__ __forceinline__ int bits_below(uint64_t m) {
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
+// OR and AND of v over the whole wave (every lane gets both)
+__device__ __forceinline__ void wave_or_and(uint32_t& o, uint32_t& a) {
+  using namespace dpp;
+  o |= static_cast<uint32_t>(movi<kRowRor8>(static_cast<int>(o)));
+  a &= static_cast<uint32_t>(movi<kRowRor8>(static_cast<int>(a)));
+  o |= static_cast<uint32_t>(movi<kRowRor4>(static_cast<int>(o)));
+  a &= static_cast<uint32_t>(movi<kRowRor4>(static_cast<int>(a)));
+  o |= static_cast<uint32_t>(movi<kQuad2301>(static_cast<int>(o)));
+  a &= static_cast<uint32_t>(movi<kQuad2301>(static_cast<int>(a)));
+  o |= static_cast<uint32_t>(movi<kQuad1032>(static_cast<int>(o)));
+  a &= static_cast<uint32_t>(movi<kQuad1032>(static_cast<int>(a)));
+  auto r = __builtin_amdgcn_permlane16_swap(o, o, false, false);
+  o = r[0] | r[1];
+  r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  a = r[0] & r[1];
+  r = __builtin_amdgcn_permlane32_swap(o, o, false, false);
+  o = r[0] | r[1];
+  r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  a = r[0] & r[1];
+}
+
 // Valid keys are order_key() values (always >= 0x007fffff); an empty slot holds 0.
 // Returns the largest T with #{keys >= T} >= k, for 1 <= k <= number of valid keys
 // (the k-th largest key, or a value with exactly k keys at or above it).
-template <int E>
+//
+// With Prefix set, the search starts below the keys' common prefix: the bits
+// above the highest bit in which two valid keys differ are the same in every
+// valid key, and a greedy search from bit 31 would set exactly those of them
+// that the keys have (each such step counts every valid key, or none).  The
+// selection that follows (keys > T, then ties) is the same as the full
+// search's.  It pays for keys that share many top bits (small integers under
+// a complement); scores of mixed sign differ in bit 31 already.
+template <int E, bool Prefix = false>
 __device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&key)[E], int k) {
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  uint32_t T = 0u;
+  int top = 31;
+  if constexpr (Prefix) {
+    uint32_t o = 0u, a = ~0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      o |= key[e];
+      a &= key[e] != 0u ? key[e] : ~0u;
+    }
+    wave_or_and(o, a);
+    o = __builtin_amdgcn_readfirstlane(o);
+    a = __builtin_amdgcn_readfirstlane(a);
+    const uint32_t diff = o ^ a;  // no valid key holds a bit that the AND lacks above this
+    if (diff == 0u) return a;     // every valid key is equal
+    top = 31 - __builtin_clz(diff);
+    T = top == 31 ? 0u : (a & ~((2u << top) - 1u));
+  }
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
 #pragma unroll
@@ -88,7 +133,7 @@ __device__ __forceinline__ void wave_emit_all(const uint32_t (&key)[E], OutFn ou
 
 // One wave: keys key_of(e) for slots (e, lane), e < E; emit the best k
 // (every valid key when all is set) through out(rank, e, key).
-template <int E, typename KeyFn, typename OutFn>
+template <int E, bool Prefix = false, typename KeyFn, typename OutFn>
 __device__ __forceinline__ void wave_topk(KeyFn key_of, int k, bool all, OutFn out) {
   uint32_t key[E];
 #pragma unroll
@@ -96,7 +141,7 @@ __device__ __forceinline__ void wave_topk(KeyFn key_of, int k, bool all, OutFn o
   if (all) {
     wave_emit_all(key, out);
   } else if (k > 0) {
-    const uint32_t T = wave_kth_key(key, k);
+    const uint32_t T = wave_kth_key<E, Prefix>(key, k);
     wave_emit(key, k, T, out);
   }
 }
@@ -106,20 +151,20 @@ __device__ __forceinline__ void wave_topk(KeyFn key_of, int k, bool all, OutFn o
 // MaxE are compiled: a kernel that inlines the 8- and 16-slot ones needs more
 // scalar registers at its peak, and the excess spills to vector lanes with
 // reloads all over the kernel.
-template <int MaxE, typename KeyFn, typename OutFn>
+template <int MaxE, bool Prefix = false, typename KeyFn, typename OutFn>
 __device__ __forceinline__ void wave_topk_n(int slots, KeyFn key_of, int k, bool all, OutFn out) {
   static_assert(MaxE >= 2 && MaxE <= kSelMaxE && (MaxE & (MaxE - 1)) == 0, "MaxE: 2, 4, 8 or 16");
   if (slots <= 0) return;
   if (slots <= 1) {
-    wave_topk<1>(key_of, k, all, out);
+    wave_topk<1, Prefix>(key_of, k, all, out);
   } else if (MaxE == 2 || slots <= 2) {
-    wave_topk<2>(key_of, k, all, out);
+    wave_topk<2, Prefix>(key_of, k, all, out);
   } else if constexpr (MaxE >= 4) {
     if (MaxE == 4 || slots <= 4) {
-      wave_topk<4>(key_of, k, all, out);
+      wave_topk<4, Prefix>(key_of, k, all, out);
     } else if constexpr (MaxE >= 8) {
-      if (MaxE == 8 || slots <= 8) wave_topk<8>(key_of, k, all, out);
-      else wave_topk<kSelMaxE>(key_of, k, all, out);
+      if (MaxE == 8 || slots <= 8) wave_topk<8, Prefix>(key_of, k, all, out);
+      else wave_topk<kSelMaxE, Prefix>(key_of, k, all, out);
     }
   }
 }

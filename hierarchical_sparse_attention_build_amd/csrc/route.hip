@@ -21,32 +21,44 @@
 // In a decode step one extra workgroup per (b, kv head) summarises the chunk
 // that the query completes, so a decode loop keeps the tables current.  With
 // the warm tier, the workgroup that finishes a unit's lists also runs the
-// unit's LRU lookup (hga_warm.hpp) on them, in LDS the selections no longer
-// use.
+// unit's LRU lookup (hga_warm.hpp) on them.
 #include "hga_kernels.hpp"
 #include "hga_select.hpp"
 #include "hga_summarize.hpp"
 #include "hga_warm.hpp"
 
+#include <type_traits>
+
 namespace hga {
 
-constexpr int kRouteThreads = 256;
-constexpr int kRouteWaves = kRouteThreads / kWave;
-constexpr int kRowLanes = 8;                                    // lanes per summary row
-constexpr int kRowsPerRound = kRouteWaves * kWave / kRowLanes;  // 32 rows per block round
-constexpr int kRounds = 4;                                      // rounds in flight per lane
-constexpr int kQB = 4;                                          // query vectors per register batch
-constexpr int kSliceRows = kRowsPerRound * kRounds;             // candidate chunks per workgroup
-constexpr int kLdsCand = 2048;                                  // candidates staged in LDS for the selections
-constexpr int kRouteQs = 16 * 128;                              // query elements staged in LDS (one query per sequence)
+// Workgroup shapes: NT threads, eight lanes per summary row, kRounds rows in
+// flight per lane.  Prefill units use 256 threads; a decode unit uses 512, so
+// a unit has half as many slices and slice winners, and the last workgroup
+// scores the group rows of the routed chunks in one round of loads.
+constexpr int kRouteThreads = 256;     // prefill
+constexpr int kRouteDecThreads = 512;  // decode (one query per sequence)
+constexpr int kRowLanes = 8;           // lanes per summary row
+constexpr int kRounds = 4;             // rounds in flight per lane
+template <int NT>
+struct RouteShape {
+  static constexpr int kRowsPerRound = NT / kRowLanes;            // rows per block round
+  static constexpr int kSliceRows = kRowsPerRound * kRounds;      // candidate chunks per workgroup
+  // query vectors per register batch; the wide shape holds fewer, so that it
+  // stays within 128 registers and two workgroups fit on a CU
+  static constexpr int kQB = NT > 256 ? 2 : 4;
+  static constexpr int kWavesPerSimd = NT > 256 ? 4 : 1;          // occupancy asked of the compiler
+};
+constexpr int kLdsCand = 2048;         // candidates staged in LDS for the selections
+constexpr int kRouteQs = 16 * 128;     // query elements staged in LDS (one query per sequence)
 
+template <int NT>
 struct RouteSmem {
   union {  // scratch of the selection in use
-    TopkSmem<kRouteThreads> topk;
-    SelSmem<kRouteThreads> sel;
+    TopkSmem<NT> topk;
+    SelSmem<NT> sel;
   };
-  float loc[kSliceRows];
-  int loc_sel[kSliceRows];
+  float loc[RouteShape<NT>::kSliceRows];
+  int loc_sel[RouteShape<NT>::kSliceRows];
   int sel_chunks[1024];
   int sel_groups[1024];
   float cand_s[kLdsCand];
@@ -66,7 +78,7 @@ __device__ __forceinline__ int slice_count(int x, int nM, int cps, int k) {
 // [0, n); only lanes with lane % 8 == 0 call put.  row(i) is a float32 row.
 // The query vectors come from qs (LDS, fp32, vector v at qs + v * D) when it
 // is set, else from global memory at qbase.
-template <typename T, int D, typename RowFn, typename PutFn>
+template <typename T, int D, int NT, typename RowFn, typename PutFn>
 __device__ __forceinline__ void score_rows(const T* __restrict__ qbase, int64_t head_stride,
                                            int rows_per_head, int nqv, const float* qs, const KParams& kp,
                                            int n, RowFn row, PutFn put) {
@@ -75,6 +87,8 @@ __device__ __forceinline__ void score_rows(const T* __restrict__ qbase, int64_t 
   const int wid = threadIdx.x / kWave;
   const int piece = lane % kRowLanes;
   const int rw = wid * (kWave / kRowLanes) + lane / kRowLanes;  // row within a round
+  constexpr int kRowsPerRound = RouteShape<NT>::kRowsPerRound;
+  constexpr int kQB = RouteShape<NT>::kQB;
   for (int base = 0; base < n; base += kRowsPerRound * kRounds) {
     float4 s[kRounds][NV];
 #pragma unroll
@@ -130,8 +144,8 @@ __device__ __forceinline__ void score_rows(const T* __restrict__ qbase, int64_t 
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) {
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT, RouteShape<NT>::kWavesPerSimd) void route_scan_kernel(RouteArgs a) {
   const KParams& kp = a.kp;
   const int bh = blockIdx.z;
   const int u = blockIdx.y;
@@ -142,12 +156,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   const bool prefill = a.nq > 1;
   const int j = t0 / kp.C + (prefill ? u : 0);
 
-  __shared__ union {
-    RouteSmem r;
-    WarmSmem w;
-  } smu;
-  RouteSmem& sm = smu.r;
-  __shared__ int wlist[kWarmMaxList];  // the unit's group list for the warm lookup
+  __shared__ RouteSmem<NT> sm;
+  // the warm tier's stage (decode shape only; a prefill launch never has it)
+  constexpr bool kWarm = NT == kRouteDecThreads;
+  __shared__ std::conditional_t<kWarm, WarmStage, char> wst;
   const int n_groups_cap = static_cast<int>(kp.n_cap / kp.G);
 
   // positions outside the cache (or a prefill block not aligned to C): the unit
@@ -156,12 +168,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   if (t0 < 0 || t_last >= kp.n_cap || (prefill && t0 % kp.C != 0)) {
     if (x == 0) {
       const int64_t unit = static_cast<int64_t>(bh) * a.n_units + u;
-      for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads) a.chunk_idx[unit * kp.top_k + i] = -1;
-      for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) a.group_idx[unit * kp.top_g + i] = -1;
-      if (a.warm.tags) {  // the step still counts
-        for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) wlist[i] = -1;
-        __syncthreads();
-        warm_lookup_unit<kRouteThreads>(a.warm, unit, kp.top_g, n_groups_cap, wlist, smu.w);
+      for (int i = threadIdx.x; i < kp.top_k; i += NT) a.chunk_idx[unit * kp.top_k + i] = -1;
+      for (int i = threadIdx.x; i < kp.top_g; i += NT) a.group_idx[unit * kp.top_g + i] = -1;
+      if constexpr (kWarm) {
+        if (a.warm.tags) {  // the step still counts
+          warm_stage_load<NT>(a.warm, unit, wst);
+          for (int i = threadIdx.x; i < kp.top_g; i += NT) wst.list[i] = -1;
+          __syncthreads();
+          warm_lookup_unit<NT>(a.warm, unit, kp.top_g, n_groups_cap, wst);
+        }
       }
     }
     return;
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   // global loads of each vector for every batch of rows in both scans
   const float* qs = !prefill && nqv * D <= kRouteQs ? sm.qs : nullptr;
   if (qs)
-    for (int e = threadIdx.x; e < nqv * D; e += kRouteThreads) sm.qs[e] = elem<T>::get(qbase, e);
+    for (int e = threadIdx.x; e < nqv * D; e += NT) sm.qs[e] = elem<T>::get(qbase, e);
   __syncthreads();
 
   float* cand_s = a.scores + unit * kp.n_chunks_cap;   // published (score, chunk) pairs
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   const float* ctab = a.chunk_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * D;
   float* sc_out = a.scores_out ? a.scores_out + static_cast<int64_t>(bh) * kp.n_chunks_cap : nullptr;
   if (n_here > 0) {
-    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, qs, kp, n_here,
+    score_rows<T, D, NT>(qbase, head_stride, rows_per_head, nqv, qs, kp, n_here,
                      [&](int i) { return ctab + static_cast<int64_t>(c_lo + i) * D; },
                      [&](int i, float v) {
                        sm.loc[i] = v;
@@ -220,14 +235,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
     const int kk = slice_count(x, nM, a.chunks_per_slice, kp.top_k);
     if (kk > 0) {
       if (kk < n_here) {
-        block_select<kRouteThreads>([&](int i) { return sm.loc[i]; }, n_here, kk, sm.loc_sel, sm.sel);
-        for (int r = threadIdx.x; r < kk; r += kRouteThreads) {
+        block_select<NT>([&](int i) { return sm.loc[i]; }, n_here, kk, sm.loc_sel, sm.sel);
+        for (int r = threadIdx.x; r < kk; r += NT) {
           const int i = sm.loc_sel[r];
           st_agent(cand_s + off + r, sm.loc[i]);
           st_agent(cand_i + off + r, c_lo + i);
         }
       } else {
-        for (int r = threadIdx.x; r < kk; r += kRouteThreads) {
+        for (int r = threadIdx.x; r < kk; r += NT) {
           st_agent(cand_s + off + r, sm.loc[r]);
           st_agent(cand_i + off + r, c_lo + r);
         }
@@ -238,11 +253,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   // ---- last workgroup of the unit does the selections
   if (!arrive_last(&a.counters[unit], static_cast<uint32_t>(a.slices), &sm.is_last)) return;
 
+  // the warm slots' loads share the round trip of the winners' loads
+  if constexpr (kWarm) {
+    if (a.warm.tags) warm_stage_load<NT>(a.warm, unit, wst);
+  }
   int n_c = 0;
   for (int xx = 0; xx < a.slices; ++xx) n_c += slice_count(xx, nM, a.chunks_per_slice, kp.top_k);
   const bool in_lds = n_c <= kLdsCand;
   if (in_lds) {
-    for (int i = threadIdx.x; i < n_c; i += kRouteThreads) {
+    for (int i = threadIdx.x; i < n_c; i += NT) {
       sm.cand_s[i] = cand_s[i];
       sm.cand_i[i] = cand_i[i];
     }
@@ -250,28 +269,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   __syncthreads();
   // candidates are in ascending chunk order, so position order breaks ties
   int cnt;
-  if (in_lds && block_select_fits<kRouteThreads>(n_c, kp.top_k)) {
-    cnt = block_select<kRouteThreads>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.sel);
+  if (in_lds && block_select_fits<NT>(n_c, kp.top_k)) {
+    cnt = block_select<NT>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.sel);
   } else if (in_lds) {
-    cnt = block_topk<kRouteThreads>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
+    cnt = block_topk<NT>([&](int i) { return sm.cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
   } else {
-    cnt = block_topk<kRouteThreads>([&](int i) { return cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
+    cnt = block_topk<NT>([&](int i) { return cand_s[i]; }, n_c, kp.top_k, sm.sel_chunks, sm.topk);
   }
   // selected positions -> chunk ids (ascending)
-  for (int i = threadIdx.x; i < cnt; i += kRouteThreads) {
+  for (int i = threadIdx.x; i < cnt; i += NT) {
     const int pos = sm.sel_chunks[i];
     sm.sel_chunks[i] = in_lds ? sm.cand_i[pos] : cand_i[pos];
   }
   __syncthreads();
   int32_t* ci = a.chunk_idx + unit * kp.top_k;
-  for (int i = threadIdx.x; i < kp.top_k; i += kRouteThreads) ci[i] = i < cnt ? sm.sel_chunks[i] : -1;
+  for (int i = threadIdx.x; i < kp.top_k; i += NT) ci[i] = i < cnt ? sm.sel_chunks[i] : -1;
 
   const int nG = cnt * kp.m;
   const int m = kp.m;
   const float* gtab = a.group_sum + static_cast<int64_t>(bh) * kp.n_chunks_cap * kp.m * D;
   float* gsc = nG <= kLdsCand ? sm.cand_s : a.gscores + unit * static_cast<int64_t>(kp.top_k) * kp.m;
   if (nG > 0) {
-    score_rows<T, D>(qbase, head_stride, rows_per_head, nqv, qs, kp, nG,
+    score_rows<T, D, NT>(qbase, head_stride, rows_per_head, nqv, qs, kp, nG,
                      [&](int i) {
                        const int64_t gid = static_cast<int64_t>(sm.sel_chunks[i / m]) * m + i % m;
                        return gtab + gid * D;
@@ -281,36 +300,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(RouteArgs a) 
   __threadfence_block();
   __syncthreads();
   int gcnt;
-  if (block_select_fits<kRouteThreads>(nG, kp.top_g))
-    gcnt = block_select<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.sel);
+  if (block_select_fits<NT>(nG, kp.top_g))
+    gcnt = block_select<NT>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.sel);
   else
-    gcnt = block_topk<kRouteThreads>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
+    gcnt = block_topk<NT>([&](int i) { return gsc[i]; }, nG, kp.top_g, sm.sel_groups, sm.topk);
   int32_t* gi = a.group_idx + unit * kp.top_g;
-  for (int i = threadIdx.x; i < kp.top_g; i += kRouteThreads) {
+  for (int i = threadIdx.x; i < kp.top_g; i += NT) {
     int32_t v = -1;
     if (i < gcnt) {
       const int sg = sm.sel_groups[i];
       v = sm.sel_chunks[sg / m] * m + sg % m;
     }
     gi[i] = v;
-    if (a.warm.tags) wlist[i] = v;
+    if constexpr (kWarm) {
+      if (a.warm.tags) wst.list[i] = v;
+    }
   }
-  if (a.warm.tags) {
-    __syncthreads();  // the selections' LDS is free from here on
-    warm_lookup_unit<kRouteThreads>(a.warm, unit, kp.top_g, n_groups_cap, wlist, smu.w);
+  if constexpr (kWarm) {
+    if (a.warm.tags) {
+      __syncthreads();
+      warm_lookup_unit<NT>(a.warm, unit, kp.top_g, n_groups_cap, wst);
+    }
   }
 }
 
 int route_chunks_per_slice(const KParams& kp, int64_t nq) {
   (void)kp;
-  (void)nq;
-  return kSliceRows;
+  return nq == 1 ? RouteShape<kRouteDecThreads>::kSliceRows : RouteShape<kRouteThreads>::kSliceRows;
 }
 
 template <typename T, int D>
 static hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
   dim3 grid(a.slices + (a.build_summary ? 1 : 0), a.n_units, a.kp.B * a.kp.Hkv);
-  route_scan_kernel<T, D><<<grid, kRouteThreads, 0, st>>>(a);
+  if (a.nq == 1)
+    route_scan_kernel<T, D, kRouteDecThreads><<<grid, kRouteDecThreads, 0, st>>>(a);
+  else
+    route_scan_kernel<T, D, kRouteThreads><<<grid, kRouteThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
