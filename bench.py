@@ -1,6 +1,7 @@
 """Benchmark of the HGA routed-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--no-secondary]
+                    [--offload-only]
 
 A step is one decode step of the 32K-context workload (B=8, 32 query / 8 KV
 heads, d=128, C=64, G=16, sink 1, local 4, top-k 16, top-g 32, bf16): the
@@ -156,6 +157,8 @@ def main():
                     help="skip the 64K decode and the 128K cold-tier decode figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy, a known-size reference for HBM counters")
+    ap.add_argument("--offload-only", action="store_true",
+                    help="only the 128K host-offload decode (cold and warm tiers), for a kernel trace of it")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -179,6 +182,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copies done")
+    if args.offload_only:
+        print(json.dumps({"offload_decode_128k": bench_offload(args, dev)}), flush=True)
+        return
 
     s = W.spec("decode_32k")
     log(f"[bench] generating {s.name} (seed {s.seed})")
