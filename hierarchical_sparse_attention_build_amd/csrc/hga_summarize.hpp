@@ -117,13 +117,13 @@ __device__ void summarize_chunk(const T* __restrict__ Kc, int c, const KParams& 
 
 // ---------------------------------------------------------------------------
 // Fast path for bf16 post-RoPE keys (C <= 64, G a multiple of the rows that
-// one 64-lane load covers): the same arithmetic as above, with 16-byte row
+// one 64-lane load covers): the same arithmetic as above, with 8-byte row
 // loads, one wave per group, and the rotation angles read from tables:
 //   rot[r * P + i]  = (cos, sin) of theta_i * (gcen - r)         for r < G,
 //   crot[g * P + i] = (cos, sin) of theta_i * (ccen - gcen_g)     for g < m,
-// the identity for high-frequency pairs.  The pair (x_i, x_{i+P}) of a row
-// sits in two lanes of the same row (one holds first halves, the other second
-// halves); each lane rotates its own half with the other's values.
+// the identity for high-frequency pairs.  A lane loads both halves of four
+// pairs of a row (dimensions 4 q .. 4 q + 3 and the same plus P, two 8-byte
+// loads), so it rotates them with no exchange between lanes.
 
 template <int D>
 __host__ __device__ constexpr int summarize_rows_per_load() { return kWave / (D / 8); }
@@ -161,13 +161,6 @@ __device__ void build_summary_tables(const KParams& kp, float2* rot, float2* cro
   __syncthreads();
 }
 
-// The value that the lane holding the other half of this lane's pairs has.
-template <int D>
-__device__ __forceinline__ float pair_partner(float v) {
-  if constexpr (D == 128) return dpp::movf<dpp::kRowRor8>(v);  // lane c <-> c ^ 8 of a row of 16
-  else return __shfl_xor(v, 4, kWave);                          // lane c <-> c ^ 4 of a group of 8
-}
-
 // Sum over the lanes that hold the same columns (different rows).
 template <int D>
 __device__ __forceinline__ float sum_row_lanes(float v) {
@@ -175,29 +168,37 @@ __device__ __forceinline__ float sum_row_lanes(float v) {
   return sum_rows(v);
 }
 
-// The rows of one group that this lane loads (16 bytes each), MAXL loads at
-// most (G <= MAXL rows per load).
+// The rows of one group that this lane loads, MAXL rows at most (G <= MAXL
+// rows per load): four values of the first half and the same four of the
+// second half of each row.
 template <int D, int MAXL>
 struct GroupRows {
-  uint4 w[MAXL];
+  uint2 lo[MAXL];
+  uint2 hi[MAXL];
 };
 
 template <int D, int MAXL>
 __device__ __forceinline__ void load_group_rows(const bf16* __restrict__ Kc, const KParams& kp, int g,
                                                 GroupRows<D, MAXL>& rows) {
-  constexpr int LR = D / 8;
+  constexpr int P = D / 2;
+  constexpr int LR = D / 8;  // lanes per row, four pairs each
   constexpr int RPI = summarize_rows_per_load<D>();
   const int lane = threadIdx.x & (kWave - 1);
-  const int cb = lane % LR, ro = lane / LR;
+  const int pc = lane % LR, ro = lane / LR;
   const int spg = kp.G / RPI;
 #pragma unroll
-  for (int s = 0; s < MAXL; ++s)
-    if (s < spg)
-      rows.w[s] = *reinterpret_cast<const uint4*>(Kc + static_cast<int64_t>(g * kp.G + s * RPI + ro) * D + cb * 8);
+  for (int s = 0; s < MAXL; ++s) {
+    if (s < spg) {
+      const bf16* r = Kc + static_cast<int64_t>(g * kp.G + s * RPI + ro) * D + 4 * pc;
+      rows.lo[s] = *reinterpret_cast<const uint2*>(r);
+      rows.hi[s] = *reinterpret_cast<const uint2*>(r + P);
+    }
+  }
 }
 
 // One wave: group g's mean from its loaded rows, into gs_out (global) and
-// gmean (LDS, [m][D]).
+// gmean (LDS, [m][D]).  Pair i = 4 pc + j of a row with offset r becomes
+// (a c - b s, a s + b c), (c, s) = rot[r * P + i].
 template <int D, int MAXL>
 __device__ __forceinline__ void group_mean_wave(const GroupRows<D, MAXL>& rows, const KParams& kp, const float2* rot,
                                                 int g, float* __restrict__ gs_out, float* gmean) {
@@ -205,40 +206,43 @@ __device__ __forceinline__ void group_mean_wave(const GroupRows<D, MAXL>& rows, 
   constexpr int LR = D / 8;
   constexpr int RPI = summarize_rows_per_load<D>();
   const int lane = threadIdx.x & (kWave - 1);
-  const int cb = lane % LR, ro = lane / LR;
-  const int i0 = (cb % (LR / 2)) * 8;                // first pair of this lane's 8 columns
-  const float sgn = cb >= LR / 2 ? 1.f : -1.f;       // second halves: +, first halves: -
+  const int pc = lane % LR, ro = lane / LR;
+  const int i0 = 4 * pc;
   const int spg = kp.G / RPI;
-  float acc[8];
+  float ra[4], rb[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int j = 0; j < 4; ++j) ra[j] = rb[j] = 0.f;
 #pragma unroll
   for (int s = 0; s < MAXL; ++s) {
     if (s < spg) {
-      const uint32_t ww[4] = {rows.w[s].x, rows.w[s].y, rows.w[s].z, rows.w[s].w};
       const float4* tr = reinterpret_cast<const float4*>(rot + (s * RPI + ro) * P + i0);
+      const float4 t01 = tr[0], t23 = tr[1];  // (c, s) of pairs i0 .. i0 + 3
+      const float a[4] = {bf16lo(rows.lo[s].x), bf16hi(rows.lo[s].x), bf16lo(rows.lo[s].y), bf16hi(rows.lo[s].y)};
+      const float b[4] = {bf16lo(rows.hi[s].x), bf16hi(rows.hi[s].x), bf16lo(rows.hi[s].y), bf16hi(rows.hi[s].y)};
+      const float c[4] = {t01.x, t01.z, t23.x, t23.z};
+      const float sn[4] = {t01.y, t01.w, t23.y, t23.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float x0 = bf16lo(ww[q]), x1 = bf16hi(ww[q]);
-        const float y0 = pair_partner<D>(x0), y1 = pair_partner<D>(x1);
-        const float4 t = tr[q];  // (cos, sin) of pairs i0 + 2q and i0 + 2q + 1
-        acc[2 * q] = fmaf(x0, t.x, fmaf(sgn * y0, t.y, acc[2 * q]));
-        acc[2 * q + 1] = fmaf(x1, t.z, fmaf(sgn * y1, t.w, acc[2 * q + 1]));
+      for (int j = 0; j < 4; ++j) {
+        ra[j] = fmaf(a[j], c[j], fmaf(-b[j], sn[j], ra[j]));
+        rb[j] = fmaf(b[j], c[j], fmaf(a[j], sn[j], rb[j]));
       }
     }
   }
   const float invG = 1.0f / static_cast<float>(kp.G);
-  float gm[8];
+  float ga[4], gb[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) gm[e] = sum_row_lanes<D>(acc[e]) * invG;
+  for (int j = 0; j < 4; ++j) {
+    ga[j] = sum_row_lanes<D>(ra[j]) * invG;
+    gb[j] = sum_row_lanes<D>(rb[j]) * invG;
+  }
   if (ro == 0) {
-    const float4 v0 = make_float4(gm[0], gm[1], gm[2], gm[3]), v1 = make_float4(gm[4], gm[5], gm[6], gm[7]);
-    float4* go = reinterpret_cast<float4*>(gs_out + static_cast<int64_t>(g) * D + cb * 8);
-    go[0] = v0;
-    go[1] = v1;
-    float4* gl = reinterpret_cast<float4*>(gmean + g * D + cb * 8);
-    gl[0] = v0;
-    gl[1] = v1;
+    const float4 va = make_float4(ga[0], ga[1], ga[2], ga[3]), vb = make_float4(gb[0], gb[1], gb[2], gb[3]);
+    float* go = gs_out + static_cast<int64_t>(g) * D + i0;
+    *reinterpret_cast<float4*>(go) = va;
+    *reinterpret_cast<float4*>(go + P) = vb;
+    float* gl = gmean + g * D + i0;
+    *reinterpret_cast<float4*>(gl) = va;
+    *reinterpret_cast<float4*>(gl + P) = vb;
   }
 }
 

@@ -1,6 +1,7 @@
 // Step 1 of HGA: RoPE-aware chunk and group key summaries.
 // [HGA technical summary (it), Meccanismo Core, item 3].  bf16 post-RoPE keys
-// with C <= 64: 16-byte row loads and one wave per group; otherwise the generic
+// with C <= 64: 8-byte row loads (both halves of each pair) and one wave per
+// group; otherwise the generic
 // routine.  One workgroup per chunk of one (b, kv head).  See hga_summarize.hpp.
 #include "hga_kernels.hpp"
 #include "hga_summarize.hpp"
