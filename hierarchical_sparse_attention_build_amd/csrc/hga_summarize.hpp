@@ -139,24 +139,32 @@ __host__ __device__ inline bool summarize_fast_ok(const KParams& kp, bool bf16_i
          summarize_lds_floats(kp) <= lds_floats;
 }
 
-// All threads of the workgroup build the tables (ends with a barrier).
+// All threads of the workgroup build the tables (ends with a barrier).  The
+// offsets are symmetric: gcen - r and gcen - (G - 1 - r) are exact negatives
+// (small multiples of 1/2), and so are the chunk offsets of groups g and
+// m - 1 - g, so one sincos serves both entries (the sine changes sign).
 template <int D>
 __device__ void build_summary_tables(const KParams& kp, float2* rot, float2* crot) {
   constexpr int P = D / 2;
   const float gcen = 0.5f * static_cast<float>(kp.G - 1);
   const float ccen = 0.5f * static_cast<float>(kp.C - 1);
-  for (int x = threadIdx.x; x < kp.G * P; x += blockDim.x) {
+  const int hr = (kp.G + 1) / 2, hg = (kp.m + 1) / 2;
+  for (int x = threadIdx.x; x < hr * P; x += blockDim.x) {
     const int r = x / P, i = x % P;
     float sn = 0.f, cn = 1.f;
     if (!((kp.hf_mask >> i) & 1ull)) sincosf(kp.theta_f[i] * (gcen - static_cast<float>(r)), &sn, &cn);
-    rot[x] = make_float2(cn, sn);
+    rot[r * P + i] = make_float2(cn, sn);
+    const int rm = kp.G - 1 - r;
+    if (rm != r) rot[rm * P + i] = make_float2(cn, -sn);
   }
-  for (int x = threadIdx.x; x < kp.m * P; x += blockDim.x) {
+  for (int x = threadIdx.x; x < hg * P; x += blockDim.x) {
     const int g = x / P, i = x % P;
     float sn = 0.f, cn = 1.f;
     if (!((kp.hf_mask >> i) & 1ull))
       sincosf(kp.theta_f[i] * (ccen - (static_cast<float>(g * kp.G) + gcen)), &sn, &cn);
-    crot[x] = make_float2(cn, sn);
+    crot[g * P + i] = make_float2(cn, sn);
+    const int gm = kp.m - 1 - g;
+    if (gm != g) crot[gm * P + i] = make_float2(cn, -sn);
   }
   __syncthreads();
 }
