@@ -66,13 +66,16 @@ def measured_traffic(kernel):
     or None when no summary was taken on the current sources."""
     d = os.path.join(ROOT, "profiles")
     fp = source_fingerprint()
+    want = kernel.replace(" ", "")
     for f in sorted(os.listdir(d)):
         with open(os.path.join(d, f)) as fh:
             for line in fh:
+                # kernel names may hold spaces ("k<bf16, 128, 4>"): read the
+                # fields from the right
                 t = line.strip().strip("`").split()
-                if len(t) == 5 and t[0] == "traffic" and t[1] == kernel and t[3] == "sources":
-                    if t[4] == fp:
-                        return int(t[2])
+                if len(t) >= 5 and t[0] == "traffic" and t[-2] == "sources":
+                    if "".join(t[1:-3]) == want and t[-1] == fp:
+                        return int(t[-3])
     return None
 
 
@@ -375,9 +378,11 @@ def bench_prefill(args, dev):
             "route": {"kernel": "route_prefill_mfma_kernel<128,8>", "avg_us": round(t_route, 2),
                       "includes": ["summary_split_kernel<128> (x2)", "route_prefill_mfma_kernel<128,8>"],
                       "flops_per_launch": fl_route, "achieved_tflops": round(tf_route, 1),
-                      "frac": round(tf_route / MFMA_BF16_PEAK_TFLOPS, 4)},
+                      "frac": round(tf_route / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "traffic_mfma_kernel": measured_traffic("route_prefill_mfma_kernel<128,8>")},
             "summaries": {"kernel": "summaries_fast_kernel<128,4>", "avg_us": round(t_sum, 2),
                           "bytes_per_launch": summ_bytes,
+                          "traffic": measured_traffic("summaries_fast_kernel<128,4>"),
                           "achieved_gbs": round(summ_bytes / (t_sum * 1e-6) / 1e9, 1),
                           "frac": round(summ_bytes / (t_sum * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
             "backward": bench_backward(s, p, Q, K, V, gi, dev)}
