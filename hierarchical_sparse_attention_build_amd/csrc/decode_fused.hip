@@ -16,6 +16,10 @@
 //   * F forced workgroups attend shares of the sink, local and current chunks
 //     (known before routing) while the routing workgroups work.  Forced
 //     workgroup 0 then summarises the chunk that the query completes.
+//   * When the grid leaves compute units idle, one more workgroup per unit
+//     reads the second half of the candidate summaries at launch, so that the
+//     routing scans, which start from the first half, find it in the XCD's L2
+//     (it computes nothing and takes no part in the merge).
 // The F + R partial softmax results (max, sum, output) are merged by the last
 // of them to finish; no workgroup waits for another.
 //
@@ -480,6 +484,25 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, int r,
   }
 }
 
+// Warm-up role: touch candidate summary rows [nM/2, nM) of unit bh (every
+// 16-byte piece, as the scans read them) and discard the values.
+template <int D>
+__device__ __forceinline__ void warm_summaries(const DecodeArgs& a, int bh) {
+  const KParams& kp = a.kp;
+  const int t = a.seq_len[bh / kp.Hkv] + a.pos_offset;
+  if (t < 0 || t >= kp.n_cap) return;
+  const int nM = max(0, t / kp.C - kp.n_local - kp.n_sink);
+  const float4* tab = reinterpret_cast<const float4*>(a.chunk_sum + (static_cast<int64_t>(bh) * kp.n_chunks_cap + kp.n_sink) * D);
+  const int end = nM * (D / 4);
+  float acc = 0.f;
+#pragma unroll 8
+  for (int i = (nM / 2) * (D / 4) + static_cast<int>(threadIdx.x); i < end; i += kDecThreads) {
+    const float4 v = tab[i];
+    acc = fmaxf(acc, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  }
+  asm volatile("" ::"v"(acc));  // keeps the loads; nothing is written
+}
+
 // Unit bh of the workgroup at blockIdx.x: consecutive workgroups go to
 // consecutive XCDs, so all workgroups of a unit share blockIdx.x % 8 and its
 // summaries and rows are shared through one L2; roles in blockIdx order.
@@ -491,13 +514,17 @@ __device__ __forceinline__ void unit_of(const DecodeArgs& a, int& bh, int& role)
 }
 
 // One launch per step.  Roles: 0..R-1 routing and routed attention, R..R+F-1
-// forced.
+// forced, R+F the summary warm-up (when present).
 template <typename T, int D, int GQ>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeArgs a) {
   int bh, role;
   unit_of(a, bh, role);
   const KParams& kp = a.kp;
-  if (bh >= kp.B * kp.Hkv || role >= a.routing_wgs + a.forced_wgs) return;
+  if (bh >= kp.B * kp.Hkv || role >= a.routing_wgs + a.forced_wgs + a.warm_wgs) return;
+  if (role >= a.routing_wgs + a.forced_wgs) {
+    warm_summaries<D>(a, bh);
+    return;
+  }
   __shared__ DecodeSmem<GQ, D> sm;
   if (role < a.routing_wgs) {
     routing_role<T, D, GQ>(a, bh, role, sm);
@@ -520,7 +547,7 @@ bool decode_fused_supported(const KParams& kp) {
 template <typename T, int D, int GQ>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
   const unsigned per_role = static_cast<unsigned>(kXcds) * a.units_per_xcd;
-  decode_step_kernel<T, D, GQ><<<per_role * (a.routing_wgs + a.forced_wgs), kDecThreads, 0, st>>>(a);
+  decode_step_kernel<T, D, GQ><<<per_role * (a.routing_wgs + a.forced_wgs + a.warm_wgs), kDecThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -535,7 +562,8 @@ static hipError_t launch_gq(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode_step(const DecodeArgs& a, bool bf16_in, hipStream_t st) {
-  if (a.forced_wgs < 1 || a.forced_wgs > kDecMaxForced || a.routing_wgs < 1 || a.routing_wgs > kDecMaxRouting)
+  if (a.forced_wgs < 1 || a.forced_wgs > kDecMaxForced || a.routing_wgs < 1 || a.routing_wgs > kDecMaxRouting ||
+      a.warm_wgs < 0 || a.warm_wgs > 1 || (a.warm_wgs && a.routes_in))
     return hipErrorInvalidValue;
   if (bf16_in) return a.kp.d == 64 ? launch_gq<bf16, 64>(a, st) : launch_gq<bf16, 128>(a, st);
   return a.kp.d == 64 ? launch_gq<float, 64>(a, st) : launch_gq<float, 128>(a, st);

@@ -243,7 +243,10 @@ int device_cus() {
 // top_g = 0, streaming heads): one routing workgroup and two forced.  One
 // routing workgroup with routing, but a grid of three per unit would share
 // CUs: one forced workgroup when that makes it fit (decode_64k, 128 units:
-// 44.7 us against 45.1).
+// 44.7 us against 45.1).  With routing and CUs to spare after that, one
+// warm-up workgroup per unit reads the second half of its candidate summaries
+// into L2 while the routing scans read the first (decode_32k, B = 8, 256
+// workgroups: 21.19 us against 21.52).
 void fused_shape(const KParams& kp, const FusedPlan& fp, bool given, DecodeArgs& da) {
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   const int want = std::max(1, std::min(HGA_DECODE_ROUTING_WGS, kDecMaxRouting));
@@ -257,6 +260,7 @@ void fused_shape(const KParams& kp, const FusedPlan& fp, bool given, DecodeArgs&
   da.forced_wgs = std::max(1, std::min(std::min(forced, fp.forced_blocks), kDecMaxForced));
   da.forced_bpw = static_cast<int>(cdiv(fp.forced_blocks, da.forced_wgs));
   da.units_per_xcd = fp.units_per_xcd;
+  da.warm_wgs = routed && !given && units * (da.routing_wgs + da.forced_wgs + 1) <= cus ? 1 : 0;
 }
 
 struct IdxPlan {
