@@ -17,9 +17,9 @@
 //     (known before routing) while the routing workgroups work.  Forced
 //     workgroup 0 then summarises the chunk that the query completes.
 //   * When the grid leaves compute units idle, one more workgroup per unit
-//     reads the second half of the candidate summaries at launch, so that the
-//     routing scans, which start from the first half, find it in the XCD's L2
-//     (it computes nothing and takes no part in the merge).
+//     reads the candidate summaries at launch, in the scans' order, so that
+//     the routing scans find much of the table in the XCD's L2 (it computes
+//     nothing and takes no part in the merge).
 // The F + R partial softmax results (max, sum, output) are merged by the last
 // of them to finish; no workgroup waits for another.
 //
@@ -484,8 +484,9 @@ __device__ __forceinline__ void routing_role(const DecodeArgs& a, int bh, int r,
   }
 }
 
-// Warm-up role: touch candidate summary rows [nM/2, nM) of unit bh (every
-// 16-byte piece, as the scans read them) and discard the values.
+// Warm-up role: read candidate summary rows [0, nM) of unit bh (every 16-byte
+// piece, in the scans' order, eight loads of a thread in flight: more or fewer
+// were slower) and discard the values.
 template <int D>
 __device__ __forceinline__ void warm_summaries(const DecodeArgs& a, int bh) {
   const KParams& kp = a.kp;
@@ -496,7 +497,7 @@ __device__ __forceinline__ void warm_summaries(const DecodeArgs& a, int bh) {
   const int end = nM * (D / 4);
   float acc = 0.f;
 #pragma unroll 8
-  for (int i = (nM / 2) * (D / 4) + static_cast<int>(threadIdx.x); i < end; i += kDecThreads) {
+  for (int i = static_cast<int>(threadIdx.x); i < end; i += kDecThreads) {
     const float4 v = tab[i];
     acc = fmaxf(acc, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
   }

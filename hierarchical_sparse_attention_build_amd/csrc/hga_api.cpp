@@ -244,9 +244,10 @@ int device_cus() {
 // routing workgroup with routing, but a grid of three per unit would share
 // CUs: one forced workgroup when that makes it fit (decode_64k, 128 units:
 // 44.7 us against 45.1).  With routing and CUs to spare after that, one
-// warm-up workgroup per unit reads the second half of its candidate summaries
-// into L2 while the routing scans read the first (decode_32k, B = 8, 256
-// workgroups: 21.19 us against 21.52).
+// warm-up workgroup per unit reads its candidate summaries into L2 alongside
+// the routing scans (decode_32k, B = 8, 256 workgroups: 20.83 us against
+// 21.52 without; 20.92 when it reads only the last three quarters, 21.19 the
+// second half).
 void fused_shape(const KParams& kp, const FusedPlan& fp, bool given, DecodeArgs& da) {
   const int64_t units = static_cast<int64_t>(kp.B) * kp.Hkv;
   const int want = std::max(1, std::min(HGA_DECODE_ROUTING_WGS, kDecMaxRouting));
