@@ -257,6 +257,48 @@ def test_visible_set_with_given_lists_is_a_causal_union():
     np.testing.assert_allclose(o[0, 0, 0], w @ V[0, 0, want] / w.sum(), atol=1e-12)
 
 
+def test_unit_block_attention_matches_masked_softmax_per_row():
+    """The prefill oracle's per-unit form (all g_q*C rows of a query chunk at
+    once) against a mask built row by row from the rule (sink chunks, local
+    chunks, the current chunk up to the row, the listed groups) and a float64
+    masked softmax in torch: GQA head grouping, causality inside the current
+    chunk, holes, repeats and a listed group inside a forced chunk."""
+    cf = cfg(chunk_size=8, group_size=4, n_sink=1, n_local=1, top_g=4)
+    Hkv, gq, d, n = 2, 2, 16, 64
+    rng = np.random.default_rng(11)
+    Q = rng.standard_normal((1, Hkv * gq, n, d))
+    K = rng.standard_normal((1, Hkv, n, d))
+    V = rng.standard_normal((1, Hkv, n, d))
+    nU = n // 8
+    gi = np.full((1, Hkv, nU, 4), -1, dtype=np.int64)
+    for h in range(Hkv):
+        for u in range(nU):
+            cands = list(range(1 * 2, max(1, u - 1) * 2))  # groups of chunks [1, u - 1)
+            pick = rng.permutation(cands)[:3].tolist() if cands else []
+            row = pick + [pick[0] if pick else -1]     # a repeat (or a hole)
+            if u >= 3:
+                row[-1] = 2 * (u - 1)                   # a group of the local chunk u - 1
+            gi[0, h, u, :len(row)] = row
+    for h in range(Hkv):
+        for u in range(nU):
+            o, lse = O.attend_unit_block(Q, np.array([0]), K, V, gi, cf, Hkv, 0, h, u)
+            listed = {int(g) for g in gi[0, h, u] if g >= 0}
+            for hh in range(gq):
+                for c in range(8):
+                    t = 8 * u + c
+                    s = torch.arange(n)
+                    vis = (s < 8) | (s >= 8 * (u - 1))
+                    vis |= torch.tensor([(x // 4) in listed for x in range(n)])
+                    vis &= s <= t  # causal: nothing after the row
+                    q = torch.from_numpy(Q[0, h * gq + hh, t])
+                    z = torch.from_numpy(K[0, h]) @ q / math.sqrt(d)
+                    z = torch.where(vis, z, torch.tensor(-math.inf, dtype=torch.float64))
+                    w = torch.softmax(z, dim=0)
+                    want = (w @ torch.from_numpy(V[0, h])).numpy()
+                    np.testing.assert_allclose(o[hh, c], want, atol=1e-12)
+                    np.testing.assert_allclose(lse[hh, c], torch.logsumexp(z, dim=0).item(), atol=1e-12)
+
+
 def test_route_takes_all_when_fewer_candidates():
     cf = cfg(head_dim=8, chunk_size=4, group_size=2, n_sink=1, n_local=1, top_k=50, top_g=500)
     rng = np.random.default_rng(2)
