@@ -25,6 +25,7 @@
 // workspace with device-coherent stores, and the last of the parts of a row
 // merges them.
 #pragma once
+#include <type_traits>
 
 #include "hga_device.hpp"
 #include "hga_kparams.hpp"
@@ -385,6 +386,45 @@ struct AttnLaneMfma {
     b.ok = okm;
   }
 
+  // Without write-back the loads of a round go out as every block's K rows
+  // (and visibility bits), then every block's V rows: the scores need only
+  // the K rows, so they start while the V rows are still in flight
+  // (decode_32k 20.71 against 20.90 us per step, streaming heads 12.77
+  // against 12.98).
+  template <typename RowFn>
+  __device__ __forceinline__ void fetch_k(int R0, int blkid, Buf& b, RowFn row) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4;
+    const int cc = lane & 15;
+    const int s0 = R0 + blkid * kAttnBlock;
+    uint32_t okm = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16* kp;
+      const bf16* vp;
+      const bool ok = row(s0 + 4 * g + i, kp, vp);
+      b.k[i] = load_raw<RB>(kp + cc * EPL);
+      const uint64_t m = __ballot(ok);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) okm |= static_cast<uint32_t>((m >> (16 * gg)) & 1u) << (4 * gg + i);
+    }
+    b.ok = okm;
+  }
+  template <typename RowFn>
+  __device__ __forceinline__ void fetch_v(int R0, int blkid, Buf& b, RowFn row) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4;
+    const int cc = lane & 15;
+    const int s0 = R0 + blkid * kAttnBlock;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16* kp;
+      const bf16* vp;
+      row(s0 + 4 * g + i, kp, vp);
+      b.v[i] = load_raw<RB>(vp + cc * EPL);
+    }
+  }
+
   // S[row 4g+i][head h] (raw dot products) of one block: its K rows go
   // through the tile into the A operand layout.
   __device__ __forceinline__ f32x4_t scores(const Buf& b) {
@@ -424,9 +464,18 @@ struct AttnLaneMfma {
       }
     };
     auto load = [&](int c0, Buf (&buf)[PF]) {
+      if constexpr (std::is_same<WbFn, NoWriteBack>::value) {
 #pragma unroll
-      for (int p = 0; p < PF; ++p)
-        if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row, wb);
+        for (int p = 0; p < PF; ++p)
+          if (c0 + p < n) fetch_k(R0, first + (c0 + p) * step, buf[p], row);
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+          if (c0 + p < n) fetch_v(R0, first + (c0 + p) * step, buf[p], row);
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+          if (c0 + p < n) fetch(R0, first + (c0 + p) * step, buf[p], row, wb);
+      }
     };
     for (int c0 = 0; c0 < n; c0 += PF) {
       Buf buf[PF];
