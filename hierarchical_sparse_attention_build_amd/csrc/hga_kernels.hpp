@@ -113,8 +113,8 @@ struct DecodeArgs {
   const int32_t* routes_in;  // nullable [B*Hkv, top_g]: given group lists (no routing; chunk_idx,
                              // group_idx, chunk_sum and group_sum unused)
   int32_t pos_offset;        // the query position is seq_len[b] + pos_offset
-  int32_t warm_wgs;          // 0 or 1 per (b, kv head): reads the second half of the unit's
-                             // candidate summaries into its XCD's L2 ahead of the routing scans
+  int32_t warm_wgs;          // 0 or 1 per (b, kv head): reads the unit's candidate summaries
+                             // into its XCD's L2 alongside the routing scans
 };
 
 struct GatherArgs {
