@@ -169,19 +169,20 @@ __device__ __forceinline__ void wave_topk_n(int slots, KeyFn key_of, int k, bool
   }
 }
 
-template <int NT>
+template <int NT, int MK = kSelMaxK>
 struct SelSmem {
   static constexpr int NW = NT / kWave;
-  uint32_t key[NW * kSelMaxK];
-  int pos[NW * kSelMaxK];
+  uint32_t key[NW * MK];
+  int pos[NW * MK];
 };
 
-// True when block_select<NT, MaxE> handles (n, k): at most MaxE keys per lane
-// in either phase.  Monotone in n: it holds for every smaller n as well.
-template <int NT, int MaxE = kSelMaxE>
+// True when block_select<NT, MaxE, MK> handles (n, k): k <= MK and at most
+// MaxE keys per lane in either phase.  Monotone in n: it holds for every
+// smaller n as well.
+template <int NT, int MaxE = kSelMaxE, int MK = kSelMaxK>
 __host__ __device__ constexpr bool block_select_fits(int n, int k) {
   constexpr int NW = NT / kWave;
-  if (k > kSelMaxK) return false;
+  if (k > MK) return false;
   if (n <= k || n <= 2 * kWave) return true;  // nothing to select, or one wave with two keys per lane
   const int q = (n + NW - 1) / NW;
   return q <= kWave * MaxE && NW * (k < q ? k : q) <= kWave * MaxE;
@@ -190,9 +191,9 @@ __host__ __device__ constexpr bool block_select_fits(int n, int k) {
 // Exact selection of the min(n, k) best of sc(0..n) (sc reads LDS or memory);
 // the chosen positions go to sel[] (LDS) in ascending order.  Every thread of
 // the workgroup calls it; returns min(n, k) and ends with a barrier.
-// Requires block_select_fits<NT, MaxE>(n, k).
-template <int NT, int MaxE = kSelMaxE, typename ScoreFn>
-__device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT>& sm) {
+// Requires block_select_fits<NT, MaxE, MK>(n, k).
+template <int NT, int MaxE = kSelMaxE, int MK = kSelMaxK, typename ScoreFn>
+__device__ int block_select(ScoreFn sc, int n, int k, int* sel, SelSmem<NT, MK>& sm) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);

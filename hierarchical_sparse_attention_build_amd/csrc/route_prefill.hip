@@ -9,14 +9,20 @@
 // of a lane are 16 query rows, so the max over queries is lane-local (plus the
 // partner half-wave and the other waves through LDS).  Q is exact in bf16;
 // the fp32 summaries are split as s = hi + lo with hi = bf16(s) and
-// lo = bf16(s - hi) and both products accumulate in fp32 (relative error of
-// the split about 2^-17).  The split is done once per call by a pre-pass over
-// both tables (every unit of a KV head reads the same rows); the units copy
-// their tiles of hi and lo rows into LDS.  Top-k on the chunk scores, then
-// the same contraction over the C/G groups of every routed chunk and a top-g.
+// lo = bf16(s - hi); the lo and then the hi products accumulate in one fp32
+// chain (relative error of the split about 2^-17).  The split is done once
+// per call by a pre-pass over both tables (every unit of a KV head reads the
+// same rows); the units copy their tiles of hi and lo rows from memory
+// straight into LDS.  Top-k on the chunk scores, then the same contraction
+// over the C/G groups of every routed chunk and a top-g.  Where the shape
+// allows (at most 1024 candidate chunks and routed groups, k <= 64) the score
+// and selection arrays are sized for it, so three 512-thread workgroups
+// share a CU.
 #include "hga_device.hpp"
 #include "hga_kernels.hpp"
 #include "hga_select.hpp"
+
+#include <algorithm>
 
 namespace hga {
 
@@ -26,19 +32,32 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRTile = 32;  // summaries per tile
 
-template <int D, int NW>
+// Selection scratch: the compact variant's k <= 64; the general one also holds
+// the radix path's scratch for a k too large for the ballot search.
+template <int NT, bool SMALL>
+union RouteSelSmem;
+template <int NT>
+union RouteSelSmem<NT, true> {
+  SelSmem<NT, 64> sel;
+};
+template <int NT>
+union RouteSelSmem<NT, false> {
+  SelSmem<NT> sel;
+  TopkSmem<NT> topk;
+};
+
+template <int D, int NW, bool SMALL>
 struct RoutePrefillSmem {
-  static constexpr int ROW = D * 2 + 16;  // bytes per bf16 row (padded)
-  alignas(16) unsigned char hi[2][kRTile * ROW];
-  alignas(16) unsigned char lo[2][kRTile * ROW];
+  static constexpr int ROW = D * 2 + 16;       // bytes per bf16 row (padded by one 16-byte piece)
+  static constexpr int PART = kRTile * ROW;    // one table's rows of a tile
+  static constexpr int MAXN = SMALL ? 1024 : 4096;  // candidate chunks, and routed chunks x C/G
+  static constexpr int MAXK = SMALL ? 64 : 1024;
+  alignas(16) unsigned char tile[2][2 * PART];  // per buffer: hi rows, then lo rows
   float wmax[2][NW][kRTile];  // per tile parity: each wave's column maxima
-  float scores[1024 * 4];   // chunk scores of the unit, then group scores
-  int sel_chunks[1024];
-  int sel_groups[1024];
-  union {  // scratch of the selection in use
-    SelSmem<NW * 64> sel;
-    TopkSmem<NW * 64> topk;
-  } u;
+  float scores[MAXN];         // chunk scores of the unit, then group scores
+  int sel_chunks[MAXK];
+  int sel_groups[MAXK];
+  RouteSelSmem<NW * 64, SMALL> u;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -72,14 +91,18 @@ size_t route_prefill_split_bytes(const KParams& kp) {
   return rows * kp.d * 2 * sizeof(uint16_t);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a) {
+// Waves per SIMD the compact variant is compiled for: three workgroups of
+// eight waves per CU need at most 80 VGPRs per lane.
+template <int NW, bool SMALL>
+constexpr int route_waves_per_eu() { return SMALL && NW == 8 ? 6 : 1; }
+
+template <int D, int NW, bool SMALL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(route_waves_per_eu<NW, SMALL>(), 8)))
+void route_prefill_mfma_kernel(RouteArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;
   constexpr int P8 = D / 8;                     // 16-byte pieces per bf16 row
-  constexpr int PPT = 2 * kRTile * P8 / NT;     // pieces per thread per tile (hi and lo)
-  static_assert(PPT >= 1 && 2 * kRTile * P8 % NT == 0, "tile split");
-  using Smem = RoutePrefillSmem<D, NW>;
+  using Smem = RoutePrefillSmem<D, NW, SMALL>;
   const KParams& kp = a.kp;
 
   int x = blockIdx.x;
@@ -123,45 +146,56 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
   // hi, lo) into out[0..n).  Tiles are loaded two ahead (register sets A and B
   // alternate, the loop is unrolled by two so each set is named statically)
   // and copied into the LDS buffer of their parity.
+  // scores of n rows (row(i): index of the summary row in the split tables
+  // hi, lo) into out[0..n).  A tile's hi and lo rows go from memory straight
+  // into the LDS buffer of its parity (17 copies of 1 KB per tile: each row
+  // is 16 pieces of 16 bytes plus a padding piece, which loads a duplicate),
+  // one tile ahead; one barrier per tile.
+  constexpr int PIECES = 2 * kRTile * (P8 + 1);        // pieces of a tile, padding included
+  constexpr int NCOPY = (PIECES + 63) / 64;            // 1 KB copies per tile
+  constexpr int CPW = (NCOPY + NW - 1) / NW;           // copies per wave
+  static_assert(PIECES % 64 == 0, "whole copies");
+  int c_part[CPW], c_row[CPW], c_off[CPW];
+#pragma unroll
+  for (int k = 0; k < CPW; ++k) {
+    const int q = 64 * (wid + NW * k) + lane;
+    const int part = q / (kRTile * (P8 + 1)), rq = q % (kRTile * (P8 + 1));
+    const int pc = rq % (P8 + 1);
+    c_part[k] = part;
+    c_row[k] = rq / (P8 + 1);
+    c_off[k] = (pc < P8 ? pc : 0) * 8;  // elements; the padding piece repeats piece 0
+  }
   auto score_tiles = [&](int n, auto row, const uint16_t* hi, const uint16_t* lo, float* out) {
     const int n_tiles = (n + kRTile - 1) / kRTile;
-    u32x4_t regA[PPT], regB[PPT];
-    auto fetch = [&](int tt, u32x4_t (&reg)[PPT]) {
+    auto copy = [&](int tt, int buf) {
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int f = tid + i * NT;
-        const int part = f / (kRTile * P8), q = f % (kRTile * P8);
-        const int r = q / P8, c = q % P8;
-        const int idx = tt * kRTile + r;
-        const uint16_t* tab = part ? lo : hi;
-        reg[i] = idx < n ? *reinterpret_cast<const u32x4_t*>(tab + row(idx) * D + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      for (int k = 0; k < CPW; ++k) {
+        if (wid + NW * k < NCOPY) {
+          const int idx = min(tt * kRTile + c_row[k], n - 1);  // rows past n: any valid row
+          const uint16_t* src = (c_part[k] ? lo : hi) + row(idx) * D + c_off[k];
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                           (__attribute__((address_space(3))) void*)(&sm.tile[buf][1024 * (wid + NW * k)]),
+                                           16, 0, 0);
+        }
       }
     };
-    auto stage = [&](int buf, const u32x4_t (&reg)[PPT]) {
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int f = tid + i * NT;
-        const int part = f / (kRTile * P8), q = f % (kRTile * P8);
-        const int r = q / P8, c = q % P8;
-        unsigned char* dst = part ? sm.lo[buf] : sm.hi[buf];
-        *reinterpret_cast<u32x4_t*>(dst + r * Smem::ROW + c * 16) = reg[i];
-      }
-    };
-    // tile tt from LDS buffer buf: the max over the unit's query rows of every
-    // column; the hi and lo products accumulate in two independent chains
     auto compute = [&](int buf) {
-      f32x16_t acc_h = f32x16_t{}, acc_l = f32x16_t{};
+      f32x16_t acc = f32x16_t{};
+      const unsigned char* th = sm.tile[buf];
+      const unsigned char* tl = sm.tile[buf] + Smem::PART;
 #pragma unroll
       for (int d = 0; d < KSTEPS; ++d) {
         const int off = ql * Smem::ROW + (16 * d + 8 * hb) * 2;
-        const bf16x8_t bh_ = *reinterpret_cast<const bf16x8_t*>(&sm.hi[buf][off]);
-        const bf16x8_t bl_ = *reinterpret_cast<const bf16x8_t*>(&sm.lo[buf][off]);
-        acc_h = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], bh_, acc_h, 0, 0, 0);
-        acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], bl_, acc_l, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], *reinterpret_cast<const bf16x8_t*>(tl + off), acc, 0, 0, 0);
       }
-      float mx = acc_h[0] + acc_l[0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc_h[v] + acc_l[v]);
+      for (int d = 0; d < KSTEPS; ++d) {
+        const int off = ql * Smem::ROW + (16 * d + 8 * hb) * 2;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[d], *reinterpret_cast<const bf16x8_t*>(th + off), acc, 0, 0, 0);
+      }
+      float mx = acc[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
       {
         float pa, pb;
         dpp::swap32(mx, pa, pb);
@@ -179,25 +213,19 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
       }
     };
     if (n_tiles == 0) return;
-    // tile tt: its buffer tt % 2 is staged; tile tt + 1 is in the other
-    // register set, tile tt + 2 goes into this one.  One barrier per tile:
-    // buffer (tt + 1) % 2 was last read before the previous barrier, and the
-    // maxima of tile tt are reduced after this one (those of tile tt + 2, in
-    // the same slots, are written after the next).
-    auto step = [&](int tt, u32x4_t (&mine)[PPT], u32x4_t (&other)[PPT]) {
-      if (tt + 2 < n_tiles) fetch(tt + 2, mine);
+    // tile tt computes from buffer tt % 2 while tile tt + 1 lands in the
+    // other; that buffer was last read by tile tt - 1, before the previous
+    // barrier.  Each wave waits for its own copies, then the barrier publishes
+    // the tile to all waves.
+    copy(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int tt = 0; tt < n_tiles; ++tt) {
+      if (tt + 1 < n_tiles) copy(tt + 1, (tt + 1) & 1);
       compute(tt & 1);
-      if (tt + 1 < n_tiles) stage((tt + 1) & 1, other);
+      wait_vmem();
       __syncthreads();
       reduce(tt);
-    };
-    fetch(0, regA);
-    if (n_tiles > 1) fetch(1, regB);
-    stage(0, regA);
-    __syncthreads();
-    for (int tt = 0; tt < n_tiles; tt += 2) {
-      step(tt, regA, regB);
-      if (tt + 1 < n_tiles) step(tt + 1, regB, regA);
     }
     __syncthreads();  // the last scores are in out
   };
@@ -213,9 +241,13 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
   // exact top-k of sm.scores[0, n) into out (ascending positions): ballot
   // search by whole waves, or the radix path for a k too large for it
   auto select = [&](int n, int k, int* out) -> int {
-    if (block_select_fits<NT>(n, k))
-      return block_select<NT>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.sel);
-    return block_topk<NT>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.topk);
+    if constexpr (SMALL) {
+      return block_select<NT, 4, 64>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.sel);
+    } else {
+      if (block_select_fits<NT>(n, k))
+        return block_select<NT>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.sel);
+      return block_topk<NT>([&](int i) { return sm.scores[i]; }, n, k, out, sm.u.topk);
+    }
   };
   const int cnt = select(nM, kp.top_k, sm.sel_chunks);
   int32_t* ci = a.chunk_idx + unit * kp.top_k;
@@ -243,7 +275,20 @@ __global__ __launch_bounds__(NW * 64) void route_prefill_mfma_kernel(RouteArgs a
 bool route_prefill_mfma_supported(const KParams& kp, bool bf16_in, int64_t nq) {
   return bf16_in && nq > 1 && kp.C == 64 && (kp.d == 64 || kp.d == 128) &&
          (kp.gq == 1 || kp.gq == 2 || kp.gq == 4) && kp.n_chunks_cap <= 4096 &&
-         static_cast<int64_t>(kp.top_k) * kp.m <= 4096;
+         static_cast<int64_t>(kp.top_k) * kp.m <= 4096 && kp.top_k <= 1024 && kp.top_g <= 1024;
+}
+
+// The compact variant holds every unit of this shape: at most 1024 candidate
+// chunks and 1024 routed groups, k <= 64, and both selections within four
+// keys per lane (block_select_fits is monotone in n, so the largest unit
+// decides).
+template <int NW>
+static bool route_small_fits(const KParams& kp) {
+  constexpr int NT = NW * 64;
+  const int max_cand = std::max(0, kp.n_chunks_cap - 1 - kp.n_local - kp.n_sink);
+  const int max_groups = kp.top_k * kp.m;
+  return max_cand <= 1024 && max_groups <= 1024 && kp.top_k <= 64 && kp.top_g <= 64 &&
+         block_select_fits<NT, 4, 64>(max_cand, kp.top_k) && block_select_fits<NT, 4, 64>(max_groups, kp.top_g);
 }
 
 template <int D, int NW>
@@ -258,7 +303,10 @@ static hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
   split(a.chunk_sum, crows, a.split, a.split + n_ctab);
   split(a.group_sum, crows * kp.m, a.split + 2 * n_ctab, a.split + 2 * n_ctab + n_ctab * kp.m);
   const unsigned n_wg = static_cast<unsigned>(kp.B) * kp.Hkv * a.n_units;
-  route_prefill_mfma_kernel<D, NW><<<n_wg, NW * 64, 0, st>>>(a);
+  if (route_small_fits<NW>(kp))
+    route_prefill_mfma_kernel<D, NW, true><<<n_wg, NW * 64, 0, st>>>(a);
+  else
+    route_prefill_mfma_kernel<D, NW, false><<<n_wg, NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -358,7 +358,9 @@ def test_prefill_tiny_fp32(hga, over):
 
 @pytest.mark.parametrize("over", [{"n_tokens": 2048}, {"n_tokens": 4096, "batch": 1},
                                   {"n_tokens": 2048, "head_dim": 64, "n_q_heads": 16},
-                                  {"n_tokens": 2048, "n_q_heads": 8, "top_g": 40}])
+                                  {"n_tokens": 2048, "n_q_heads": 8, "top_g": 40},
+                                  # k > 64: the routing kernel's general variant (large LDS arrays)
+                                  {"n_tokens": 8192, "top_k": 72, "top_g": 96}])
 def test_prefill_bf16(hga, over):
     s = W.spec("prefill_32k", **over)
     say(f"[prefill bf16] {over} seed={s.seed}")
