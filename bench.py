@@ -375,11 +375,11 @@ def bench_prefill(args, dev):
                          "traffic": measured_traffic("hga_attend_prefill"),
                          "flops_per_launch": fl_att, "avg_us": round(t_att, 2),
                          "includes": ["v16_blocks_kernel<128>", "attend_prefill_pipe_kernel<128,8>"]},
-            "route": {"kernel": "route_prefill_mfma_kernel<128,8>", "avg_us": round(t_route, 2),
-                      "includes": ["summary_split_kernel<128> (x2)", "route_prefill_mfma_kernel<128,8>"],
+            "route": {"kernel": "route_prefill_mfma_kernel<128,8,true>", "avg_us": round(t_route, 2),
+                      "includes": ["summary_split_kernel<128> (x2)", "route_prefill_mfma_kernel<128,8,true>"],
                       "flops_per_launch": fl_route, "achieved_tflops": round(tf_route, 1),
                       "frac": round(tf_route / MFMA_BF16_PEAK_TFLOPS, 4),
-                      "traffic_mfma_kernel": measured_traffic("route_prefill_mfma_kernel<128,8>")},
+                      "traffic_mfma_kernel": measured_traffic("route_prefill_mfma_kernel<128,8,true>")},
             "summaries": {"kernel": "summaries_fast_kernel<128,4>", "avg_us": round(t_sum, 2),
                           "bytes_per_launch": summ_bytes,
                           "traffic": measured_traffic("summaries_fast_kernel<128,4>"),
